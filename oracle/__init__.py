@@ -1,0 +1,144 @@
+"""CPU oracle for single-query decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the bench's CPU-baseline leg
+may import this package.  The product path (the HIP library and its Python
+binding) never touches it.
+
+The arithmetic lives in ``attn_oracle.c`` (fp64 scalar loops, its own
+binary16 decoder); this module only marshals numpy arrays through ctypes.  It
+follows the page "Developing Apple Metal Kernels in Rust - A Deep Dive
+Through Attention", section "The MSL, briefly" (kernels attention_qk_f16 and
+attention_pv_f16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import _build
+
+
+def _bits(a) -> np.ndarray:
+    """Contiguous uint16 view of an fp16/uint16 numpy array or torch tensor."""
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().contiguous().numpy()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("expected float16 or uint16 data, got %s" % a.dtype)
+    return a
+
+
+def _ptr(a, ct):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+class OracleLib:
+    """ctypes view of one build of the oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        u32 = ctypes.c_uint32
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_half_to_double_array.argtypes = [u16p, ctypes.c_size_t, f64p]
+        lib.oracle_half_to_double_array.restype = None
+        lib.oracle_attn_decode.argtypes = [u16p, u16p, u16p, u32, u32, u32, u32, u32, u32,
+                                           f64p, f64p, f64p]
+        lib.oracle_attn_decode.restype = ctypes.c_int
+        self.path = path
+        self.lib = lib
+
+    def half_to_double(self, bits) -> np.ndarray:
+        b = _bits(bits)
+        out = np.empty(b.shape, dtype=np.float64)
+        self.lib.oracle_half_to_double_array(_ptr(b, ctypes.c_uint16), b.size,
+                                             _ptr(out, ctypes.c_double))
+        return out
+
+    def decode(self, q, k, v, current_pos: int, *, want_scores=False, want_weights=False,
+               threads: int = 1):
+        """One sequence.  q [H, D], k/v [S, H, D] (fp16 or uint16 bits).
+
+        Returns ``(out [H, D], scores [H, S] or None, weights [H, S] or None)``,
+        all float64.  ``threads > 1`` splits the heads over host threads
+        (ctypes releases the GIL); each head is computed the same way.
+        """
+        shape = tuple(k.shape)
+        if len(shape) != 3:
+            raise ValueError("k must be [seq_len, n_heads, head_dim]")
+        S, H, D = shape
+        if tuple(v.shape) != shape or tuple(q.shape)[-2:] != (H, D):
+            raise ValueError("shape mismatch")
+        if int(current_pos) < 0:
+            raise ValueError("current_pos must be >= 0")
+        qb, kb, vb = _bits(q), _bits(k), _bits(v)
+        out = np.zeros((H, D), dtype=np.float64)
+        scores = np.empty((H, S), dtype=np.float64) if want_scores else None
+        weights = np.empty((H, S), dtype=np.float64) if want_weights else None
+        cp = min(int(current_pos), 0xFFFFFFFF)
+        f64 = ctypes.c_double
+        u16 = ctypes.c_uint16
+
+        def run(lo_hi):
+            lo, hi = lo_hi
+            rc = self.lib.oracle_attn_decode(_ptr(qb, u16), _ptr(kb, u16), _ptr(vb, u16),
+                                             H, D, S, cp, lo, hi, _ptr(out, f64),
+                                             _ptr(scores, f64), _ptr(weights, f64))
+            if rc != 0:
+                raise RuntimeError("oracle_attn_decode failed")
+
+        threads = max(1, min(int(threads), H))
+        if threads == 1:
+            run((0, H))
+        else:
+            bounds = [(H * i // threads, H * (i + 1) // threads) for i in range(threads)]
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(run, bounds))
+        return out, scores, weights
+
+    def decode_batched(self, q, k, v, current_pos, *, want_scores=False, threads: int = 1):
+        """Independent sequences: q [B, H, D], k/v [B, S, H, D], current_pos [B].
+
+        The batched form is a loop of single-sequence calls, each with its
+        own current_pos.
+        """
+        outs, scs = [], []
+        for b in range(k.shape[0]):
+            o, s, _ = self.decode(q[b], k[b], v[b], int(current_pos[b]),
+                                  want_scores=want_scores, threads=threads)
+            outs.append(o)
+            scs.append(s)
+        return np.stack(outs), (np.stack(scs) if want_scores else None)
+
+
+_default = None
+
+
+def load(build_if_missing: bool = True) -> OracleLib:
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB):
+            if not build_if_missing:
+                raise RuntimeError("oracle library not built: %s" % _build.LIB)
+            _build.build()
+        _default = OracleLib(_build.LIB)
+    return _default
+
+
+def half_to_double(bits) -> np.ndarray:
+    return load().half_to_double(bits)
+
+
+def decode(q, k, v, current_pos, **kw):
+    return load().decode(q, k, v, current_pos, **kw)
+
+
+def decode_batched(q, k, v, current_pos, **kw):
+    return load().decode_batched(q, k, v, current_pos, **kw)

@@ -1,0 +1,353 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Each pin takes an ``oracle.OracleLib`` and raises AssertionError when the
+oracle disagrees with a value fixed by the page or by mathematics: the IEEE
+binary16 definition (via numpy's own conversion), exact rational arithmetic,
+closed forms, invariants, an independent direct formula and torch's own
+scaled-dot-product attention.  ``test_oracle.py`` runs every pin on the real
+oracle; ``test_oracle_mutants.py`` runs them on deliberately broken copies of
+the oracle source and requires each copy to fail at least one pin.
+
+The page is "Developing Apple Metal Kernels in Rust - A Deep Dive Through
+Attention": section "The MSL, briefly" defines the computation, section
+"Testing" the worked cases in ``golden/page_cases.json``.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def page_cases():
+    with open(os.path.join(GOLDEN, "page_cases.json")) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _randn_f16(rng, shape, sigma=1.0):
+    return (rng.standard_normal(shape) * sigma).astype(np.float16)
+
+
+def _page_fill(n):
+    """(i % 10) * 0.1 computed in f32, then rounded to f16 (page "Testing")."""
+    i = np.arange(n)
+    return ((i % 10).astype(np.float32) * np.float32(0.1)).astype(np.float16)
+
+
+# ---------------------------------------------------------------- decoder
+
+
+def pin_half_decoder_all_patterns(orc):
+    """Every binary16 pattern decodes to numpy's own fp16->fp64 value."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.half_to_double(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "NaN patterns differ"
+    assert np.array_equal(got[~nan], ref[~nan]), "finite/inf patterns differ"
+    # sign of zero is kept
+    assert math.copysign(1.0, got[0x8000]) == -1.0
+
+
+# ---------------------------------------------------------------- scores
+
+
+def pin_one_hot_query_scores(orc):
+    """q = e_i gives s[h,p] = k[p,h,i] / sqrt(D); D = 64 makes the scale 1/8 exact."""
+    rng = _rng(1)
+    S, H, D = 9, 3, 64
+    k = _randn_f16(rng, (S, H, D))
+    v = _randn_f16(rng, (S, H, D))
+    q = np.zeros((H, D), np.float16)
+    picks = [5, 17, 63]
+    for h, i in enumerate(picks):
+        q[h, i] = 1.0
+    _, s, _ = orc.decode(q, k, v, S - 1, want_scores=True)
+    for h, i in enumerate(picks):
+        assert np.array_equal(s[h], k[:, h, i].astype(np.float64) / 8.0), h
+
+
+def pin_all_ones_score(orc):
+    """q = k = 1 gives s = D / sqrt(D) = sqrt(D) (exact for D = 16, 64, 256)."""
+    for D in (16, 64, 256):
+        q = np.ones((2, D), np.float16)
+        k = np.ones((3, 2, D), np.float16)
+        _, s, _ = orc.decode(q, k, k, 2, want_scores=True)
+        assert np.all(s == math.sqrt(D)), D
+
+
+def pin_page_cases_exact_scores(orc):
+    """The page's three test cases: scores equal the exact dot product times
+    1/sqrt(D) (to 1e-14 relative, far inside the page's 0.5), and every
+    position after current_pos reads back as exactly -inf.
+
+    Exactness: every finite fp16 value times 2^24 is an integer, so the dot
+    product times 2^48 is an exact int64 sum here (|values| < 1)."""
+    meta = page_cases()
+    for case in meta["cases"]:
+        H, D, S, cp = case["n_heads"], case["head_dim"], case["seq_len"], case["current_pos"]
+        q = _page_fill(H * D).reshape(H, D)
+        k = _page_fill(S * H * D).reshape(S, H, D)
+        _, s, _ = orc.decode(q, k, k, cp, want_scores=True)
+        qi = (q.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+        ki = (k.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+        assert np.all(q.astype(np.float64) * 2.0 ** 24 == qi)
+        assert np.abs(qi).max() * np.abs(ki).max() * D < 2 ** 62
+        exact = np.einsum("hd,phd->hp", qi, ki)          # int64, exact
+        ref = exact.astype(np.float64) / 2.0 ** 48 / math.sqrt(D)
+        L = cp + 1
+        assert np.all(s[:, L:] == -math.inf), case["name"]
+        err = np.abs(s[:, :L] - ref[:, :L])
+        assert np.all(err <= 1e-14 * np.maximum(1.0, np.abs(ref[:, :L]))), case["name"]
+        assert np.all(err < meta["score_tolerance_abs"])
+
+
+# ---------------------------------------------------------------- softmax
+
+
+def pin_weights_sum_to_one(orc):
+    rng = _rng(2)
+    for (S, H, D, cp) in [(50, 3, 16, 49), (70, 2, 40, 20), (5, 1, 8, 0)]:
+        q = _randn_f16(rng, (H, D), 3.0)
+        k = _randn_f16(rng, (S, H, D))
+        _, _, w = orc.decode(q, k, k, cp, want_weights=True)
+        assert np.all(np.abs(w.sum(axis=1) - 1.0) <= 1e-12)
+        assert np.all(w[:, cp + 1:] == 0.0)
+        assert np.all(w[:, : cp + 1] > 0.0)
+
+
+def pin_two_positions_closed_form(orc):
+    """Two positions with s0 = a/2, s1 = b/2 (D = 4, q = e_0): w0 = 1/(1+e^{s1-s0})."""
+    D, H = 4, 1
+    for a, b in [(1.0, 3.0), (-2.5, 4.0), (7.0, 7.0)]:
+        q = np.array([[1, 0, 0, 0]], np.float16)
+        k = np.zeros((2, H, D), np.float16)
+        k[0, 0, 0], k[1, 0, 0] = a, b
+        v = np.zeros((2, H, D), np.float16)
+        v[0, 0, :] = [1, 2, -1, 0.5]
+        v[1, 0, :] = [-3, 0.25, 4, 1]
+        out, s, w = orc.decode(q, k, v, 1, want_scores=True, want_weights=True)
+        assert s[0, 0] == a / 2 and s[0, 1] == b / 2
+        w0 = 1.0 / (1.0 + math.exp(b / 2 - a / 2))
+        assert abs(w[0, 0] - w0) <= 1e-15 and abs(w[0, 1] - (1 - w0)) <= 1e-15
+        ref = w0 * v[0, 0].astype(np.float64) + (1 - w0) * v[1, 0].astype(np.float64)
+        assert np.allclose(out[0], ref, rtol=0, atol=1e-14)
+
+
+def pin_large_scores_stay_finite(orc):
+    """Scores in the thousands: the max-shifted softmax of the page stays
+    finite and picks the largest score's row (exp without the shift overflows)."""
+    D, H, S = 16, 2, 6
+    q = np.full((H, D), 60.0, np.float16)
+    k = np.zeros((S, H, D), np.float16)
+    k[:, 0, :] = np.array([10, 20, 30, 40, 50, 45], np.float16)[:, None]   # best p=4
+    k[:, 1, :] = -np.array([10, 20, 30, 40, 50, 45], np.float16)[:, None]  # best p=0
+    rng = _rng(3)
+    v = _randn_f16(rng, (S, H, D))
+    out, s, _ = orc.decode(q, k, v, S - 1, want_scores=True)
+    assert np.all(np.isfinite(out))
+    assert s[0, 4] == 60.0 * 50.0 * D / 4.0
+    assert np.array_equal(out[0], v[4, 0].astype(np.float64))
+    assert np.array_equal(out[1], v[0, 1].astype(np.float64))
+
+
+# ---------------------------------------------------------------- PV
+
+
+def pin_identical_keys_give_mean_of_values(orc):
+    rng = _rng(4)
+    S, H, D, cp = 40, 3, 24, 29
+    q = _randn_f16(rng, (H, D), 2.0)
+    k = np.broadcast_to(_randn_f16(rng, (1, H, D)), (S, H, D)).copy()
+    v = _randn_f16(rng, (S, H, D))
+    out, _, _ = orc.decode(q, k, v, cp)
+    ref = v[: cp + 1].astype(np.float64).mean(axis=0)
+    assert np.allclose(out, ref, rtol=0, atol=1e-14)
+
+
+def pin_dominant_score_returns_its_row(orc):
+    """K[p*,h] = q[h] and every other K row 0: s_{p*} - s_other = |q|^2/sqrt(D) = 50.9,
+    so the output is V[p*] up to about 32 e^-50.9."""
+    rng = _rng(5)
+    S, H, D = 33, 4, 32
+    q = (3.0 * rng.choice([-1.0, 1.0], (H, D))).astype(np.float16)
+    k = np.zeros((S, H, D), np.float16)
+    stars = [0, 7, 20, 32]
+    for h, p in enumerate(stars):
+        k[p, h] = q[h]
+    v = _randn_f16(rng, (S, H, D))
+    out, _, _ = orc.decode(q, k, v, S - 1)
+    for h, p in enumerate(stars):
+        assert np.allclose(out[h], v[p, h].astype(np.float64), rtol=0, atol=1e-15), h
+
+
+def pin_first_position_only(orc):
+    """current_pos = 0: one weight equal to 1, the output is V[0] exactly."""
+    rng = _rng(6)
+    S, H, D = 12, 5, 20
+    q = _randn_f16(rng, (H, D), 4.0)
+    k = _randn_f16(rng, (S, H, D), 4.0)
+    v = _randn_f16(rng, (S, H, D))
+    out, _, _ = orc.decode(q, k, v, 0)
+    assert np.array_equal(out, v[0].astype(np.float64))
+
+
+def pin_masked_rows_never_matter(orc):
+    """Any K/V bits after current_pos (huge, infinite, NaN) leave the output
+    bit-identical, and equal to the cache cut at current_pos."""
+    rng = _rng(7)
+    S, H, D, cp = 30, 3, 16, 17
+    q = _randn_f16(rng, (H, D))
+    k = _randn_f16(rng, (S, H, D))
+    v = _randn_f16(rng, (S, H, D))
+    base, s0, _ = orc.decode(q, k, v, cp, want_scores=True)
+    cut, _, _ = orc.decode(q, k[: cp + 1].copy(), v[: cp + 1].copy(), cp)
+    assert np.array_equal(base, cut)
+    for fill in (np.float16(65504), np.float16(-np.inf), np.float16(np.nan)):
+        k2, v2 = k.copy(), v.copy()
+        k2[cp + 1:] = fill
+        v2[cp + 1:] = -fill
+        out, s2, _ = orc.decode(q, k2, v2, cp, want_scores=True)
+        assert np.array_equal(out, base)
+        assert np.array_equal(s2, s0)
+    k3 = k.copy()
+    k3[cp + 1:] = _randn_f16(rng, (S - cp - 1, H, D), 10.0)
+    out, _, _ = orc.decode(q, k3, v, cp)
+    assert np.array_equal(out, base)
+
+
+def pin_current_pos_beyond_cache_masks_nothing(orc):
+    rng = _rng(8)
+    S, H, D = 21, 2, 8
+    q = _randn_f16(rng, (H, D))
+    k = _randn_f16(rng, (S, H, D))
+    v = _randn_f16(rng, (S, H, D))
+    a, sa, _ = orc.decode(q, k, v, S - 1, want_scores=True)
+    for cp in (S, S + 7, 2 ** 32 - 1):
+        b, sb, _ = orc.decode(q, k, v, cp, want_scores=True)
+        assert np.array_equal(a, b) and np.array_equal(sa, sb)
+    assert np.all(np.isfinite(sa))
+
+
+# ---------------------------------------------------------------- independent formulas
+
+
+def direct_formula(q, k, v, cp):
+    """exp(s)/sum(exp(s)) with no max shift, from numpy's fp16 decoding
+    (valid for small |s|).  Shapes: q [H,D], k/v [S,H,D]."""
+    D = q.shape[-1]
+    L = min(cp, k.shape[0] - 1) + 1
+    qf = q.astype(np.float64)
+    kf = k[:L].astype(np.float64)
+    vf = v[:L].astype(np.float64)
+    s = np.einsum("hd,phd->hp", qf, kf) / np.sqrt(D)
+    e = np.exp(s)
+    w = e / e.sum(axis=1, keepdims=True)
+    return np.einsum("hp,phd->hd", w, vf), s
+
+
+def pin_direct_formula_bruteforce(orc):
+    rng = _rng(9)
+    shapes = [(1, 1, 1, 0), (7, 3, 5, 6), (13, 2, 48, 9), (35, 8, 48, 34), (64, 12, 64, 31),
+              (3, 5, 130, 2), (100, 4, 256, 99), (17, 9, 7, 16)]
+    for (S, H, D, cp) in shapes:
+        q = _randn_f16(rng, (H, D))
+        k = _randn_f16(rng, (S, H, D))
+        v = _randn_f16(rng, (S, H, D))
+        out, s, _ = orc.decode(q, k, v, cp, want_scores=True)
+        ref, sref = direct_formula(q, k, v, cp)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-13), (S, H, D, cp)
+        assert np.allclose(s[:, : cp + 1], sref, rtol=1e-12, atol=1e-13), (S, H, D, cp)
+
+
+def pin_torch_sdpa_float64(orc):
+    """torch's own scaled_dot_product_attention in float64 on the CPU, with
+    its default 1/sqrt(D) scale and a boolean mask hiding p > current_pos."""
+    rng = _rng(10)
+    for (S, H, D, cp) in [(40, 4, 64, 25), (19, 3, 48, 18), (9, 2, 128, 0)]:
+        q = _randn_f16(rng, (H, D), 2.0)
+        k = _randn_f16(rng, (S, H, D))
+        v = _randn_f16(rng, (S, H, D))
+        out, _, _ = orc.decode(q, k, v, cp)
+        qt = torch.from_numpy(q.astype(np.float64)).view(H, 1, D)
+        kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2).contiguous()
+        vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2).contiguous()
+        mask = (torch.arange(S) <= cp).view(1, 1, S).expand(H, 1, S)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+        assert np.allclose(out, ref.view(H, D).numpy(), rtol=1e-12, atol=1e-13), (S, H, D, cp)
+
+
+# ---------------------------------------------------------------- invariants
+
+
+def pin_position_permutation_invariance(orc):
+    rng = _rng(11)
+    S, H, D, cp = 26, 3, 32, 21
+    q = _randn_f16(rng, (H, D))
+    k = _randn_f16(rng, (S, H, D))
+    v = _randn_f16(rng, (S, H, D))
+    base, _, _ = orc.decode(q, k, v, cp)
+    perm = np.concatenate([rng.permutation(cp + 1), np.arange(cp + 1, S)])
+    out, _, _ = orc.decode(q, k[perm].copy(), v[perm].copy(), cp)
+    assert np.allclose(out, base, rtol=0, atol=1e-14)
+
+
+def pin_linear_in_values(orc):
+    """out(V1 + V2) = out(V1) + out(V2) with V1, V2 small integers (exact in fp16)."""
+    rng = _rng(12)
+    S, H, D, cp = 20, 2, 16, 14
+    q = _randn_f16(rng, (H, D))
+    k = _randn_f16(rng, (S, H, D))
+    v1 = rng.integers(-8, 8, (S, H, D)).astype(np.float16)
+    v2 = rng.integers(-8, 8, (S, H, D)).astype(np.float16)
+    o1, _, _ = orc.decode(q, k, v1, cp)
+    o2, _, _ = orc.decode(q, k, v2, cp)
+    o12, _, _ = orc.decode(q, k, (v1 + v2).astype(np.float16), cp)
+    assert np.allclose(o12, o1 + o2, rtol=0, atol=1e-13)
+
+
+def pin_heads_are_independent(orc):
+    """Changing the cache of one head leaves every other head's output alone."""
+    rng = _rng(13)
+    S, H, D, cp = 15, 4, 8, 14
+    q = _randn_f16(rng, (H, D))
+    k = _randn_f16(rng, (S, H, D))
+    v = _randn_f16(rng, (S, H, D))
+    base, _, _ = orc.decode(q, k, v, cp)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 2] = _randn_f16(rng, (S, D))
+    v2[:, 2] = _randn_f16(rng, (S, D))
+    out, _, _ = orc.decode(q, k2, v2, cp)
+    for h in (0, 1, 3):
+        assert np.array_equal(out[h], base[h])
+    assert not np.array_equal(out[2], base[2])
+
+
+ALL_PINS = [
+    pin_half_decoder_all_patterns,
+    pin_one_hot_query_scores,
+    pin_all_ones_score,
+    pin_page_cases_exact_scores,
+    pin_weights_sum_to_one,
+    pin_two_positions_closed_form,
+    pin_large_scores_stay_finite,
+    pin_identical_keys_give_mean_of_values,
+    pin_dominant_score_returns_its_row,
+    pin_first_position_only,
+    pin_masked_rows_never_matter,
+    pin_current_pos_beyond_cache_masks_nothing,
+    pin_direct_formula_bruteforce,
+    pin_torch_sdpa_float64,
+    pin_position_permutation_invariance,
+    pin_linear_in_values,
+    pin_heads_are_independent,
+]

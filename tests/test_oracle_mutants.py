@@ -1,0 +1,53 @@
+"""Plant mistakes in copies of the oracle source and check that the pins notice.
+
+Each mutant is a one-line edit of ``oracle/attn_oracle.c`` of the kind that
+slips into a hand-written attention routine (a dropped term, a wrong sign,
+index or operand).  The copy is built in a temporary directory on the CPU;
+every mutant must fail at least one pin.  No GPU is involved.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import _build
+import oracle_pins
+
+MUTANTS = {
+    "scale_dropped": ("s[p] = dot * scale;", "s[p] = dot;"),
+    "scale_without_sqrt": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
+    "k_layout_transposed": ("k[(p * H + h) * D + i]", "k[(h * S + p) * D + i]"),
+    "v_always_head0": ("v[(p * H + h) * D + d]", "v[(p * H) * D + d]"),
+    "v_positions_reversed": ("v[(p * H + h) * D + d]", "v[((L - 1 - p) * H + h) * D + d]"),
+    "q_always_head0": ("q[h * D + i]", "q[i]"),
+    "mask_one_past": ("(size_t)current_pos : S - 1) + 1;", "(size_t)current_pos + 1 : S - 1) + 1;"),
+    "shift_sign_flipped": ("e[p] = exp(s[p] - m);", "e[p] = exp(m - s[p]);"),
+    "min_instead_of_max": ("if (s[p] > m)", "if (s[p] < m)"),
+    "not_normalised": ("acc += (e[p] / z) *", "acc += e[p] *"),
+    "decoder_bias_off": ("expo - 25", "expo - 24"),
+    "decoder_subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "decoder_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+    "decoder_implicit_bit_dropped": ("(1024 + frac)", "(frac)"),
+    "masked_score_zero": ("p < L ? s[p] : -INFINITY", "p < L ? s[p] : 0.0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(_build.SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, "mutation site missing: %r" % old
+    mutated = src.replace(old, new)
+    c_path = os.path.join(tmp_path, "mutant.c")
+    with open(c_path, "w") as f:
+        f.write(mutated)
+    lib = _build.build(src=c_path, lib=os.path.join(tmp_path, "libmutant.so"))
+    orc = oracle.OracleLib(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, RuntimeError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, "no pin caught mutant %s" % name
