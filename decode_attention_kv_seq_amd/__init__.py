@@ -1,0 +1,216 @@
+"""decode_attention_kv_seq_amd -- fp16 single-query decode attention on MI355X.
+
+A thin Python binding over ``libattn_decode.so`` (declared in
+``include/attn_decode.h``).  This module only checks and marshals
+arguments: every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and the stream; calls enqueue on
+``torch.cuda.current_stream()`` unless a stream is given.
+
+The operation (page "Developing Apple Metal Kernels in Rust - A Deep Dive
+Through Attention", section "The MSL, briefly"): per head,
+``softmax(q . K^T / sqrt(head_dim))`` over positions ``0..current_pos``,
+then the weighted sum of V; K and V laid out ``[seq_len, n_heads, head_dim]``,
+q and the output ``[n_heads, head_dim]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_decode.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DIM", 3: "ATTN_ERR_ALIGN",
+                4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_HIP"}
+MAX_HEAD_DIM = 256
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), detail))
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library.  There is no fallback: a missing library is an error."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libattn_decode.so is not built (%s); run "
+                          "`python -m decode_attention_kv_seq_amd._build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, sz, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32
+    lib.attn_decode_workspace_bytes.argtypes = [u32, u32, u32, u32]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode_f16.argtypes = [vp, vp, vp, vp, u32, u32, u32, u32, vp, vp, sz, vp]
+    lib.attn_decode_f16.restype = ctypes.c_int
+    lib.attn_decode_f16_batched.argtypes = [vp, vp, vp, vp, vp, u32, u32, u32, u32, vp, vp, sz, vp]
+    lib.attn_decode_f16_batched.restype = ctypes.c_int
+    lib.attn_decode_f16_split.argtypes = [vp, vp, vp, vp, u32, u32, u32, u32, u32, vp, vp, sz, vp]
+    lib.attn_decode_f16_split.restype = ctypes.c_int
+    lib.attn_decode_f16_combine.argtypes = [vp, vp, u32, u32, u32, u32, u32, vp, sz, vp]
+    lib.attn_decode_f16_combine.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, _lib.attn_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _req(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def workspace_bytes(batch: int, n_heads: int, head_dim: int, seq_len: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(batch, n_heads, head_dim, seq_len))
+
+
+def alloc_workspace(batch, n_heads, head_dim, seq_len, device) -> torch.Tensor:
+    n = workspace_bytes(batch, n_heads, head_dim, seq_len)
+    if n == 0:
+        raise ValueError("invalid sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _cp_tensor(cp: torch.Tensor, batch: int, device) -> torch.Tensor:
+    if not isinstance(cp, torch.Tensor) or cp.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("current_pos must be an int32/uint32 GPU tensor")
+    _req(cp, "current_pos", cp.dtype, device)
+    if tuple(cp.shape) != (batch,):
+        raise ValueError("current_pos must have shape [%d]" % batch)
+    return cp
+
+
+def decode(q, k, v, current_pos: int, *, out=None, dump: bool = False, workspace=None,
+           stream=None):
+    """One sequence: q [H, D], k/v [S, H, D] fp16 -> out [H, D] fp16.
+
+    With ``dump=True`` also returns the fp32 score dump [H, S] (natural-log
+    units, -inf after current_pos)."""
+    lib = load_library()
+    _req(k, "k", torch.float16)
+    dev = k.device
+    _req(q, "q", torch.float16, dev)
+    _req(v, "v", torch.float16, dev)
+    if k.dim() != 3 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [seq_len, n_heads, head_dim]")
+    S, H, D = k.shape
+    if tuple(q.shape) != (H, D):
+        raise ValueError("q must be [n_heads, head_dim] = [%d, %d]" % (H, D))
+    if not 0 <= int(current_pos) <= 0xFFFFFFFF:
+        raise ValueError("current_pos must fit in uint32")
+    if out is None:
+        out = torch.empty((H, D), dtype=torch.float16, device=dev)
+    _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != (H, D):
+        raise ValueError("out must be [n_heads, head_dim]")
+    sc = torch.empty((H, S), dtype=torch.float32, device=dev) if dump else None
+    if workspace is None:
+        workspace = alloc_workspace(1, H, D, S, dev)
+    _check(lib.attn_decode_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, D, S, int(current_pos),
+                               _ptr(sc), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream_handle(stream)))
+    return (out, sc) if dump else out
+
+
+def decode_batched(q, k, v, current_pos, *, out=None, dump: bool = False, workspace=None,
+                   stream=None):
+    """Ragged batch: q [B, H, D], k/v [B, S, H, D] fp16, current_pos int32 [B]
+    on the GPU -> out [B, H, D] fp16 (and the dump [B, H, S] with dump=True)."""
+    lib = load_library()
+    _req(k, "k", torch.float16)
+    dev = k.device
+    _req(q, "q", torch.float16, dev)
+    _req(v, "v", torch.float16, dev)
+    if k.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [batch, capacity, n_heads, head_dim]")
+    B, S, H, D = k.shape
+    if tuple(q.shape) != (B, H, D):
+        raise ValueError("q must be [batch, n_heads, head_dim]")
+    cp = _cp_tensor(current_pos, B, dev)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float16, device=dev)
+    _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [batch, n_heads, head_dim]")
+    sc = torch.empty((B, H, S), dtype=torch.float32, device=dev) if dump else None
+    if workspace is None:
+        workspace = alloc_workspace(B, H, D, S, dev)
+    _check(lib.attn_decode_f16_batched(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cp), B, H, D, S,
+                                       _ptr(sc), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream)))
+    return (out, sc) if dump else out
+
+
+def _batch_view(q, k, v):
+    """Accept single-sequence (3-D cache) or batched (4-D cache) tensors."""
+    if k.dim() == 3:
+        return q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+    return q, k, v
+
+
+def split(q, k, v, current_pos, workspace, *, dump=None, stream=None):
+    """First launch of a decode: stream the cache into the workspace.
+
+    ``current_pos`` is an int (every sequence) or an int32 GPU tensor [B]."""
+    lib = load_library()
+    q3, k4, v4 = _batch_view(q, k, v)
+    for t, n in ((q3, "q"), (k4, "k"), (v4, "v")):
+        _req(t, n, torch.float16, k.device)
+    B, S, H, D = k4.shape
+    if tuple(v4.shape) != tuple(k4.shape) or tuple(q3.shape) != (B, H, D):
+        raise ValueError("shape mismatch")
+    cp_dev, cp_host = (None, int(current_pos)) if not isinstance(current_pos, torch.Tensor) \
+        else (_cp_tensor(current_pos, B, k.device), 0)
+    _check(lib.attn_decode_f16_split(_ptr(q3), _ptr(k4), _ptr(v4), _ptr(cp_dev), cp_host, B, H, D, S,
+                                     _ptr(dump), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream)))
+
+
+def combine(out, current_pos, batch, n_heads, head_dim, seq_len, workspace, *, stream=None):
+    """Second launch: merge the workspace partials into ``out``."""
+    lib = load_library()
+    _req(out, "out", torch.float16)
+    cp_dev, cp_host = (None, int(current_pos)) if not isinstance(current_pos, torch.Tensor) \
+        else (_cp_tensor(current_pos, batch, out.device), 0)
+    _check(lib.attn_decode_f16_combine(_ptr(out), _ptr(cp_dev), cp_host, batch, n_heads, head_dim,
+                                       seq_len, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream)))
+    return out

@@ -1,0 +1,775 @@
+// attn_decode.hip -- split-sequence decode attention for gfx950 (MI355X).
+//
+// The computation is the masked, scaled Q.K^T followed by softmax and the
+// probability-weighted sum of V that the page "Developing Apple Metal Kernels
+// in Rust - A Deep Dive Through Attention" defines in section "The MSL,
+// briefly".  The page runs it as two dispatches with an fp16 score buffer in
+// between; here the cache is read once:
+//
+//   split kernel    one workgroup streams one chunk of positions for one or
+//                   more heads with 16-byte loads, takes fp32 dot products
+//                   (v_dot2 on the fp16 inputs), reduces them inside a lane
+//                   group with DPP, and keeps an online softmax state
+//                   (running max m, running sum l, weighted V sum o) in
+//                   registers, in base-2 units.  Lane groups that share a
+//                   head merge through LDS; the workgroup writes one partial
+//                   (m, l, o[D]) per head, or the final fp16 row when a single
+//                   chunk covers the sequence.
+//   combine kernel  one workgroup per (sequence, head) merges the chunk
+//                   partials: M = max m_c, l = sum l_c 2^(m_c-M),
+//                   out = sum o_c 2^(m_c-M) / l, rounded to fp16.
+//
+// Positions after current_pos are never loaded.  MFMA is not used: one query
+// row per head makes this a matrix-vector product bound by HBM bandwidth.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "attn_decode.h"
+
+namespace {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;            // waves per split workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kUnroll = 4;           // positions per lane group per loop trip
+constexpr int kCombineThreads = 256;
+
+// ------------------------------------------------------------------ packs
+// A pack is VEC consecutive fp16 values of one row held by one lane.
+
+template <int VEC> struct Pack;
+template <> struct Pack<8> { u32x4 w; };
+template <> struct Pack<4> { u32x2 w; };
+template <> struct Pack<2> { uint32_t w; };
+template <> struct Pack<1> { uint16_t w; };
+
+template <int VEC>
+__device__ __forceinline__ Pack<VEC> load_pack(const uint16_t *p) {
+    Pack<VEC> r;
+    if constexpr (VEC == 8) r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    else if constexpr (VEC == 4) r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    else if constexpr (VEC == 2) r.w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+    else r.w = __builtin_nontemporal_load(p);
+    return r;
+}
+
+template <int VEC>
+__device__ __forceinline__ Pack<VEC> zero_pack() {
+    Pack<VEC> r;
+    if constexpr (VEC == 8) r.w = u32x4{0u, 0u, 0u, 0u};
+    else if constexpr (VEC == 4) r.w = u32x2{0u, 0u};
+    else r.w = 0;
+    return r;
+}
+
+template <int VEC>
+__device__ __forceinline__ uint32_t pack_word(const Pack<VEC> &p, int j) {
+    if constexpr (VEC == 8) return p.w[j];
+    else if constexpr (VEC == 4) return p.w[j];
+    else return p.w;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// element e (0..VEC-1) of a pack as fp32
+template <int VEC>
+__device__ __forceinline__ float pack_elem(const Pack<VEC> &p, int e) {
+    if constexpr (VEC == 1) return h2f(p.w);
+    else {
+        uint32_t w = pack_word<VEC>(p, e >> 1);
+        return h2f((e & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+}
+
+// acc + sum_e a[e]*b[e] with fp32 accumulation of exact fp16 products
+template <int VEC>
+__device__ __forceinline__ float dot_pack(const Pack<VEC> &a, const Pack<VEC> &b, float acc) {
+    if constexpr (VEC == 1) {
+        return fmaf(h2f(a.w), h2f(b.w), acc);
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC / 2; ++j)
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pack_word<VEC>(a, j)),
+                                         __builtin_bit_cast(half2v, pack_word<VEC>(b, j)), acc,
+                                         false);
+        return acc;
+    }
+}
+
+// ------------------------------------------------------- lane-group sums
+// Sum over aligned groups of GL lanes; every lane of a group ends with the
+// same bits (each step adds a pair of values in both orders' common result).
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+template <int GL>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (GL >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+    if constexpr (GL >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    if constexpr (GL >= 8) x += dpp<0x141>(x);   // row_half_mirror
+    if constexpr (GL >= 16) x += dpp<0x140>(x);  // row_mirror
+    if constexpr (GL >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (GL >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t valid_len(uint32_t cp, uint32_t S) {
+    return (cp < S - 1u ? cp : S - 1u) + 1u;
+}
+
+__device__ __forceinline__ uint16_t f2h_rne(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// ------------------------------------------------------------ split kernel
+
+struct SplitArgs {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *v;
+    const uint32_t *cp_dev;   // per-sequence current_pos, or null
+    uint32_t cp_host;         // used when cp_dev is null
+    uint32_t H, D, S;         // heads, head_dim, cache length per sequence
+    uint32_t chunk;           // positions per workgroup
+    uint32_t n_hb;            // head blocks (H / hpb)
+    uint32_t hpb;             // heads per workgroup
+    uint32_t nc_stride;       // chunk stride of the partial arrays
+    float scale_log2;         // log2(e) / sqrt(D)
+    float scale;              // 1 / sqrt(D)
+    float *part_o;            // [B, H, nc_stride, D]
+    float *part_ml;           // [B, H, nc_stride, 2]
+    uint16_t *out;            // final rows when `direct`
+    float *dump;              // [B, H, S] or null
+    int direct;               // 1: one chunk per sequence, write fp16 rows
+};
+
+// VEC: fp16 values per lane load; GL: lanes per row (power of two);
+// NV: packs per lane per row; FULL: D == VEC*GL*NV (no element guards).
+template <int VEC, int GL, int NV, bool FULL, bool DUMP>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
+    constexpr int RG = 64 / GL;              // row groups per wave
+    constexpr int NG = kWaves * RG;          // row groups per workgroup
+    constexpr int DPAD = VEC * GL * NV;      // padded row length in LDS
+
+    __shared__ float sm_o[NG * DPAD];
+    __shared__ float sm_m[NG];
+    __shared__ float sm_l[NG];
+
+    const uint32_t b = blockIdx.y;
+    const uint32_t hb = blockIdx.x % a.n_hb;
+    const uint32_t chunk = blockIdx.x / a.n_hb;
+    const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
+    const uint32_t L = valid_len(cp, a.S);
+    const uint32_t c0 = chunk * a.chunk;
+    if (c0 >= L) return;                     // whole workgroup: nothing to read
+    const uint32_t c_end = min(c0 + a.chunk, L);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int g = (tid >> 6) * RG + lane / GL;   // row group in the workgroup
+    const int gl = lane % GL;                    // lane inside the row group
+    const uint32_t hg = (uint32_t)g % a.hpb;     // head inside the head block
+    const uint32_t pg = (uint32_t)g / a.hpb;     // position lane
+    const uint32_t pps = NG / a.hpb;             // positions per step
+    const uint32_t h = hb * a.hpb + hg;
+    const size_t D = a.D;
+    const size_t HD = (size_t)a.H * D;
+
+    // element offsets of this lane's packs and their validity
+    int eoff[NV];
+    bool eok[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        eoff[j] = (gl + GL * j) * VEC;
+        eok[j] = FULL || eoff[j] < (int)a.D;
+    }
+
+    Pack<VEC> qp[NV];
+    const uint16_t *qrow = a.q + ((size_t)b * a.H + h) * D;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        qp[j] = eok[j] ? load_pack<VEC>(qrow + eoff[j]) : zero_pack<VEC>();
+
+    const size_t seq_base = (size_t)b * a.S * HD + (size_t)h * D;
+    const uint16_t *kbase = a.k + seq_base;
+    const uint16_t *vbase = a.v + seq_base;
+
+    float m = -INFINITY, l = 0.f;
+    float acc[NV][VEC];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[j][e] = 0.f;
+
+    const uint32_t step = pps * kUnroll;
+    for (uint32_t base = c0; base < c_end; base += step) {
+        Pack<VEC> kr[kUnroll][NV], vr[kUnroll][NV];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t p = base + u * pps + pg;
+            ok[u] = p < c_end;
+            const size_t row = (size_t)(ok[u] ? p : c0) * HD;   // clamp: never past L
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                kr[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
+                vr[u][j] = eok[j] ? load_pack<VEC>(vbase + row + eoff[j]) : zero_pack<VEC>();
+            }
+        }
+        float t[kUnroll];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], kr[u][j], dot);
+            dot = group_sum<GL>(dot);
+            t[u] = ok[u] ? dot * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, t[u]);
+            if constexpr (DUMP) {
+                if (ok[u] && gl == 0)
+                    a.dump[((size_t)b * a.H + h) * a.S + base + u * pps + pg] = dot * a.scale;
+            }
+        }
+        const float m_new = fmaxf(m, tmax);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // group saw no position yet
+        const float corr = __builtin_amdgcn_exp2f(m - m_use);
+        l *= corr;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[j][e] *= corr;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const float pw = __builtin_amdgcn_exp2f(t[u] - m_use);   // 0 for masked slots
+            l += pw;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    acc[j][e] = fmaf(pw, pack_elem<VEC>(vr[u][j], e), acc[j][e]);
+        }
+        m = m_new;
+    }
+
+    // ---- merge the row groups that share a head
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sm_o[g * DPAD + eoff[j] + e] = acc[j][e];
+    if (gl == 0) {
+        sm_m[g] = m;
+        sm_l[g] = l;
+    }
+    __syncthreads();
+
+    const uint32_t n_out = a.hpb * a.D;
+    for (uint32_t idx = tid; idx < n_out; idx += kThreads) {
+        const uint32_t ho = idx / a.D;
+        const uint32_t d = idx % a.D;
+        float M = -INFINITY;
+        for (uint32_t r = 0; r < pps; ++r) M = fmaxf(M, sm_m[r * a.hpb + ho]);
+        // position lane 0 always saw position c0, so M is finite
+        float o = 0.f, lsum = 0.f;
+        for (uint32_t r = 0; r < pps; ++r) {
+            const int gg = r * a.hpb + ho;
+            const float w = __builtin_amdgcn_exp2f(sm_m[gg] - M);
+            o = fmaf(sm_o[gg * DPAD + d], w, o);
+            lsum = fmaf(sm_l[gg], w, lsum);
+        }
+        const uint32_t hh = hb * a.hpb + ho;
+        const size_t bh = (size_t)b * a.H + hh;
+        if (a.direct) {
+            a.out[bh * a.D + d] = f2h_rne(o / lsum);
+        } else {
+            const size_t slot = bh * a.nc_stride + chunk;
+            a.part_o[slot * a.D + d] = o;
+            if (d == 0) {
+                a.part_ml[slot * 2] = M;
+                a.part_ml[slot * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------- combine kernel
+
+struct CombineArgs {
+    const float *part_o;
+    const float *part_ml;
+    const uint32_t *cp_dev;
+    uint32_t cp_host;
+    uint32_t H, D, S, chunk, nc_stride;
+    uint16_t *out;
+};
+
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineArgs a) {
+    __shared__ float sm_red[kCombineThreads / 64];
+    __shared__ float sm_acc[kCombineThreads];
+    __shared__ float sm_l[kCombineThreads];
+
+    const uint32_t h = blockIdx.x;
+    const uint32_t b = blockIdx.y;
+    const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
+    const uint32_t L = valid_len(cp, a.S);
+    const uint32_t nc = (L + a.chunk - 1) / a.chunk;
+    const size_t bh = (size_t)b * a.H + h;
+    const float *ml = a.part_ml + bh * a.nc_stride * 2;
+    const float *po = a.part_o + bh * a.nc_stride * a.D;
+    const int tid = threadIdx.x;
+
+    // M = max over chunks
+    float mx = -INFINITY;
+    for (uint32_t c = tid; c < nc; c += kCombineThreads) mx = fmaxf(mx, ml[2 * c]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if ((tid & 63) == 0) sm_red[tid >> 6] = mx;
+    __syncthreads();
+    float M = sm_red[0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, sm_red[w]);
+
+    // thread (cg, d): chunks cg, cg+G, ... of element d
+    const uint32_t G = kCombineThreads / a.D;   // >= 1 since D <= 256
+    const uint32_t cg = tid / a.D;
+    const uint32_t d = tid % a.D;
+    float o = 0.f, lsum = 0.f;
+    if (cg < G) {
+        for (uint32_t c = cg; c < nc; c += G) {
+            const float w = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+            o = fmaf(po[(size_t)c * a.D + d], w, o);
+            lsum = fmaf(ml[2 * c + 1], w, lsum);
+        }
+    }
+    sm_acc[tid] = o;
+    sm_l[tid] = lsum;
+    __syncthreads();
+    if (tid < (int)a.D) {
+        float os = 0.f, ls = 0.f;
+        for (uint32_t r = 0; r < G; ++r) {
+            os += sm_acc[r * a.D + tid];
+            ls += sm_l[r * a.D + tid];
+        }
+        a.out[bh * a.D + tid] = f2h_rne(os / ls);
+    }
+}
+
+// ------------------------------------------------------------- dump fill
+
+__global__ __launch_bounds__(256) void attn_dump_fill_kernel(float *dump, const uint32_t *cp_dev,
+                                                             uint32_t cp_host, uint32_t H,
+                                                             uint32_t S, uint64_t total) {
+    for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * 256u) {
+        const uint64_t bh = i / S;
+        const uint32_t p = (uint32_t)(i - bh * S);
+        const uint32_t cp = cp_dev ? cp_dev[bh / H] : cp_host;
+        if (p >= valid_len(cp, S)) dump[i] = -INFINITY;
+    }
+}
+
+// =============================================================== host side
+
+thread_local char g_err[512];
+
+attn_status_t fail(attn_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+attn_status_t ok() {
+    return ATTN_OK;
+}
+
+// Planner constants, sized for 256 compute units.  The ATTN_DECODE_TUNE
+// environment variable ("items=N,cmax=N,hpb=N") overrides them for tuning
+// sweeps; it is read once per process.
+struct Tuning {
+    uint32_t items = 2048;   // target (head, chunk) work items per call
+    uint32_t cmax = 8192;    // largest chunk, positions
+    uint32_t hpb = 1;        // requested heads per workgroup
+};
+constexpr uint32_t kChunkGranule = 64;
+
+const Tuning &tuning() {
+    static const Tuning t = [] {
+        Tuning r;
+        const char *env = getenv("ATTN_DECODE_TUNE");
+        if (env) {
+            char buf[256];
+            snprintf(buf, sizeof buf, "%s", env);
+            for (char *tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+                unsigned v = 0;
+                if (sscanf(tok, "items=%u", &v) == 1 && v > 0) r.items = v;
+                else if (sscanf(tok, "cmax=%u", &v) == 1 && v >= kChunkGranule)
+                    r.cmax = v / kChunkGranule * kChunkGranule;
+                else if (sscanf(tok, "hpb=%u", &v) == 1 && v > 0) r.hpb = v;
+            }
+        }
+        return r;
+    }();
+    return t;
+}
+
+uint64_t cdiv(uint64_t a, uint64_t b) {
+    return (a + b - 1) / b;
+}
+
+struct Plan {
+    uint32_t chunk;       // positions per workgroup
+    uint32_t n_chunks;    // chunks launched per (sequence, head block)
+    uint32_t nc_stride;   // chunk stride in the workspace (an upper bound)
+};
+
+// Chunk count bound used for the workspace layout; depends only on sizes.
+uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t S) {
+    const Tuning &t = tuning();
+    const uint64_t nt = cdiv(t.items, (uint64_t)batch * H);
+    const uint64_t hi = nt > cdiv(S, t.cmax) ? nt : cdiv(S, t.cmax);
+    const uint64_t lo = cdiv(S, kChunkGranule);
+    return (uint32_t)(hi < lo ? hi : lo);
+}
+
+// Chunk size for `span` positions: about `items` work items over the batch,
+// rounded to the granule, clamped to [granule, cmax].
+Plan make_plan(uint32_t batch, uint32_t H, uint32_t S, uint32_t span) {
+    const Tuning &t = tuning();
+    const uint64_t nt = cdiv(t.items, (uint64_t)batch * H);
+    uint64_t c = cdiv(cdiv(span, nt), kChunkGranule) * kChunkGranule;
+    if (c > t.cmax) c = t.cmax;
+    if (c < kChunkGranule) c = kChunkGranule;
+    Plan p;
+    p.chunk = (uint32_t)c;
+    p.n_chunks = (uint32_t)cdiv(span, c);
+    p.nc_stride = chunk_bound(batch, H, S);
+    return p;
+}
+
+size_t workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, size_t *ml_offset) {
+    const size_t slots = (size_t)batch * H * chunk_bound(batch, H, S);
+    const size_t o_bytes = (slots * D * sizeof(float) + 255) / 256 * 256;
+    const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
+    if (ml_offset) *ml_offset = o_bytes;
+    return o_bytes + ml_bytes;
+}
+
+attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
+    if (batch == 0 || H == 0 || D == 0 || S == 0)
+        return fail(ATTN_ERR_DIM, "sizes must be nonzero (batch=%u n_heads=%u head_dim=%u seq_len=%u)",
+                    batch, H, D, S);
+    if (D > ATTN_MAX_HEAD_DIM)
+        return fail(ATTN_ERR_DIM, "head_dim=%u exceeds %u", D, ATTN_MAX_HEAD_DIM);
+    const unsigned __int128 elems = (unsigned __int128)batch * S * H * D;
+    if (elems > ((unsigned __int128)1 << 60))
+        return fail(ATTN_ERR_DIM, "cache of %llu x %u x %u x %u elements is too large",
+                    (unsigned long long)batch, S, H, D);
+    if (S > (1u << 31))
+        return fail(ATTN_ERR_DIM, "seq_len=%u exceeds 2^31", S);
+    if (batch > 65535u)
+        return fail(ATTN_ERR_DIM, "batch=%u exceeds 65535", batch);
+    if ((uint64_t)batch * H > 0x7fffffffull)
+        return fail(ATTN_ERR_DIM, "batch*n_heads too large");
+    return ok();
+}
+
+bool aligned(const void *p, uintptr_t a) {
+    return ((uintptr_t)p & (a - 1)) == 0;
+}
+
+// -------------------------------------------------------- kernel selection
+
+using SplitFn = void (*)(SplitArgs);
+
+struct Layout {
+    int vec, gl, nv;
+    bool full;
+};
+
+uint32_t pow2ceil(uint32_t x) {
+    uint32_t r = 1;
+    while (r < x) r <<= 1;
+    return r;
+}
+
+Layout choose_layout(uint32_t D, const void *q, const void *k, const void *v) {
+    int vec = 1;
+    for (int c : {8, 4, 2}) {
+        const uintptr_t bytes = 2u * c;
+        if (D % c == 0 && aligned(q, bytes) && aligned(k, bytes) && aligned(v, bytes)) {
+            vec = c;
+            break;
+        }
+    }
+    const uint32_t nvec = D / vec;
+    uint32_t gl = pow2ceil(nvec);
+    if (gl > 64) gl = 64;
+    if (gl < 8) gl = 8;
+    const uint32_t nv = (uint32_t)cdiv(nvec, gl);
+    // only the 16-byte layouts have guard-free instantiations
+    Layout L{vec, (int)gl, (int)nv, vec == 8 && (uint32_t)(vec * gl * nv) == D};
+    return L;
+}
+
+template <bool DUMP>
+SplitFn pick_split(const Layout &ly) {
+#define ATTN_CASE(V, G, N, F)                                                          \
+    if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
+        return attn_split_kernel<V, G, N, F, DUMP>;
+    // fast paths: head_dim 64, 128, 256 with 16-byte rows
+    ATTN_CASE(8, 8, 1, true)
+    ATTN_CASE(8, 16, 1, true)
+    ATTN_CASE(8, 32, 1, true)
+    // everything else
+    ATTN_CASE(8, 8, 1, false)
+    ATTN_CASE(8, 16, 1, false)
+    ATTN_CASE(8, 32, 1, false)
+    ATTN_CASE(4, 8, 1, false)
+    ATTN_CASE(4, 16, 1, false)
+    ATTN_CASE(4, 32, 1, false)
+    ATTN_CASE(4, 64, 1, false)
+    ATTN_CASE(2, 8, 1, false)
+    ATTN_CASE(2, 16, 1, false)
+    ATTN_CASE(2, 32, 1, false)
+    ATTN_CASE(2, 64, 1, false)
+    ATTN_CASE(2, 64, 2, false)
+    ATTN_CASE(1, 8, 1, false)
+    ATTN_CASE(1, 16, 1, false)
+    ATTN_CASE(1, 32, 1, false)
+    ATTN_CASE(1, 64, 1, false)
+    ATTN_CASE(1, 64, 2, false)
+    ATTN_CASE(1, 64, 3, false)
+    ATTN_CASE(1, 64, 4, false)
+#undef ATTN_CASE
+    return nullptr;
+}
+
+uint32_t choose_hpb(uint32_t H, const Layout &ly) {
+    const uint32_t ng = kWaves * (64 / ly.gl);
+    uint32_t want = tuning().hpb;
+    uint32_t hpb = 1;
+    for (uint32_t c = 1; c <= want && c <= ng && c <= H; c <<= 1)
+        if (H % c == 0) hpb = c;
+    return hpb;
+}
+
+attn_status_t hip_check(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+    return ok();
+}
+
+// Shared argument checks of the split phase.
+attn_status_t check_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          const uint32_t *cp_dev, uint32_t batch, uint32_t H, uint32_t D,
+                          uint32_t S, const float *dump) {
+    if (!q || !k || !v) return fail(ATTN_ERR_NULL, "q, k_cache and v_cache must be non-NULL");
+    attn_status_t s = check_sizes(batch, H, D, S);
+    if (s != ATTN_OK) return s;
+    if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2))
+        return fail(ATTN_ERR_ALIGN, "fp16 tensors must be 2-byte aligned");
+    if (dump && !aligned(dump, 4)) return fail(ATTN_ERR_ALIGN, "scores_dump must be 4-byte aligned");
+    if (cp_dev && !aligned(cp_dev, 4)) return fail(ATTN_ERR_ALIGN, "current_pos must be 4-byte aligned");
+    return ok();
+}
+
+attn_status_t check_workspace(const void *ws, size_t ws_bytes, uint32_t batch, uint32_t H,
+                              uint32_t D, uint32_t S) {
+    const size_t need = workspace_layout(batch, H, D, S, nullptr);
+    if (!ws) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(ws, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (ws_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                    ws_bytes, need);
+    return ok();
+}
+
+// Enqueue the split kernel (and the dump fill).  `out` non-null and a single
+// chunk per sequence: the split kernel writes the final rows itself.
+attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
+                           uint32_t D, uint32_t S, float *dump, void *ws, uint16_t *out,
+                           hipStream_t stream, bool *wrote_out) {
+    const Layout ly = choose_layout(D, q, k, v);
+    const SplitFn fn = dump ? pick_split<true>(ly) : pick_split<false>(ly);
+    if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
+    const uint32_t hpb = choose_hpb(H, ly);
+    // host current_pos: plan the exact span; device array: plan the capacity
+    const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
+    const Plan plan = make_plan(batch, H, S, span);
+    size_t ml_off = 0;
+    workspace_layout(batch, H, D, S, &ml_off);
+
+    SplitArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cp_dev = cp_dev;
+    a.cp_host = cp_host;
+    a.H = H;
+    a.D = D;
+    a.S = S;
+    a.chunk = plan.chunk;
+    a.n_hb = H / hpb;
+    a.hpb = hpb;
+    a.nc_stride = plan.nc_stride;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    a.scale = (float)(1.0 / sqrt((double)D));
+    a.part_o = ws ? static_cast<float *>(ws) : nullptr;
+    a.part_ml = ws ? reinterpret_cast<float *>(static_cast<char *>(ws) + ml_off) : nullptr;
+    a.direct = (out && plan.n_chunks == 1) ? 1 : 0;
+    a.out = out;
+    a.dump = dump;
+    *wrote_out = a.direct != 0;
+
+    if (dump) {
+        const uint64_t total = (uint64_t)batch * H * S;
+        const uint64_t blocks = cdiv(total, 256) < 4096 ? cdiv(total, 256) : 4096;
+        hipLaunchKernelGGL(attn_dump_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           dump, cp_dev, cp_host, H, S, total);
+        attn_status_t s = hip_check("dump fill launch");
+        if (s != ATTN_OK) return s;
+    }
+    dim3 grid(a.n_hb * plan.n_chunks, batch);
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, a);
+    return hip_check("split kernel launch");
+}
+
+attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_host,
+                             uint32_t batch, uint32_t H, uint32_t D, uint32_t S, const void *ws,
+                             hipStream_t stream) {
+    const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
+    const Plan plan = make_plan(batch, H, S, span);
+    size_t ml_off = 0;
+    workspace_layout(batch, H, D, S, &ml_off);
+    CombineArgs c;
+    c.part_o = static_cast<const float *>(ws);
+    c.part_ml = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ml_off);
+    c.cp_dev = cp_dev;
+    c.cp_host = cp_host;
+    c.H = H;
+    c.D = D;
+    c.S = S;
+    c.chunk = plan.chunk;
+    c.nc_stride = plan.nc_stride;
+    c.out = out;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(H, batch), dim3(kCombineThreads), 0, stream, c);
+    return hip_check("combine kernel launch");
+}
+
+attn_status_t decode_full(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
+                          const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
+                          uint32_t D, uint32_t S, float *dump, void *ws, size_t ws_bytes,
+                          void *stream) {
+    attn_status_t s = check_split(q, k, v, cp_dev, batch, H, D, S, dump);
+    if (s != ATTN_OK) return s;
+    if (!out) return fail(ATTN_ERR_NULL, "out must be non-NULL");
+    if (!aligned(out, 2)) return fail(ATTN_ERR_ALIGN, "out must be 2-byte aligned");
+    s = check_workspace(ws, ws_bytes, batch, H, D, S);
+    if (s != ATTN_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool wrote = false;
+    s = launch_split(q, k, v, cp_dev, cp_host, batch, H, D, S, dump, ws, out, st, &wrote);
+    if (s != ATTN_OK || wrote) return s;
+    return launch_combine(out, cp_dev, cp_host, batch, H, D, S, ws, st);
+}
+
+}  // namespace
+
+// ============================================================== C ABI
+
+extern "C" {
+
+size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t n_heads, uint32_t head_dim,
+                                   uint32_t seq_len) {
+    if (check_sizes(batch, n_heads, head_dim, seq_len) != ATTN_OK) return 0;
+    return workspace_layout(batch, n_heads, head_dim, seq_len, nullptr);
+}
+
+attn_status_t attn_decode_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                              uint16_t *out, uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                              uint32_t current_pos, float *scores_dump, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    return decode_full(q, k_cache, v_cache, out, nullptr, current_pos, 1, n_heads, head_dim,
+                       seq_len, scores_dump, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_f16_batched(const uint16_t *q, const uint16_t *k_cache,
+                                      const uint16_t *v_cache, uint16_t *out,
+                                      const uint32_t *current_pos, uint32_t batch,
+                                      uint32_t n_heads, uint32_t head_dim, uint32_t capacity,
+                                      float *scores_dump, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    if (!current_pos) return fail(ATTN_ERR_NULL, "current_pos must be non-NULL");
+    return decode_full(q, k_cache, v_cache, out, current_pos, 0, batch, n_heads, head_dim,
+                       capacity, scores_dump, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_f16_split(const uint16_t *q, const uint16_t *k_cache,
+                                    const uint16_t *v_cache, const uint32_t *current_pos_dev,
+                                    uint32_t current_pos, uint32_t batch, uint32_t n_heads,
+                                    uint32_t head_dim, uint32_t seq_len, float *scores_dump,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    attn_status_t s = check_split(q, k_cache, v_cache, current_pos_dev, batch, n_heads, head_dim,
+                                  seq_len, scores_dump);
+    if (s != ATTN_OK) return s;
+    s = check_workspace(workspace, workspace_bytes, batch, n_heads, head_dim, seq_len);
+    if (s != ATTN_OK) return s;
+    bool wrote = false;
+    return launch_split(q, k_cache, v_cache, current_pos_dev, current_pos, batch, n_heads,
+                        head_dim, seq_len, scores_dump, workspace, nullptr,
+                        static_cast<hipStream_t>(stream), &wrote);
+}
+
+attn_status_t attn_decode_f16_combine(uint16_t *out, const uint32_t *current_pos_dev,
+                                      uint32_t current_pos, uint32_t batch, uint32_t n_heads,
+                                      uint32_t head_dim, uint32_t seq_len, const void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    if (!out) return fail(ATTN_ERR_NULL, "out must be non-NULL");
+    attn_status_t s = check_sizes(batch, n_heads, head_dim, seq_len);
+    if (s != ATTN_OK) return s;
+    if (!aligned(out, 2)) return fail(ATTN_ERR_ALIGN, "out must be 2-byte aligned");
+    if (current_pos_dev && !aligned(current_pos_dev, 4))
+        return fail(ATTN_ERR_ALIGN, "current_pos must be 4-byte aligned");
+    s = check_workspace(workspace, workspace_bytes, batch, n_heads, head_dim, seq_len);
+    if (s != ATTN_OK) return s;
+    return launch_combine(out, current_pos_dev, current_pos, batch, n_heads, head_dim, seq_len,
+                          workspace, static_cast<hipStream_t>(stream));
+}
+
+const char *attn_status_string(attn_status_t status) {
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_DIM: return "invalid size";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *attn_last_error(void) {
+    return g_err;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+/*
+ * attn_decode.h -- single-query scaled-dot-product decode attention over an
+ * fp16 KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined on the page "Developing Apple Metal
+ * Kernels in Rust - A Deep Dive Through Attention", section "The MSL,
+ * briefly" (kernels attention_qk_f16 and attention_pv_f16), computed in one
+ * pass over the cache instead of the page's two dispatches:
+ *
+ *   s[h,p]   = (sum_i q[h,i] * k[p,h,i]) / sqrt(head_dim)   for p <= current_pos
+ *   w[h,:]   = softmax over p <= current_pos of s[h,p]      (positions after
+ *              current_pos are masked: weight 0, never read)
+ *   out[h,d] = sum_p w[h,p] * v[p,h,d]
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers on the current HIP device.  fp16
+ *    means IEEE binary16 bits.  All tensors are dense and row-major
+ *    (contiguous), as the page's layouts are.
+ *  - Layouts (page section "The MSL, briefly"): Q and out [n_heads, head_dim];
+ *    K and V caches [seq_len, n_heads, head_dim]; element (p,h,i) of the
+ *    cache at (p*n_heads + h)*head_dim + i.  Batched forms put a leading
+ *    [batch] dimension on every tensor: caches [batch, seq_len, n_heads,
+ *    head_dim], Q/out [batch, n_heads, head_dim].
+ *  - current_pos is the index of the newest cached token: positions
+ *    p > current_pos are masked (the page's attention_qk_f16 writes -inf
+ *    there).  current_pos >= seq_len masks nothing.  The number of positions
+ *    read is L = min(current_pos, seq_len - 1) + 1.
+ *  - Arithmetic: fp32 dot products and softmax state, output rounded to fp16
+ *    to nearest even.  Same inputs and shapes give bit-identical results.
+ *  - Ownership: the caller owns every buffer.  The library keeps no device
+ *    memory and no state between calls.
+ *  - Asynchrony: each call enqueues kernels on `stream` (a hipStream_t;
+ *    NULL is the null stream) and returns without synchronising.  Inputs
+ *    must stay valid until the work completes.  No call allocates memory or
+ *    synchronises, so calls may be captured in a HIP graph.
+ *  - Errors: arguments are checked on the host before any HIP call; a
+ *    non-OK status means nothing was enqueued (ATTN_ERR_HIP: a launch was
+ *    refused; work enqueued before it on the same call may have run).
+ *    attn_last_error() gives the calling thread's detail text for its last
+ *    non-OK return.
+ *  - Outputs (out, scores_dump, workspace) must not overlap any input.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    ATTN_ERR_DIM = 2,         /* a size is 0, head_dim > ATTN_MAX_HEAD_DIM,
+                                 seq_len > 2^31, batch > 65535, or the cache
+                                 is too large to index                         */
+    ATTN_ERR_ALIGN = 3,       /* fp16 pointer not 2-byte aligned, fp32/uint32
+                                 pointer not 4-byte aligned, workspace not
+                                 16-byte aligned                                */
+    ATTN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required       */
+    ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch              */
+} attn_status_t;
+
+#define ATTN_MAX_HEAD_DIM 256u
+
+/*
+ * Bytes of device workspace that every call below needs for these sizes
+ * (seq_len is the cache length, or the per-sequence capacity of a batch).
+ * Depends only on the arguments.  Returns 0 for invalid sizes.
+ * The workspace holds per-chunk partial softmax states; its content between
+ * calls is meaningless and it needs no initialisation.
+ */
+size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t n_heads, uint32_t head_dim,
+                                   uint32_t seq_len);
+
+/*
+ * One sequence.
+ *   q            [n_heads, head_dim] fp16
+ *   k_cache      [seq_len, n_heads, head_dim] fp16
+ *   v_cache      [seq_len, n_heads, head_dim] fp16
+ *   out          [n_heads, head_dim] fp16, written
+ *   scores_dump  NULL, or [n_heads, seq_len] fp32, written: the scaled score
+ *                (natural-log units) for p <= current_pos and -inf after it,
+ *                as the page's attention_qk_f16 stores them.  For checking;
+ *                it costs a write of the whole buffer.
+ *   workspace    >= attn_decode_workspace_bytes(1, n_heads, head_dim, seq_len)
+ *                bytes of device memory, 16-byte aligned.
+ */
+attn_status_t attn_decode_f16(const uint16_t *q, const uint16_t *k_cache,
+                              const uint16_t *v_cache, uint16_t *out,
+                              uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                              uint32_t current_pos, float *scores_dump,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * A batch of independent sequences sharing one cache capacity, each with
+ * its own current_pos (a ragged batch).
+ *   q            [batch, n_heads, head_dim] fp16
+ *   k_cache      [batch, capacity, n_heads, head_dim] fp16
+ *   v_cache      [batch, capacity, n_heads, head_dim] fp16
+ *   out          [batch, n_heads, head_dim] fp16, written
+ *   current_pos  DEVICE [batch] uint32; values >= capacity mask nothing.  Read
+ *                by the kernels, so it may change between enqueued calls
+ *                without a host synchronisation.
+ *   scores_dump  NULL, or [batch, n_heads, capacity] fp32 (as above)
+ *   workspace    >= attn_decode_workspace_bytes(batch, n_heads, head_dim, capacity)
+ */
+attn_status_t attn_decode_f16_batched(const uint16_t *q, const uint16_t *k_cache,
+                                      const uint16_t *v_cache, uint16_t *out,
+                                      const uint32_t *current_pos, uint32_t batch,
+                                      uint32_t n_heads, uint32_t head_dim, uint32_t capacity,
+                                      float *scores_dump, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
+ * The same computation as the two calls above, split at its one internal
+ * boundary, for callers that need to place work between the two launches
+ * (timing the streaming kernel alone, or moving the partial states between
+ * devices before merging).  attn_decode_f16_split streams the cache and
+ * leaves one partial softmax state per (sequence, head, chunk) in the
+ * workspace; attn_decode_f16_combine merges them into `out`.  Both take the
+ * same sizes and the same current_pos arguments as the call they pair with;
+ * between the two, the workspace belongs to the library.
+ *   current_pos_dev  DEVICE [batch] uint32, or NULL: then every sequence uses
+ *                    current_pos.
+ * attn_decode_f16 is split + combine with current_pos_dev = NULL, batch = 1;
+ * attn_decode_f16_batched is split + combine with the device array.
+ */
+attn_status_t attn_decode_f16_split(const uint16_t *q, const uint16_t *k_cache,
+                                    const uint16_t *v_cache, const uint32_t *current_pos_dev,
+                                    uint32_t current_pos, uint32_t batch, uint32_t n_heads,
+                                    uint32_t head_dim, uint32_t seq_len, float *scores_dump,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+attn_status_t attn_decode_f16_combine(uint16_t *out, const uint32_t *current_pos_dev,
+                                      uint32_t current_pos, uint32_t batch, uint32_t n_heads,
+                                      uint32_t head_dim, uint32_t seq_len,
+                                      const void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/* Static description of a status code. */
+const char *attn_status_string(attn_status_t status);
+
+/* Detail text of the calling thread's last non-OK return ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

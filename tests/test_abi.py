@@ -1,0 +1,115 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every
+function include/attn_decode.h declares, and rejects bad arguments on the
+host before any HIP call (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_kv_seq_amd as ad
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+OK, NULL, DIM, ALIGN, WS, HIP = range(6)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ad.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.attn_status_string(s)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert ad.workspace_bytes(0, 4, 64, 128) == 0
+    assert ad.workspace_bytes(1, 0, 64, 128) == 0
+    assert ad.workspace_bytes(1, 4, 257, 128) == 0
+    assert ad.workspace_bytes(1, 4, 64, 0) == 0
+    for (B, H, D, S) in [(1, 4, 64, 128), (1, 32, 128, 32768), (64, 32, 128, 8192),
+                         (1, 64, 64, 131072), (3, 5, 7, 11)]:
+        n = ad.workspace_bytes(B, H, D, S)
+        assert n > 0 and n % 256 == 0
+        # room for at least one partial (m, l, o[D]) per (sequence, head)
+        assert n >= B * H * (D + 2) * 4
+        assert ad.workspace_bytes(B, H, D, S + 1000) >= n or S + 1000 > 2 ** 32
+    # bounded: a few MiB for the largest single-GPU shapes here
+    assert ad.workspace_bytes(1, 64, 64, 131072) < 16 << 20
+
+
+FAKE = 0x100000  # a nonzero, 256-byte aligned address; never dereferenced
+
+
+def call_single(lib, q=FAKE, k=FAKE, v=FAKE, out=FAKE, H=4, D=64, S=128, cp=100, dump=None,
+                ws=FAKE, ws_bytes=1 << 30):
+    return lib.attn_decode_f16(q, k, v, out, H, D, S, cp, dump, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(out=None), NULL),
+    (dict(H=0), DIM), (dict(D=0), DIM), (dict(S=0), DIM), (dict(D=257), DIM),
+    (dict(q=FAKE + 1), ALIGN), (dict(k=FAKE + 1), ALIGN), (dict(out=FAKE + 1), ALIGN),
+    (dict(dump=FAKE + 2), ALIGN), (dict(ws=FAKE + 8), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS),
+])
+def test_single_rejects_bad_arguments(lib, kw, code):
+    assert call_single(lib, **kw) == code
+    assert lib.attn_last_error().decode()
+
+
+def test_batched_rejects_bad_arguments(lib):
+    f = lib.attn_decode_f16_batched
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 64, 128, None, FAKE, 1 << 30, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 2, 4, 64, 128, None, FAKE, 1 << 30, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 64, 128, None, FAKE, 1 << 30, None) == DIM
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 70000, 4, 64, 128, None, FAKE, 1 << 40, None) == DIM
+    need = ad.workspace_bytes(2, 4, 64, 128)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 128, None, FAKE, need - 1, None) == WS
+    assert b"smaller" in lib.attn_last_error()
+
+
+def test_split_and_combine_reject_bad_arguments(lib):
+    assert lib.attn_decode_f16_split(None, FAKE, FAKE, None, 5, 1, 4, 64, 128, None, FAKE,
+                                     1 << 30, None) == NULL
+    assert lib.attn_decode_f16_split(FAKE, FAKE, FAKE, None, 5, 1, 4, 300, 128, None, FAKE,
+                                     1 << 30, None) == DIM
+    assert lib.attn_decode_f16_combine(None, None, 5, 1, 4, 64, 128, FAKE, 1 << 30, None) == NULL
+    assert lib.attn_decode_f16_combine(FAKE, None, 5, 1, 4, 64, 128, None, 1 << 30, None) == WS
+    assert lib.attn_decode_f16_combine(FAKE + 1, None, 5, 1, 4, 64, 128, FAKE, 1 << 30,
+                                       None) == ALIGN
+
+
+def test_error_text_is_per_call(lib):
+    call_single(lib, D=0)
+    a = lib.attn_last_error().decode()
+    call_single(lib, ws=None)
+    b = lib.attn_last_error().decode()
+    assert "nonzero" in a and "workspace" in b
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(4, 64, dtype=torch.float16)
+    k = torch.zeros(128, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        ad.decode(q, k, k, 100)
+    with pytest.raises(TypeError):
+        ad.decode(q, k.float(), k, 100)

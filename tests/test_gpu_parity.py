@@ -1,0 +1,386 @@
+"""GPU path against the CPU oracle, through the C-ABI library.
+
+Bar (single-query decode attention, fp16 output): for every element
+    |gpu - oracle| <= 2e-3 + 4e-3 * |oracle|
+and for the fp32 score dump
+    |s_gpu - s_oracle| <= 1e-4 * max(|s_oracle|, sum_i |q_i k_i| / sqrt(D)),
+with every position after current_pos exactly -inf (page "Developing Apple
+Metal Kernels in Rust - A Deep Dive Through Attention", section "Testing").
+
+Oracle inputs are generated on the host by the seeded generator; the GPU
+inputs come from the same generator on the device (bit-identical, checked
+in test_device_generator_matches_host).
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_seq_amd as ad
+from decode_attention_kv_seq_amd import workloads as wl
+import oracle
+import oracle_pins
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ATOL, RTOL = 2e-3, 4e-3
+DUMP_RTOL = 1e-4
+
+
+def assert_close(got_f16, ref, what=""):
+    got = got_f16.detach().float().cpu().numpy().astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s: non-finite output" % what
+    err = np.abs(got - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), "%s: err %.3g > bound %.3g at %s (got %r ref %r)" % (
+        what, err[worst], bound[worst], worst, got[worst], ref[worst])
+    return float(err.max())
+
+
+def assert_dump_close(dump, ref_scores, q, k, cp, what=""):
+    """dump [H, S] fp32 (GPU); ref_scores [H, S]; q [H, D], k [S, H, D] host fp16."""
+    d = dump.detach().cpu().numpy().astype(np.float64)
+    H, S = ref_scores.shape
+    L = min(cp, S - 1) + 1
+    assert np.all(d[:, L:] == -np.inf), "%s: masked slots not -inf" % what
+    D = q.shape[-1]
+    qf = q.astype(np.float64).reshape(H, D)
+    kf = k[:L].astype(np.float64)
+    floor = np.einsum("hd,phd->hp", np.abs(qf), np.abs(kf)) / np.sqrt(D)
+    ref = ref_scores[:, :L]
+    err = np.abs(d[:, :L] - ref)
+    bound = DUMP_RTOL * np.maximum(np.abs(ref), floor)
+    assert np.all(err <= bound), "%s: dump err %.3g" % (what, (err - bound).max())
+
+
+def to_dev(a):
+    t = torch.from_numpy(np.ascontiguousarray(a)) if isinstance(a, np.ndarray) else a
+    return t.to(DEV)
+
+
+def run_single(q, k, v, cp, dump=False):
+    """q [H,D], k/v [S,H,D] host fp16 numpy -> GPU output (and dump)."""
+    r = ad.decode(to_dev(q), to_dev(k), to_dev(v), cp, dump=dump)
+    torch.cuda.synchronize()
+    return r
+
+
+def randn16(rng, shape, sigma=1.0, mean=0.0):
+    return (rng.standard_normal(shape) * sigma + mean).astype(np.float16)
+
+
+# ------------------------------------------------------------ workloads
+
+
+def test_device_generator_matches_host():
+    for name in ("h32_d128_s32768_cp20000_garbage", "h64_d64_s131072_spikes"):
+        w = wl.WORKLOADS[name]
+        k, v = wl.make_kv(w, DEV)
+        for h in (0, w.n_heads - 1):
+            qs, ks, vs = wl.head_slice(w, 0, h, n_rows=w.seq_len)
+            assert torch.equal(ks.view(w.seq_len, -1), k[0, :, h].cpu())
+            assert torch.equal(vs.view(w.seq_len, -1), v[0, :, h].cpu())
+            assert torch.equal(qs.view(-1), wl.make_q(w, DEV)[0, h].cpu())
+        del k, v
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["h4_d64_s128_cp100", "h32_d128_s4096_full",
+                                  "h32_d128_s32768_cp20000_garbage"])
+def test_workload_full_parity(name):
+    """Every output element and every score against the oracle."""
+    w = wl.WORKLOADS[name]
+    print("case", name, flush=True)
+    q_h = wl.make_q(w)[0]
+    k_h, v_h = wl.make_kv(w)
+    ref, ref_s, _ = oracle.decode(q_h, k_h[0], v_h[0], w.cur_pos, want_scores=True, threads=8)
+    q, k, v = q_h.to(DEV), k_h[0].to(DEV), v_h[0].to(DEV)
+    out = ad.decode(q, k, v, w.cur_pos)
+    out_d, dump = ad.decode(q, k, v, w.cur_pos, dump=True)
+    torch.cuda.synchronize()
+    assert_close(out, ref, name)
+    assert torch.equal(out, out_d), "dump variant differs from the timed kernel"
+    assert_dump_close(dump, ref_s, q_h.numpy(), k_h[0].numpy(), w.cur_pos, name)
+
+
+def test_workload_ragged_batch_sampled():
+    """64 sequences x 32 heads, capacity 8192: 16 sampled (sequence, head)
+    pairs against the oracle, every sequence's masked dump slots -inf."""
+    w = wl.WORKLOADS["b64_h32_d128_cap8192_ragged"]
+    q = wl.make_q(w, DEV)
+    k, v = wl.make_kv(w, DEV)
+    cp = w.positions().to(torch.int32).to(DEV)
+    out = ad.decode_batched(q, k, v, cp)
+    out_d, dump = ad.decode_batched(q, k, v, cp, dump=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_d)
+    pos = w.positions()
+    for b in range(w.batch):
+        L = w.valid_len(b)
+        assert bool(torch.all(dump[b, :, L:] == -torch.inf))
+    rng = np.random.default_rng(0)
+    picks = [(int(b), int(rng.integers(0, w.n_heads))) for b in rng.choice(w.batch, 16, replace=False)]
+    picks[0] = (int(torch.argmax(pos)), 0)    # longest sequence
+    picks[1] = (int(torch.argmin(pos)), 31)   # shortest sequence
+    for b, h in picks:
+        qs, ks, vs = wl.head_slice(w, b, h)
+        ref, ref_s, _ = oracle.decode(qs[0], ks, vs, int(pos[b]), want_scores=True)
+        assert_close(out[b, h:h + 1], ref, "b=%d h=%d" % (b, h))
+        L = w.valid_len(b)
+        assert_dump_close(dump[b, h:h + 1, :L], ref_s, qs[0].numpy(), ks.numpy(), L - 1,
+                          "b=%d h=%d" % (b, h))
+
+
+def test_workload_long_context_sampled():
+    """seq_len 131072, 64 heads, 1% of K rows x8: 8 sampled heads against the oracle."""
+    w = wl.WORKLOADS["h64_d64_s131072_spikes"]
+    q = wl.make_q(w, DEV)[0]
+    k, v = wl.make_kv(w, DEV)
+    out = ad.decode(q, k[0], v[0], w.cur_pos)
+    out_d, dump = ad.decode(q, k[0], v[0], w.cur_pos, dump=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_d)
+    for h in (0, 9, 17, 30, 33, 46, 58, 63):
+        qs, ks, vs = wl.head_slice(w, 0, h)
+        ref, ref_s, _ = oracle.decode(qs[0], ks, vs, w.cur_pos, want_scores=True)
+        assert_close(out[h:h + 1], ref, "h=%d" % h)
+        assert_dump_close(dump[h:h + 1], ref_s, qs[0].numpy(), ks.numpy(), w.cur_pos, "h=%d" % h)
+
+
+# ------------------------------------------------------------ page cases
+
+
+@pytest.mark.parametrize("case", oracle_pins.page_cases()["cases"], ids=lambda c: c["name"])
+def test_page_cases(case):
+    H, D, S, cp = case["n_heads"], case["head_dim"], case["seq_len"], case["current_pos"]
+    q = oracle_pins._page_fill(H * D).reshape(H, D)
+    k = oracle_pins._page_fill(S * H * D).reshape(S, H, D)
+    v = k[::-1].copy()
+    ref, ref_s, _ = oracle.decode(q, k, v, cp, want_scores=True)
+    out, dump = run_single(q, k, v, cp, dump=True)
+    assert_close(out, ref, case["name"])
+    assert_dump_close(dump, ref_s, q, k, cp, case["name"])
+    assert float((dump[:, : cp + 1].cpu().double() - torch.from_numpy(ref_s[:, : cp + 1])).abs().max()) < 0.5
+
+
+# ------------------------------------------------------------ shapes
+
+
+SHAPES = [  # (S, H, D, cp)
+    (1, 1, 64, 0), (2, 3, 128, 1), (65, 2, 64, 64), (129, 32, 128, 128), (1000, 8, 128, 999),
+    (4097, 32, 128, 4096), (5000, 4, 64, 3333), (300, 7, 48, 299), (77, 5, 1, 76), (90, 3, 7, 50),
+    (200, 2, 8, 199), (150, 4, 16, 149), (123, 6, 40, 100), (64, 2, 72, 63), (500, 3, 96, 499),
+    (100, 2, 100, 99), (70, 2, 130, 69), (60, 3, 200, 59), (50, 2, 250, 49), (40, 2, 255, 39),
+    (333, 9, 256, 332), (2049, 1, 128, 2048), (20000, 2, 64, 19999), (70000, 1, 32, 69999),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "S%d_H%d_D%d_cp%d" % s)
+def test_shapes_parity(shape):
+    S, H, D, cp = shape
+    rng = np.random.default_rng(S * 131 + H * 7 + D)
+    q = randn16(rng, (H, D), 2.0)
+    k = randn16(rng, (S, H, D))
+    v = randn16(rng, (S, H, D))
+    ref, ref_s, _ = oracle.decode(q, k, v, cp, want_scores=True, threads=4)
+    out, dump = run_single(q, k, v, cp, dump=True)
+    assert_close(out, ref, str(shape))
+    assert_dump_close(dump, ref_s, q, k, cp, str(shape))
+
+
+@pytest.mark.parametrize("offset", [1, 2, 4], ids=lambda o: "elem_offset%d" % o)
+@pytest.mark.parametrize("D", [64, 128, 48])
+def test_unaligned_tensors(offset, D):
+    """Tensors starting 2, 4 or 8 bytes past an aligned address take the
+    narrower-load paths; results still match the oracle."""
+    S, H, cp = 700, 3, 650
+    rng = np.random.default_rng(offset * 1000 + D)
+    q = randn16(rng, (H, D))
+    k = randn16(rng, (S, H, D))
+    v = randn16(rng, (S, H, D))
+    ref, _, _ = oracle.decode(q, k, v, cp)
+
+    def shifted(a):
+        buf = torch.zeros(a.size + 16, dtype=torch.float16, device=DEV)
+        t = buf[offset:offset + a.size].view(a.shape)
+        t.copy_(torch.from_numpy(a))
+        return t
+
+    qt, kt, vt = shifted(q), shifted(k), shifted(v)
+    assert kt.data_ptr() % 16 != 0
+    out = ad.decode(qt, kt, vt, cp)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "offset %d" % offset)
+
+
+# ------------------------------------------------------------ special cases
+
+
+@pytest.mark.parametrize("D", [64, 128, 48, 7])
+def test_first_position_only_is_exact(D):
+    rng = np.random.default_rng(D)
+    S, H = 50, 4
+    q = randn16(rng, (H, D), 3.0)
+    k = randn16(rng, (S, H, D), 3.0)
+    v = randn16(rng, (S, H, D))
+    out = run_single(q, k, v, 0)
+    assert np.array_equal(out.cpu().numpy(), v[0])
+
+
+@pytest.mark.parametrize("S", [100, 5000, 40000])
+def test_values_all_one_give_one(S):
+    rng = np.random.default_rng(S)
+    H, D = 8, 128
+    q = randn16(rng, (H, D), 2.0)
+    k = randn16(rng, (S, H, D))
+    v = np.ones((S, H, D), np.float16)
+    out = run_single(q, k, v, S - 1)
+    assert bool(torch.all(out == 1.0))
+
+
+def test_values_near_one_relative():
+    """V ~ N(1, 1): outputs near 1, where the 4e-3 relative term dominates."""
+    rng = np.random.default_rng(5)
+    S, H, D = 30000, 16, 64
+    q = randn16(rng, (H, D))
+    k = randn16(rng, (S, H, D))
+    v = randn16(rng, (S, H, D), 1.0, 1.0)
+    ref, _, _ = oracle.decode(q, k, v, S - 1, threads=8)
+    out = run_single(q, k, v, S - 1)
+    got = out.float().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= 1e-3 * np.abs(ref) + 1e-4)
+
+
+def test_identical_keys_give_mean_of_values():
+    rng = np.random.default_rng(6)
+    S, H, D, cp = 3000, 4, 128, 2500
+    q = randn16(rng, (H, D), 2.0)
+    k = np.broadcast_to(randn16(rng, (1, H, D)), (S, H, D)).copy()
+    v = randn16(rng, (S, H, D))
+    out = run_single(q, k, v, cp)
+    assert_close(out, v[: cp + 1].astype(np.float64).mean(axis=0), "mean of V")
+
+
+def test_dominant_score_returns_its_row():
+    rng = np.random.default_rng(7)
+    S, H, D = 5000, 4, 64
+    q = (3.0 * rng.choice([-1.0, 1.0], (H, D))).astype(np.float16)
+    k = np.zeros((S, H, D), np.float16)
+    stars = [0, 1234, 4000, 4999]
+    for h, p in enumerate(stars):
+        k[p, h] = q[h]
+    v = randn16(rng, (S, H, D))
+    out = run_single(q, k, v, S - 1).cpu().numpy()
+    for h, p in enumerate(stars):
+        assert np.array_equal(out[h], v[p, h]), h
+
+
+@pytest.mark.parametrize("fill", [65504.0, np.inf, -np.inf, np.nan, "noise"])
+def test_masked_garbage_leaves_output_bitwise_unchanged(fill):
+    rng = np.random.default_rng(8)
+    S, H, D, cp = 9000, 8, 128, 5000
+    q = randn16(rng, (H, D))
+    k = randn16(rng, (S, H, D))
+    v = randn16(rng, (S, H, D))
+    clean = run_single(q, k, v, cp)
+    k2, v2 = k.copy(), v.copy()
+    if fill == "noise":
+        k2[cp + 1:] = randn16(rng, (S - cp - 1, H, D), 10.0)
+        v2[cp + 1:] = randn16(rng, (S - cp - 1, H, D), 10.0)
+    else:
+        k2[cp + 1:] = fill
+        v2[cp + 1:] = -np.float16(fill)
+    out, dump = run_single(q, k2, v2, cp, dump=True)
+    assert torch.equal(out, clean)
+    assert bool(torch.all(torch.isfinite(dump[:, : cp + 1])))
+    assert bool(torch.all(dump[:, cp + 1:] == -torch.inf))
+
+
+def test_current_pos_beyond_cache_masks_nothing():
+    rng = np.random.default_rng(9)
+    S, H, D = 1500, 4, 128
+    q, k, v = randn16(rng, (H, D)), randn16(rng, (S, H, D)), randn16(rng, (S, H, D))
+    a = run_single(q, k, v, S - 1)
+    for cp in (S, S + 100, 2 ** 32 - 1):
+        assert torch.equal(run_single(q, k, v, cp), a)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    rng = np.random.default_rng(10)
+    S, H, D = 50000, 32, 128
+    q, k, v = to_dev(randn16(rng, (H, D))), to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
+    outs = [ad.decode(q, k, v, S - 1) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+# ------------------------------------------------------------ batched, phases, streams
+
+
+def test_batched_matches_single_calls():
+    rng = np.random.default_rng(11)
+    B, S, H, D = 6, 3000, 8, 128
+    q = randn16(rng, (B, H, D))
+    k = randn16(rng, (B, S, H, D))
+    v = randn16(rng, (B, S, H, D))
+    pos = np.array([0, 63, 64, 1999, 2999, 10 ** 6], dtype=np.int64)
+    cp = torch.from_numpy(np.minimum(pos, 2 ** 31 - 1).astype(np.int32)).to(DEV)
+    out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref, _, _ = oracle.decode(q[b], k[b], v[b], int(pos[b]))
+        assert_close(out[b], ref, "b=%d" % b)
+        single = run_single(q[b], k[b], v[b], int(pos[b]))
+        assert_close(out[b], single.float().cpu().numpy(), "batched vs single b=%d" % b)
+
+
+def test_many_short_sequences():
+    rng = np.random.default_rng(12)
+    B, S, H, D = 300, 40, 2, 64
+    q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, 45, B)
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_batched(q, k, v, pos)
+    assert_close(out, ref, "300 sequences")
+
+
+def test_split_then_combine_equals_fused_call():
+    rng = np.random.default_rng(13)
+    S, H, D, cp = 40000, 16, 128, 33333
+    q, k, v = to_dev(randn16(rng, (H, D))), to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
+    fused = ad.decode(q, k, v, cp)
+    ws = ad.alloc_workspace(1, H, D, S, DEV)
+    out = torch.empty_like(fused)
+    ad.split(q, k, v, cp, ws)
+    ad.combine(out, cp, 1, H, D, S, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, fused)
+
+
+def test_side_stream():
+    rng = np.random.default_rng(14)
+    S, H, D = 8000, 8, 64
+    q, k, v = to_dev(randn16(rng, (H, D))), to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
+    ref = ad.decode(q, k, v, S - 1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = ad.decode(q, k, v, S - 1)
+    s.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_workspace_errors_on_gpu():
+    rng = np.random.default_rng(15)
+    S, H, D = 1000, 4, 64
+    q, k, v = to_dev(randn16(rng, (H, D))), to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
+    small = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ad.AttnError) as e:
+        ad.decode(q, k, v, S - 1, workspace=small)
+    assert e.value.status == 4
