@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Decode-attention bench: K+V bytes read per second on one MI355X.
+
+One step is one full decode-attention call (split kernel + combine kernel)
+over a synthetic fp16 cache resident in HBM.  The default workload is the
+single-sequence cache of 131072 positions x 64 heads x head_dim 64 (2 GiB of
+K+V, 1% of K rows scaled x8), the largest at seq_len >= 32768.
+
+Prints ONE JSON line on stdout:
+  value          algorithmic K+V GB/s of the whole step (rows p <= current_pos)
+  ms_per_step    HIP-event time per step over the timed loop
+  roofline       the split kernel alone: the same bytes over its average
+                 duration (HIP events around each split launch, on the stream
+                 it runs on), against the 8 TB/s HBM peak; `traffic` holds the
+                 rocprofv3 FETCH_SIZE/WRITE_SIZE bytes per launch when a
+                 counter summary for the current kernel source is committed
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+Everything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention HBM GB/s (K+V bytes/s) and % of MI355X HBM peak; µs/step"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_seq_amd", "csrc", "attn_decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--workload", default=None, help="workload name (default: the 131072-position cache)")
+    p.add_argument("--rotate", type=int, default=0,
+                   help="K/V copies to cycle through (0: enough for >= 2 GiB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
+    return p.parse_args()
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the oracle (as it is) on whole (sequence, head) units of the workload."""
+    import numpy as np
+    from decode_attention_kv_seq_amd import workloads as wl
+    import oracle
+
+    orc = oracle.load()
+    cores = min(os.cpu_count() or 1, 16)
+    pos = w.positions()
+    rng = np.random.default_rng(0)
+    units = [(int(b), int(h)) for b in range(w.batch) for h in range(w.n_heads)]
+    order = rng.permutation(len(units))
+    units = [units[i] for i in order]
+
+    def one(b, h):
+        q, k, v = wl.head_slice(w, b, h)
+        return q[0], k, v, int(pos[b]), k.shape[0] * w.head_dim * 2 * 2
+
+    # estimate the rate on one unit, then size a sample of ~`seconds`
+    q, k, v, cp, nbytes = one(*units[0])
+    t0 = time.perf_counter()
+    orc.decode(q, k, v, cp)
+    t1 = time.perf_counter() - t0
+    n_units = max(cores, int(seconds * cores / max(t1, 1e-6)))
+    n_units = min(n_units, len(units))
+    sample = [one(*u) for u in units[:n_units]]
+    total_bytes = sum(s[4] for s in sample)
+
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(lambda s: orc.decode(s[0], s[1], s[2], s[3]), sample))
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(total_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d (sequence, head) units, %.1f MB of K+V, %.2f s on %d threads "
+                  "(fp64 scalar C oracle)" % (n_units, len(units), total_bytes / 1e6, dt, cores),
+    }
+
+
+def load_traffic(workload: str):
+    """HBM bytes per split launch from the committed rocprofv3 counter summary
+    of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known
+    size), or None when there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, "split_kernel_%s_counters.md" % workload)
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("machine-readable:"):
+            for tok in line.split(":", 1)[1].split():
+                k, _, v = tok.partition("=")
+                fields[k] = v
+    if fields.get("kernel_sha") != kernel_sha() or "bytes_per_launch" not in fields:
+        return None
+    return int(fields["bytes_per_launch"])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_kv_seq_amd as ad
+    from decode_attention_kv_seq_amd import workloads as wl
+
+    name = args.workload or wl.BENCH_WORKLOAD
+    w = wl.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = ad.load_library()
+    props = torch.cuda.get_device_properties(dev)
+    log("device: %s, %d CUs, %.0f GiB" % (props.name, props.multi_processor_count,
+                                          props.total_memory / 2 ** 30))
+
+    t0 = time.perf_counter()
+    q = wl.make_q(w, dev)
+    k0, v0 = wl.make_kv(w, dev)
+    kv_alloc = 2 * k0.numel() * 2
+    copies = args.rotate or max(1, math.ceil((2 << 30) / kv_alloc))
+    ks, vs = [k0], [v0]
+    for _ in range(copies - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    torch.cuda.synchronize()
+    log("inputs: %s, %d cop%s of %.1f MiB K+V, generated in %.1f s"
+        % (name, copies, "y" if copies == 1 else "ies", kv_alloc / 2 ** 20, time.perf_counter() - t0))
+
+    B, S, H, D = w.kv_shape
+    out = torch.empty(w.q_shape, dtype=torch.float16, device=dev)
+    ws = ad.alloc_workspace(B, H, D, S, dev)
+    ws_bytes = ws.numel()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    nbytes = w.kv_bytes_read()
+    vp = ctypes.c_void_p
+    if w.batched:
+        cp_dev = w.positions().to(torch.int32).to(dev)
+        cp_host = 0
+    else:
+        cp_dev = None
+        cp_host = w.cur_pos
+
+    # pre-marshalled arguments: the timed loop is one ctypes call per step
+    full_args, split_args = [], []
+    for r in range(copies):
+        if w.batched:
+            full_args.append((vp(q.data_ptr()), vp(ks[r].data_ptr()), vp(vs[r].data_ptr()),
+                              vp(out.data_ptr()), vp(cp_dev.data_ptr()), B, H, D, S, None,
+                              vp(ws.data_ptr()), ws_bytes, sh))
+        else:
+            full_args.append((vp(q.data_ptr()), vp(ks[r].data_ptr()), vp(vs[r].data_ptr()),
+                              vp(out.data_ptr()), H, D, S, cp_host, None,
+                              vp(ws.data_ptr()), ws_bytes, sh))
+        split_args.append((vp(q.data_ptr()), vp(ks[r].data_ptr()), vp(vs[r].data_ptr()),
+                           vp(cp_dev.data_ptr()) if cp_dev is not None else None, cp_host,
+                           B, H, D, S, None, vp(ws.data_ptr()), ws_bytes, sh))
+    combine_args = (vp(out.data_ptr()), vp(cp_dev.data_ptr()) if cp_dev is not None else None,
+                    cp_host, B, H, D, S, vp(ws.data_ptr()), ws_bytes, sh)
+    full = lib.attn_decode_f16_batched if w.batched else lib.attn_decode_f16
+
+    def check(rc):
+        if rc != 0:
+            raise ad.AttnError(rc, lib.attn_last_error().decode())
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---- whole steps
+    for i in range(args.warmup):
+        check(full(*full_args[i % copies]))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        check(full(*full_args[i % copies]))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # ---- the split kernel alone, inside otherwise unchanged steps
+    n_split = max(20, min(args.steps, 500))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_split)]
+    for i in range(n_split):
+        evs[i][0].record(stream)
+        check(lib.attn_decode_f16_split(*split_args[i % copies]))
+        evs[i][1].record(stream)
+        check(lib.attn_decode_f16_combine(*combine_args))
+    torch.cuda.synchronize()
+    split_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    split_avg = sum(split_ms) / len(split_ms)
+
+    value = nbytes / (ms * 1e-3) / 1e9
+    achieved = nbytes / (split_avg * 1e-3) / 1e9
+    log("step %.2f us -> %.1f GB/s (%.1f%% of 8 TB/s); split kernel %.2f us (median %.2f) -> %.1f GB/s"
+        % (ms * 1e3, value, 100 * value / HBM_PEAK_GBS, split_avg * 1e3,
+           split_ms[len(split_ms) // 2] * 1e3, achieved))
+
+    traffic = load_traffic(name)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log("cpu baseline: %s" % json.dumps(cpu))
+
+    config = {
+        "workload": name,
+        "batch": B, "n_heads": H, "head_dim": D, "seq_len": S,
+        "current_pos": w.cur_pos if not w.batched else "per-sequence U[0,%d]" % (S - 1),
+        "kv_bytes_per_step": nbytes,
+        "kv_copies_rotated": copies,
+        "us_per_step": round(ms * 1e3, 3),
+        "split_kernel_us": round(split_avg * 1e3, 3),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+    }
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": config,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -41,8 +41,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kUnroll = 4;           // positions per lane group per loop trip
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 1024;
 
 // ------------------------------------------------------------------ packs
 // A pack is VEC consecutive fp16 values of one row held by one lane.
@@ -160,8 +159,9 @@ struct SplitArgs {
 };
 
 // VEC: fp16 values per lane load; GL: lanes per row (power of two);
-// NV: packs per lane per row; FULL: D == VEC*GL*NV (no element guards).
-template <int VEC, int GL, int NV, bool FULL, bool DUMP>
+// NV: packs per lane per row; FULL: D == VEC*GL*NV (no element guards);
+// U: positions per row group per block; PF: double-buffered blocks.
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     constexpr int RG = 64 / GL;              // row groups per wave
     constexpr int NG = kWaves * RG;          // row groups per workgroup
@@ -217,34 +217,37 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[j][e] = 0.f;
 
-    const uint32_t step = pps * kUnroll;
-    for (uint32_t base = c0; base < c_end; base += step) {
-        Pack<VEC> kr[kUnroll][NV], vr[kUnroll][NV];
-        bool ok[kUnroll];
+    // One block = U positions per row group.  Slots past the chunk end load
+    // the chunk's first row (always valid) and get weight 0.
+    struct Block {
+        Pack<VEC> k[U][NV], v[U][NV];
+    };
+    auto load_block = [&](Block &blk, uint32_t base) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const uint32_t p = base + u * pps + pg;
-            ok[u] = p < c_end;
-            const size_t row = (size_t)(ok[u] ? p : c0) * HD;   // clamp: never past L
+            const size_t row = (size_t)(p < c_end ? p : c0) * HD;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                kr[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
-                vr[u][j] = eok[j] ? load_pack<VEC>(vbase + row + eoff[j]) : zero_pack<VEC>();
+                blk.k[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
+                blk.v[u][j] = eok[j] ? load_pack<VEC>(vbase + row + eoff[j]) : zero_pack<VEC>();
             }
         }
-        float t[kUnroll];
+    };
+    auto consume = [&](const Block &blk, uint32_t base) {
+        float t[U];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
+            const uint32_t p = base + u * pps + pg;
             float dot = 0.f;
 #pragma unroll
-            for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], kr[u][j], dot);
+            for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], blk.k[u][j], dot);
             dot = group_sum<GL>(dot);
-            t[u] = ok[u] ? dot * a.scale_log2 : -INFINITY;
+            t[u] = p < c_end ? dot * a.scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, t[u]);
             if constexpr (DUMP) {
-                if (ok[u] && gl == 0)
-                    a.dump[((size_t)b * a.H + h) * a.S + base + u * pps + pg] = dot * a.scale;
+                if (p < c_end && gl == 0) a.dump[((size_t)b * a.H + h) * a.S + p] = dot * a.scale;
             }
         }
         const float m_new = fmaxf(m, tmax);
@@ -256,16 +259,45 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[j][e] *= corr;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const float pw = __builtin_amdgcn_exp2f(t[u] - m_use);   // 0 for masked slots
             l += pw;
 #pragma unroll
             for (int j = 0; j < NV; ++j)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    acc[j][e] = fmaf(pw, pack_elem<VEC>(vr[u][j], e), acc[j][e]);
+                    acc[j][e] = fmaf(pw, pack_elem<VEC>(blk.v[u][j], e), acc[j][e]);
         }
         m = m_new;
+    };
+
+    const uint32_t step = pps * U;
+    if constexpr (PF) {
+        // two register blocks: the next block's loads are in flight while the
+        // current one is reduced
+        Block A, B;
+        uint32_t base = c0;
+        load_block(A, base);
+        while (true) {
+            uint32_t nb = base + step;
+            const bool more = nb < c_end;
+            if (more) load_block(B, nb);
+            consume(A, base);
+            if (!more) break;
+            base = nb;
+            nb = base + step;
+            const bool more2 = nb < c_end;
+            if (more2) load_block(A, nb);
+            consume(B, base);
+            if (!more2) break;
+            base = nb;
+        }
+    } else {
+        for (uint32_t base = c0; base < c_end; base += step) {
+            Block A;
+            load_block(A, base);
+            consume(A, base);
+        }
     }
 
     // ---- merge the row groups that share a head
@@ -319,9 +351,16 @@ struct CombineArgs {
     uint16_t *out;
 };
 
+// One workgroup per (sequence, head).  Pass 1 finds M = max_c m_c; then, a
+// tile of chunks at a time, the weights 2^(m_c - M) go to LDS and thread
+// (cg, d) accumulates o_c[d] and l_c over chunks cg, cg+G, ... with the
+// loads of a tile independent of each other.  o and l go through the same
+// operations in the same order, so all-equal V rows give exactly 1.
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineArgs a) {
-    __shared__ float sm_red[kCombineThreads / 64];
-    __shared__ float sm_acc[kCombineThreads];
+    constexpr int NW = kCombineThreads / 64;
+    __shared__ float sm_w[kCombineThreads];
+    __shared__ float sm_red[NW];
+    __shared__ float sm_o[kCombineThreads];
     __shared__ float sm_l[kCombineThreads];
 
     const uint32_t h = blockIdx.x;
@@ -334,7 +373,6 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineAr
     const float *po = a.part_o + bh * a.nc_stride * a.D;
     const int tid = threadIdx.x;
 
-    // M = max over chunks
     float mx = -INFINITY;
     for (uint32_t c = tid; c < nc; c += kCombineThreads) mx = fmaxf(mx, ml[2 * c]);
 #pragma unroll
@@ -343,27 +381,48 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineAr
     __syncthreads();
     float M = sm_red[0];
 #pragma unroll
-    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, sm_red[w]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_red[w]);
 
-    // thread (cg, d): chunks cg, cg+G, ... of element d
-    const uint32_t G = kCombineThreads / a.D;   // >= 1 since D <= 256
+    const uint32_t G = kCombineThreads / a.D;   // chunk groups (D <= 256)
     const uint32_t cg = tid / a.D;
     const uint32_t d = tid % a.D;
+    const bool active = cg < G;
     float o = 0.f, lsum = 0.f;
-    if (cg < G) {
-        for (uint32_t c = cg; c < nc; c += G) {
-            const float w = __builtin_amdgcn_exp2f(ml[2 * c] - M);
-            o = fmaf(po[(size_t)c * a.D + d], w, o);
-            lsum = fmaf(ml[2 * c + 1], w, lsum);
+    for (uint32_t t0 = 0; t0 < nc; t0 += kCombineThreads) {
+        const uint32_t tn = min(nc - t0, (uint32_t)kCombineThreads);
+        __syncthreads();   // previous tile's weights are consumed
+        if ((uint32_t)tid < tn) sm_w[tid] = __builtin_amdgcn_exp2f(ml[2 * (t0 + tid)] - M);
+        __syncthreads();
+        if (active) {
+            uint32_t c = cg;
+            for (; c + 3 * G < tn; c += 4 * G) {
+                float ov[4], lv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ov[u] = po[(size_t)(t0 + c + u * G) * a.D + d];
+                    lv[u] = ml[2 * (t0 + c + u * G) + 1];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float w = sm_w[c + u * G];
+                    o = fmaf(ov[u], w, o);
+                    lsum = fmaf(lv[u], w, lsum);
+                }
+            }
+            for (; c < tn; c += G) {
+                const float w = sm_w[c];
+                o = fmaf(po[(size_t)(t0 + c) * a.D + d], w, o);
+                lsum = fmaf(ml[2 * (t0 + c) + 1], w, lsum);
+            }
         }
     }
-    sm_acc[tid] = o;
+    sm_o[tid] = o;
     sm_l[tid] = lsum;
     __syncthreads();
     if (tid < (int)a.D) {
         float os = 0.f, ls = 0.f;
         for (uint32_t r = 0; r < G; ++r) {
-            os += sm_acc[r * a.D + tid];
+            os += sm_o[r * a.D + tid];
             ls += sm_l[r * a.D + tid];
         }
         a.out[bh * a.D + tid] = f2h_rne(os / ls);
@@ -400,29 +459,38 @@ attn_status_t ok() {
     return ATTN_OK;
 }
 
-// Planner constants, sized for 256 compute units.  The ATTN_DECODE_TUNE
-// environment variable ("items=N,cmax=N,hpb=N") overrides them for tuning
-// sweeps; it is read once per process.
-struct Tuning {
-    uint32_t items = 2048;   // target (head, chunk) work items per call
-    uint32_t cmax = 8192;    // largest chunk, positions
-    uint32_t hpb = 1;        // requested heads per workgroup
+// Planner knobs, sized for 256 compute units and measured on MI355X: the
+// best head blocking makes each position's read 512 contiguous bytes or
+// more, and about 1024 workgroups (4 per CU) keep enough loads in flight.
+// The ATTN_DECODE_TUNE environment variable
+// ("wgs=N,cmax=N,hpb=N,unroll=N,pf=N") overrides them for tuning sweeps; it
+// is read once per process.
+struct Knobs {
+    uint32_t wgs;      // target workgroups per call
+    uint32_t cmax;     // largest chunk, positions
+    uint32_t hpb;      // requested heads per workgroup
+    uint32_t unroll;   // positions per row group per block (2, 4, 8)
+    uint32_t pf;       // double-buffered blocks
 };
 constexpr uint32_t kChunkGranule = 64;
+constexpr uint32_t kMaxHeadsPerWG = kWaves * 64 / 8;   // row groups at 8 lanes per row
 
-const Tuning &tuning() {
-    static const Tuning t = [] {
-        Tuning r;
+const Knobs &env_knobs() {
+    static const Knobs t = [] {
+        Knobs r{0, 0, 0, 0, 2};
         const char *env = getenv("ATTN_DECODE_TUNE");
         if (env) {
             char buf[256];
             snprintf(buf, sizeof buf, "%s", env);
             for (char *tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
                 unsigned v = 0;
-                if (sscanf(tok, "items=%u", &v) == 1 && v > 0) r.items = v;
+                if (sscanf(tok, "wgs=%u", &v) == 1 && v > 0) r.wgs = v;
                 else if (sscanf(tok, "cmax=%u", &v) == 1 && v >= kChunkGranule)
                     r.cmax = v / kChunkGranule * kChunkGranule;
                 else if (sscanf(tok, "hpb=%u", &v) == 1 && v > 0) r.hpb = v;
+                else if (sscanf(tok, "unroll=%u", &v) == 1 && (v == 2 || v == 4 || v == 8))
+                    r.unroll = v;
+                else if (sscanf(tok, "pf=%u", &v) == 1) r.pf = v ? 1 : 0;
             }
         }
         return r;
@@ -430,8 +498,69 @@ const Tuning &tuning() {
     return t;
 }
 
+// Defaults by row size (head_dim) and by whether current_pos is per sequence.
+Knobs knobs(uint32_t D, bool batched) {
+    Knobs k;
+    if (batched) k = Knobs{1792, 8192, 8, 4, 1};          // ragged batches
+    else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0};    // 128-byte rows
+    else k = Knobs{512, 8192, 2, 2, 1};                  // 256-byte rows and wider
+    const Knobs &e = env_knobs();
+    if (e.wgs) k.wgs = e.wgs;
+    if (e.cmax) k.cmax = e.cmax;
+    if (e.hpb) k.hpb = e.hpb;
+    if (e.unroll) k.unroll = e.unroll;
+    if (e.pf != 2) k.pf = e.pf;
+    return k;
+}
+
 uint64_t cdiv(uint64_t a, uint64_t b) {
     return (a + b - 1) / b;
+}
+
+uint32_t pow2ceil(uint32_t x) {
+    uint32_t r = 1;
+    while (r < x) r <<= 1;
+    return r;
+}
+
+bool aligned(const void *p, uintptr_t a) {
+    return ((uintptr_t)p & (a - 1)) == 0;
+}
+
+// Lane layout of one cache row: VEC fp16 values per load, GL lanes per row
+// (power of two, >= 8), NV loads per lane.
+struct Layout {
+    int vec, gl, nv;
+    bool full;
+};
+
+Layout choose_layout(uint32_t D, const void *q, const void *k, const void *v) {
+    int vec = 1;
+    for (int c : {8, 4, 2}) {
+        const uintptr_t bytes = 2u * c;
+        if (D % c == 0 && aligned(q, bytes) && aligned(k, bytes) && aligned(v, bytes)) {
+            vec = c;
+            break;
+        }
+    }
+    const uint32_t nvec = D / vec;
+    uint32_t gl = pow2ceil(nvec);
+    if (gl > 64) gl = 64;
+    if (gl < 8) gl = 8;
+    const uint32_t nv = (uint32_t)cdiv(nvec, gl);
+    // only the 16-byte layouts have guard-free instantiations
+    Layout L{vec, (int)gl, (int)nv, vec == 8 && (uint32_t)(vec * gl * nv) == D};
+    return L;
+}
+
+// Heads per workgroup: the largest power of two <= the request that divides
+// H and fits the layout's row groups.
+uint32_t heads_per_wg(uint32_t H, const Layout &ly, uint32_t want) {
+    const uint32_t ng = kWaves * (64 / ly.gl);
+    uint32_t hpb = 1;
+    for (uint32_t c = 1; c <= want && c <= ng && c <= H; c <<= 1)
+        if (H % c == 0) hpb = c;
+    return hpb;
 }
 
 struct Plan {
@@ -440,32 +569,43 @@ struct Plan {
     uint32_t nc_stride;   // chunk stride in the workspace (an upper bound)
 };
 
-// Chunk count bound used for the workspace layout; depends only on sizes.
-uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t S) {
-    const Tuning &t = tuning();
-    const uint64_t nt = cdiv(t.items, (uint64_t)batch * H);
-    const uint64_t hi = nt > cdiv(S, t.cmax) ? nt : cdiv(S, t.cmax);
+// Chunk count bound of one knob set for the workspace layout.
+uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S) {
+    const uint64_t nhb_min = cdiv(H, kMaxHeadsPerWG);
+    const uint64_t nt = cdiv(k.wgs, (uint64_t)batch * nhb_min);
+    const uint64_t hi = nt > cdiv(S, k.cmax) ? nt : cdiv(S, k.cmax);
     const uint64_t lo = cdiv(S, kChunkGranule);
     return (uint32_t)(hi < lo ? hi : lo);
 }
 
-// Chunk size for `span` positions: about `items` work items over the batch,
-// rounded to the granule, clamped to [granule, cmax].
-Plan make_plan(uint32_t batch, uint32_t H, uint32_t S, uint32_t span) {
-    const Tuning &t = tuning();
-    const uint64_t nt = cdiv(t.items, (uint64_t)batch * H);
+// Workspace chunk stride: covers single-sequence and batched plans, so it
+// depends on sizes only.
+uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
+    const uint32_t a = chunk_bound_for(knobs(D, false), batch, H, S);
+    const uint32_t b = chunk_bound_for(knobs(D, true), batch, H, S);
+    return a > b ? a : b;
+}
+
+// Chunk size for `span` positions.  The head blocking assumed here is the
+// one of the widest-load layout for this head_dim, so the plan depends on
+// sizes only (the combine launch recomputes it without the cache pointers).
+Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span, bool batched) {
+    const Knobs k = knobs(D, batched);
+    const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
+    const uint64_t n_hb = H / heads_per_wg(H, best, k.hpb);
+    const uint64_t nt = cdiv(k.wgs, (uint64_t)batch * n_hb);
     uint64_t c = cdiv(cdiv(span, nt), kChunkGranule) * kChunkGranule;
-    if (c > t.cmax) c = t.cmax;
+    if (c > k.cmax) c = k.cmax;
     if (c < kChunkGranule) c = kChunkGranule;
     Plan p;
     p.chunk = (uint32_t)c;
     p.n_chunks = (uint32_t)cdiv(span, c);
-    p.nc_stride = chunk_bound(batch, H, S);
+    p.nc_stride = chunk_bound(batch, H, D, S);
     return p;
 }
 
 size_t workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, size_t *ml_offset) {
-    const size_t slots = (size_t)batch * H * chunk_bound(batch, H, S);
+    const size_t slots = (size_t)batch * H * chunk_bound(batch, H, D, S);
     const size_t o_bytes = (slots * D * sizeof(float) + 255) / 256 * 256;
     const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
     if (ml_offset) *ml_offset = o_bytes;
@@ -491,54 +631,29 @@ attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     return ok();
 }
 
-bool aligned(const void *p, uintptr_t a) {
-    return ((uintptr_t)p & (a - 1)) == 0;
-}
-
 // -------------------------------------------------------- kernel selection
 
 using SplitFn = void (*)(SplitArgs);
 
-struct Layout {
-    int vec, gl, nv;
-    bool full;
-};
-
-uint32_t pow2ceil(uint32_t x) {
-    uint32_t r = 1;
-    while (r < x) r <<= 1;
-    return r;
-}
-
-Layout choose_layout(uint32_t D, const void *q, const void *k, const void *v) {
-    int vec = 1;
-    for (int c : {8, 4, 2}) {
-        const uintptr_t bytes = 2u * c;
-        if (D % c == 0 && aligned(q, bytes) && aligned(k, bytes) && aligned(v, bytes)) {
-            vec = c;
-            break;
-        }
-    }
-    const uint32_t nvec = D / vec;
-    uint32_t gl = pow2ceil(nvec);
-    if (gl > 64) gl = 64;
-    if (gl < 8) gl = 8;
-    const uint32_t nv = (uint32_t)cdiv(nvec, gl);
-    // only the 16-byte layouts have guard-free instantiations
-    Layout L{vec, (int)gl, (int)nv, vec == 8 && (uint32_t)(vec * gl * nv) == D};
-    return L;
+template <int V, int G, int N, bool F, bool DUMP>
+SplitFn pick_unroll(const Knobs &t) {
+    if (t.unroll == 2) return t.pf ? attn_split_kernel<V, G, N, F, 2, true, DUMP>
+                                   : attn_split_kernel<V, G, N, F, 2, false, DUMP>;
+    if (t.unroll == 8) return t.pf ? attn_split_kernel<V, G, N, F, 8, true, DUMP>
+                                   : attn_split_kernel<V, G, N, F, 8, false, DUMP>;
+    return t.pf ? attn_split_kernel<V, G, N, F, 4, true, DUMP>
+                : attn_split_kernel<V, G, N, F, 4, false, DUMP>;
 }
 
 template <bool DUMP>
-SplitFn pick_split(const Layout &ly) {
+SplitFn pick_split(const Layout &ly, const Knobs &k) {
+    // fast paths: head_dim 64 and 128 with 16-byte rows
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP>(k);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP>(k);
 #define ATTN_CASE(V, G, N, F)                                                          \
     if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
-        return attn_split_kernel<V, G, N, F, DUMP>;
-    // fast paths: head_dim 64, 128, 256 with 16-byte rows
-    ATTN_CASE(8, 8, 1, true)
-    ATTN_CASE(8, 16, 1, true)
+        return attn_split_kernel<V, G, N, F, 4, true, DUMP>;
     ATTN_CASE(8, 32, 1, true)
-    // everything else
     ATTN_CASE(8, 8, 1, false)
     ATTN_CASE(8, 16, 1, false)
     ATTN_CASE(8, 32, 1, false)
@@ -560,15 +675,6 @@ SplitFn pick_split(const Layout &ly) {
     ATTN_CASE(1, 64, 4, false)
 #undef ATTN_CASE
     return nullptr;
-}
-
-uint32_t choose_hpb(uint32_t H, const Layout &ly) {
-    const uint32_t ng = kWaves * (64 / ly.gl);
-    uint32_t want = tuning().hpb;
-    uint32_t hpb = 1;
-    for (uint32_t c = 1; c <= want && c <= ng && c <= H; c <<= 1)
-        if (H % c == 0) hpb = c;
-    return hpb;
 }
 
 attn_status_t hip_check(const char *what) {
@@ -610,12 +716,13 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
                            uint32_t D, uint32_t S, float *dump, void *ws, uint16_t *out,
                            hipStream_t stream, bool *wrote_out) {
     const Layout ly = choose_layout(D, q, k, v);
-    const SplitFn fn = dump ? pick_split<true>(ly) : pick_split<false>(ly);
+    const Knobs kn = knobs(D, cp_dev != nullptr);
+    const SplitFn fn = dump ? pick_split<true>(ly, kn) : pick_split<false>(ly, kn);
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
-    const uint32_t hpb = choose_hpb(H, ly);
+    const uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // host current_pos: plan the exact span; device array: plan the capacity
     const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
-    const Plan plan = make_plan(batch, H, S, span);
+    const Plan plan = make_plan(batch, H, D, S, span, cp_dev != nullptr);
     size_t ml_off = 0;
     workspace_layout(batch, H, D, S, &ml_off);
 
@@ -658,7 +765,7 @@ attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_
                              uint32_t batch, uint32_t H, uint32_t D, uint32_t S, const void *ws,
                              hipStream_t stream) {
     const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
-    const Plan plan = make_plan(batch, H, S, span);
+    const Plan plan = make_plan(batch, H, D, S, span, cp_dev != nullptr);
     size_t ml_off = 0;
     workspace_layout(batch, H, D, S, &ml_off);
     CombineArgs c;
