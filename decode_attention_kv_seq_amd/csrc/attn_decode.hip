@@ -351,15 +351,31 @@ struct CombineArgs {
     uint16_t *out;
 };
 
-// One workgroup per (sequence, head).  Pass 1 finds M = max_c m_c; then, a
-// tile of chunks at a time, the weights 2^(m_c - M) go to LDS and thread
-// (cg, d) accumulates o_c[d] and l_c over chunks cg, cg+G, ... with the
-// loads of a tile independent of each other.  o and l go through the same
-// operations in the same order, so all-equal V rows give exactly 1.
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineArgs a) {
+// One workgroup per (sequence, head); thread (cg, d) handles element d of
+// chunks cg, cg+G, ...  When every chunk fits in registers (the usual case)
+// all partials are loaded in one round before any arithmetic: M = max m_c
+// across the workgroup, weights 2^(m_c - M) go through LDS, and each thread
+// sums its o_c[d]*w and l_c*w.  More chunks take a tiled loop.  o and l go
+// through the same operations in the same order, so all-equal V rows give
+// exactly 1.
+constexpr int kCombineRegs = 8;   // chunk values per thread held in registers
+
+__device__ __forceinline__ float block_max(float x, float *sm_red) {
     constexpr int NW = kCombineThreads / 64;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    if ((threadIdx.x & 63) == 0) sm_red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float M = sm_red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_red[w]);
+    return M;
+}
+
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineArgs a) {
     __shared__ float sm_w[kCombineThreads];
-    __shared__ float sm_red[NW];
+    __shared__ float sm_lc[kCombineThreads];
+    __shared__ float sm_red[kCombineThreads / 64];
     __shared__ float sm_o[kCombineThreads];
     __shared__ float sm_l[kCombineThreads];
 
@@ -371,55 +387,75 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineAr
     const size_t bh = (size_t)b * a.H + h;
     const float *ml = a.part_ml + bh * a.nc_stride * 2;
     const float *po = a.part_o + bh * a.nc_stride * a.D;
-    const int tid = threadIdx.x;
-
-    float mx = -INFINITY;
-    for (uint32_t c = tid; c < nc; c += kCombineThreads) mx = fmaxf(mx, ml[2 * c]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if ((tid & 63) == 0) sm_red[tid >> 6] = mx;
-    __syncthreads();
-    float M = sm_red[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_red[w]);
-
+    const uint32_t tid = threadIdx.x;
     const uint32_t G = kCombineThreads / a.D;   // chunk groups (D <= 256)
     const uint32_t cg = tid / a.D;
     const uint32_t d = tid % a.D;
     const bool active = cg < G;
     float o = 0.f, lsum = 0.f;
-    for (uint32_t t0 = 0; t0 < nc; t0 += kCombineThreads) {
-        const uint32_t tn = min(nc - t0, (uint32_t)kCombineThreads);
-        __syncthreads();   // previous tile's weights are consumed
-        if ((uint32_t)tid < tn) sm_w[tid] = __builtin_amdgcn_exp2f(ml[2 * (t0 + tid)] - M);
+
+    if (nc <= G * kCombineRegs && nc <= (uint32_t)kCombineThreads) {
+        // one round of loads
+        const float mc = tid < nc ? ml[2 * tid] : -INFINITY;
+        const float lc = tid < nc ? ml[2 * tid + 1] : 0.f;
+        float ov[kCombineRegs];
+#pragma unroll
+        for (int j = 0; j < kCombineRegs; ++j) {
+            const uint32_t c = cg + j * G;
+            ov[j] = (active && c < nc) ? po[(size_t)c * a.D + d] : 0.f;
+        }
+        const float M = block_max(mc, sm_red);
+        if (tid < nc) {
+            sm_w[tid] = __builtin_amdgcn_exp2f(mc - M);
+            sm_lc[tid] = lc;
+        }
         __syncthreads();
-        if (active) {
-            uint32_t c = cg;
-            for (; c + 3 * G < tn; c += 4 * G) {
-                float ov[4], lv[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    ov[u] = po[(size_t)(t0 + c + u * G) * a.D + d];
-                    lv[u] = ml[2 * (t0 + c + u * G) + 1];
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float w = sm_w[c + u * G];
-                    o = fmaf(ov[u], w, o);
-                    lsum = fmaf(lv[u], w, lsum);
-                }
-            }
-            for (; c < tn; c += G) {
+        for (int j = 0; j < kCombineRegs; ++j) {
+            const uint32_t c = cg + j * G;
+            if (active && c < nc) {
                 const float w = sm_w[c];
-                o = fmaf(po[(size_t)(t0 + c) * a.D + d], w, o);
-                lsum = fmaf(ml[2 * (t0 + c) + 1], w, lsum);
+                o = fmaf(ov[j], w, o);
+                lsum = fmaf(sm_lc[c], w, lsum);
+            }
+        }
+    } else {
+        float mx = -INFINITY;
+        for (uint32_t c = tid; c < nc; c += kCombineThreads) mx = fmaxf(mx, ml[2 * c]);
+        const float M = block_max(mx, sm_red);
+        for (uint32_t t0 = 0; t0 < nc; t0 += kCombineThreads) {
+            const uint32_t tn = min(nc - t0, (uint32_t)kCombineThreads);
+            __syncthreads();   // previous tile's weights are consumed
+            if (tid < tn) {
+                sm_w[tid] = __builtin_amdgcn_exp2f(ml[2 * (t0 + tid)] - M);
+                sm_lc[tid] = ml[2 * (t0 + tid) + 1];
+            }
+            __syncthreads();
+            if (active) {
+                uint32_t c = cg;
+                for (; c + 3 * G < tn; c += 4 * G) {
+                    float ov[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) ov[u] = po[(size_t)(t0 + c + u * G) * a.D + d];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float w = sm_w[c + u * G];
+                        o = fmaf(ov[u], w, o);
+                        lsum = fmaf(sm_lc[c + u * G], w, lsum);
+                    }
+                }
+                for (; c < tn; c += G) {
+                    const float w = sm_w[c];
+                    o = fmaf(po[(size_t)(t0 + c) * a.D + d], w, o);
+                    lsum = fmaf(sm_lc[c], w, lsum);
+                }
             }
         }
     }
     sm_o[tid] = o;
     sm_l[tid] = lsum;
     __syncthreads();
-    if (tid < (int)a.D) {
+    if (tid < a.D) {
         float os = 0.f, ls = 0.f;
         for (uint32_t r = 0; r < G; ++r) {
             os += sm_o[r * a.D + tid];
@@ -472,7 +508,7 @@ struct Knobs {
     uint32_t unroll;   // positions per row group per block (2, 4, 8)
     uint32_t pf;       // double-buffered blocks
 };
-constexpr uint32_t kChunkGranule = 64;
+constexpr uint32_t kChunkGranule = 16;
 constexpr uint32_t kMaxHeadsPerWG = kWaves * 64 / 8;   // row groups at 8 lanes per row
 
 const Knobs &env_knobs() {
@@ -604,12 +640,17 @@ Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span
     return p;
 }
 
-size_t workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, size_t *ml_offset) {
+// Workspace: [o: B*H*nc_stride*D fp32][(m,l): B*H*nc_stride*2 fp32], each
+// region 256-byte aligned.
+struct WsLayout {
+    size_t o_off, ml_off, total;
+};
+
+WsLayout workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     const size_t slots = (size_t)batch * H * chunk_bound(batch, H, D, S);
     const size_t o_bytes = (slots * D * sizeof(float) + 255) / 256 * 256;
     const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
-    if (ml_offset) *ml_offset = o_bytes;
-    return o_bytes + ml_bytes;
+    return WsLayout{0, o_bytes, o_bytes + ml_bytes};
 }
 
 attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
@@ -700,7 +741,7 @@ attn_status_t check_split(const uint16_t *q, const uint16_t *k, const uint16_t *
 
 attn_status_t check_workspace(const void *ws, size_t ws_bytes, uint32_t batch, uint32_t H,
                               uint32_t D, uint32_t S) {
-    const size_t need = workspace_layout(batch, H, D, S, nullptr);
+    const size_t need = workspace_layout(batch, H, D, S).total;
     if (!ws) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (!aligned(ws, 16)) return fail(ATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (ws_bytes < need)
@@ -723,8 +764,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     // host current_pos: plan the exact span; device array: plan the capacity
     const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
     const Plan plan = make_plan(batch, H, D, S, span, cp_dev != nullptr);
-    size_t ml_off = 0;
-    workspace_layout(batch, H, D, S, &ml_off);
+    const WsLayout wl = workspace_layout(batch, H, D, S);
 
     SplitArgs a;
     a.q = q;
@@ -741,8 +781,8 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.nc_stride = plan.nc_stride;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     a.scale = (float)(1.0 / sqrt((double)D));
-    a.part_o = ws ? static_cast<float *>(ws) : nullptr;
-    a.part_ml = ws ? reinterpret_cast<float *>(static_cast<char *>(ws) + ml_off) : nullptr;
+    a.part_o = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.o_off);
+    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.ml_off);
     a.direct = (out && plan.n_chunks == 1) ? 1 : 0;
     a.out = out;
     a.dump = dump;
@@ -766,11 +806,10 @@ attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_
                              hipStream_t stream) {
     const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
     const Plan plan = make_plan(batch, H, D, S, span, cp_dev != nullptr);
-    size_t ml_off = 0;
-    workspace_layout(batch, H, D, S, &ml_off);
+    const WsLayout wl = workspace_layout(batch, H, D, S);
     CombineArgs c;
-    c.part_o = static_cast<const float *>(ws);
-    c.part_ml = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ml_off);
+    c.part_o = reinterpret_cast<const float *>(static_cast<const char *>(ws) + wl.o_off);
+    c.part_ml = reinterpret_cast<const float *>(static_cast<const char *>(ws) + wl.ml_off);
     c.cp_dev = cp_dev;
     c.cp_host = cp_host;
     c.H = H;
@@ -809,7 +848,7 @@ extern "C" {
 size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t n_heads, uint32_t head_dim,
                                    uint32_t seq_len) {
     if (check_sizes(batch, n_heads, head_dim, seq_len) != ATTN_OK) return 0;
-    return workspace_layout(batch, n_heads, head_dim, seq_len, nullptr);
+    return workspace_layout(batch, n_heads, head_dim, seq_len).total;
 }
 
 attn_status_t attn_decode_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,

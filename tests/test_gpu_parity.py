@@ -350,17 +350,54 @@ def test_many_short_sequences():
     assert_close(out, ref, "300 sequences")
 
 
-def test_split_then_combine_equals_fused_call():
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_then_combine_matches_single_call(D):
+    """The two-launch form (split kernel, then combine kernel) gives the
+    single call's result bit for bit, and both match the oracle."""
     rng = np.random.default_rng(13)
-    S, H, D, cp = 40000, 16, 128, 33333
-    q, k, v = to_dev(randn16(rng, (H, D))), to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
-    fused = ad.decode(q, k, v, cp)
+    S, H, cp = 40000, 16, 33333
+    qh, kh, vh = randn16(rng, (H, D)), randn16(rng, (S, H, D)), randn16(rng, (S, H, D))
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
+    one = ad.decode(q, k, v, cp)
     ws = ad.alloc_workspace(1, H, D, S, DEV)
-    out = torch.empty_like(fused)
+    out = torch.empty_like(one)
     ad.split(q, k, v, cp, ws)
     ad.combine(out, cp, 1, H, D, S, ws)
     torch.cuda.synchronize()
-    assert torch.equal(out, fused)
+    ref, _, _ = oracle.decode(qh, kh, vh, cp, threads=8)
+    assert_close(one, ref, "single call")
+    assert_close(out, ref, "split + combine")
+    assert torch.equal(one, out)
+
+
+def test_workspace_reuse_across_sizes_and_repeats():
+    """One workspace reused by 72 calls of changing sizes and positions: every
+    output matches its first run bit for bit."""
+    rng = np.random.default_rng(21)
+    S, H, D = 30000, 32, 128
+    k, v = to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
+    q = to_dev(randn16(rng, (H, D)))
+    ws = ad.alloc_workspace(4, H, D, S, DEV)
+    cases = [20000, 29999, 777, 12345, 3]
+    first = {}
+    for rep in range(12):
+        for cp in cases:
+            out = ad.decode(q, k, v, cp, workspace=ws)
+            if rep == 0:
+                first[cp] = out.clone()
+            else:
+                assert torch.equal(out, first[cp]), (rep, cp)
+        # a batched call of another shape on the same workspace
+        kb = k[: 4 * 7000].view(4, 7000, H, D)
+        vb = v[: 4 * 7000].view(4, 7000, H, D)
+        qb = q.unsqueeze(0).expand(4, H, D).contiguous()
+        cpb = torch.tensor([6999, 100, 5000, 0], dtype=torch.int32, device=DEV)
+        ob = ad.decode_batched(qb, kb, vb, cpb, workspace=ws)
+        torch.cuda.synchronize()
+    ref, _, _ = oracle.decode(q.cpu(), k.cpu(), v.cpu(), 20000, threads=8)
+    assert_close(first[20000], ref, "cp=20000")
+    refb, _ = oracle.decode_batched(qb.cpu(), kb.cpu(), vb.cpu(), [6999, 100, 5000, 0], threads=8)
+    assert_close(ob, refb, "batched on a shared workspace")
 
 
 def test_side_stream():
@@ -384,3 +421,18 @@ def test_workspace_errors_on_gpu():
     with pytest.raises(ad.AttnError) as e:
         ad.decode(q, k, v, S - 1, workspace=small)
     assert e.value.status == 4
+
+
+@pytest.mark.parametrize("S,D", [(60000, 64), (30000, 128), (9000, 256)])
+def test_combine_with_many_chunks(S, D):
+    """One head and one sequence through the batched path: the workspace holds
+    more chunk partials than the combine keeps in registers (its tiled loop)."""
+    rng = np.random.default_rng(S + D)
+    q = randn16(rng, (1, 1, D), 2.0)
+    k = randn16(rng, (1, S, 1, D))
+    v = randn16(rng, (1, S, 1, D))
+    cp = torch.tensor([S - 3], dtype=torch.int32, device=DEV)
+    out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.decode(q[0], k[0], v[0], S - 3)
+    assert_close(out[0], ref, "S=%d D=%d" % (S, D))
