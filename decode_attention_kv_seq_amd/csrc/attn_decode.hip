@@ -41,7 +41,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kCombineThreads = 1024;
+constexpr uint32_t kBalancedMaxBatch = 1024;   // sequences the balanced grid handles
+constexpr uint32_t kCombineWide = 512;   // (sequence, head) pairs below which the combine uses 1024 threads
 
 // ------------------------------------------------------------------ packs
 // A pack is VEC consecutive fp16 values of one row held by one lane.
@@ -145,40 +146,59 @@ struct SplitArgs {
     const uint32_t *cp_dev;   // per-sequence current_pos, or null
     uint32_t cp_host;         // used when cp_dev is null
     uint32_t H, D, S;         // heads, head_dim, cache length per sequence
-    uint32_t chunk;           // positions per workgroup
+    uint32_t chunk;           // positions per workgroup (chunked grid)
     uint32_t n_hb;            // head blocks (H / hpb)
     uint32_t hpb;             // heads per workgroup
-    uint32_t nc_stride;       // chunk stride of the partial arrays
+    uint32_t nc_stride;       // chunk stride of the partial arrays (chunked grid)
     float scale_log2;         // log2(e) / sqrt(D)
     float scale;              // 1 / sqrt(D)
-    float *part_o;            // [B, H, nc_stride, D]
-    float *part_ml;           // [B, H, nc_stride, 2]
+    float *part_o;            // partial o rows (layout: see the kernels)
+    float *part_ml;           // partial (m, l) pairs
     uint16_t *out;            // final rows when `direct`
     float *dump;              // [B, H, S] or null
     int direct;               // 1: one chunk per sequence, write fp16 rows
+    uint32_t batch;           // sequences (balanced grid)
+    uint32_t grid;            // workgroups launched (balanced grid)
+    uint32_t *header;         // workspace header: how the partials are laid out
 };
 
-// VEC: fp16 values per lane load; GL: lanes per row (power of two);
-// NV: packs per lane per row; FULL: D == VEC*GL*NV (no element guards);
-// U: positions per row group per block; PF: double-buffered blocks.
+// Workspace header written by the split launch and read by the combine.
+enum : uint32_t { kHdrBalanced = 0, kHdrChunk, kHdrNcStride, kHdrNHb, kHdrHpb, kHdrGrid, kHdrWords };
+constexpr uint32_t kHdrPrefixWord = 64;   // balanced grid: uint64 length prefix [batch + 1] from byte 256
+constexpr size_t kHeaderBytes = 256 + ((size_t)kBalancedMaxBatch + 1) * 8 + 248;   // 256-byte multiple
+
+__device__ __forceinline__ void write_header(const SplitArgs &a, uint32_t balanced) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        a.header[kHdrBalanced] = balanced;
+        a.header[kHdrChunk] = a.chunk;
+        a.header[kHdrNcStride] = a.nc_stride;
+        a.header[kHdrNHb] = a.n_hb;
+        a.header[kHdrHpb] = a.hpb;
+        a.header[kHdrGrid] = a.grid;
+    }
+}
+
+// Where one workgroup's merged result for head ho of its head block goes:
+// o row at po + ho*po_hs, (m, l) at pml + ho*pml_hs; or, when direct, the
+// fp16 row at out + ho*D.
+struct PieceDst {
+    float *po;
+    size_t po_hs;
+    float *pml;
+    size_t pml_hs;
+    uint16_t *out;
+};
+
+// Stream positions [c0, c_end) of head block hb of sequence b through the
+// online softmax and leave one merged state per head at `dst`.  The caller
+// guarantees c0 < c_end.  LDS is free again when this returns.
 template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
+__device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint32_t hb,
+                                            uint32_t c0, uint32_t c_end, const PieceDst &dst,
+                                            float *sm_o, float *sm_m, float *sm_l) {
     constexpr int RG = 64 / GL;              // row groups per wave
     constexpr int NG = kWaves * RG;          // row groups per workgroup
     constexpr int DPAD = VEC * GL * NV;      // padded row length in LDS
-
-    __shared__ float sm_o[NG * DPAD];
-    __shared__ float sm_m[NG];
-    __shared__ float sm_l[NG];
-
-    const uint32_t b = blockIdx.y;
-    const uint32_t hb = blockIdx.x % a.n_hb;
-    const uint32_t chunk = blockIdx.x / a.n_hb;
-    const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
-    const uint32_t L = valid_len(cp, a.S);
-    const uint32_t c0 = chunk * a.chunk;
-    if (c0 >= L) return;                     // whole workgroup: nothing to read
-    const uint32_t c_end = min(c0 + a.chunk, L);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -325,18 +345,136 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
             o = fmaf(sm_o[gg * DPAD + d], w, o);
             lsum = fmaf(sm_l[gg], w, lsum);
         }
-        const uint32_t hh = hb * a.hpb + ho;
-        const size_t bh = (size_t)b * a.H + hh;
-        if (a.direct) {
-            a.out[bh * a.D + d] = f2h_rne(o / lsum);
+        if (dst.out) {
+            dst.out[ho * a.D + d] = f2h_rne(o / lsum);
         } else {
-            const size_t slot = bh * a.nc_stride + chunk;
-            a.part_o[slot * a.D + d] = o;
+            dst.po[ho * dst.po_hs + d] = o;
             if (d == 0) {
-                a.part_ml[slot * 2] = M;
-                a.part_ml[slot * 2 + 1] = lsum;
+                dst.pml[ho * dst.pml_hs] = M;
+                dst.pml[ho * dst.pml_hs + 1] = lsum;
             }
         }
+    }
+    __syncthreads();   // LDS may be reused by the caller's next piece
+}
+
+// VEC: fp16 values per lane load; GL: lanes per row (power of two);
+// NV: packs per lane per row; FULL: D == VEC*GL*NV (no element guards);
+// U: positions per row group per block; PF: double-buffered blocks.
+#define ATTN_SPLIT_LDS                                                                   \
+    constexpr int NG_ = kWaves * (64 / GL);                                              \
+    __shared__ float sm_o[NG_ * VEC * GL * NV];                                          \
+    __shared__ float sm_m[NG_];                                                          \
+    __shared__ float sm_l[NG_];
+
+// Chunked grid: workgroup (hb + n_hb*chunk, b) takes positions
+// [chunk*C, (chunk+1)*C) of head block hb.  Partials: o [B, H, nc_stride, D],
+// (m, l) [B, H, nc_stride, 2].
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
+    ATTN_SPLIT_LDS
+    write_header(a, 0);
+    const uint32_t b = blockIdx.y;
+    const uint32_t hb = blockIdx.x % a.n_hb;
+    const uint32_t chunk = blockIdx.x / a.n_hb;
+    const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
+    const uint32_t L = valid_len(cp, a.S);
+    const uint32_t c0 = chunk * a.chunk;
+    if (c0 >= L) return;                     // whole workgroup: nothing to read
+    const uint32_t c_end = min(c0 + a.chunk, L);
+    const size_t bh0 = (size_t)b * a.H + (size_t)hb * a.hpb;
+    PieceDst dst;
+    dst.po = a.part_o + (bh0 * a.nc_stride + chunk) * a.D;
+    dst.po_hs = (size_t)a.nc_stride * a.D;
+    dst.pml = a.part_ml + (bh0 * a.nc_stride + chunk) * 2;
+    dst.pml_hs = (size_t)a.nc_stride * 2;
+    dst.out = a.direct ? a.out + bh0 * a.D : nullptr;
+    split_piece<VEC, GL, NV, FULL, U, PF, DUMP>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+}
+
+// Inclusive prefix of the valid lengths: pref[0] = 0, pref[b+1] = sum of
+// L_0..L_b, for batch <= kBalancedMaxBatch.  Hillis-Steele scan in LDS over
+// per-thread sums of consecutive sequences.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ void length_prefix(const uint32_t *cp, uint32_t S, uint32_t batch,
+                                              uint64_t *pref, uint64_t *tmp) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t per = (batch + NT - 1) / NT;   // <= kBalancedMaxBatch / NT
+    const uint32_t b0 = tid * per;
+    uint64_t sum = 0;
+    for (uint32_t i = 0; i < per; ++i)
+        if (b0 + i < batch) sum += valid_len(cp[b0 + i], S);
+    tmp[tid] = sum;
+    __syncthreads();
+    for (uint32_t off = 1; off < NT; off <<= 1) {
+        const uint64_t add = tid >= off ? tmp[tid - off] : 0;
+        __syncthreads();
+        tmp[tid] += add;
+        __syncthreads();
+    }
+    uint64_t run = tid ? tmp[tid - 1] : 0;
+    if (tid == 0) pref[0] = 0;
+    for (uint32_t i = 0; i < per; ++i)
+        if (b0 + i < batch) {
+            run += valid_len(cp[b0 + i], S);
+            pref[b0 + i + 1] = run;
+        }
+    __syncthreads();
+}
+
+// Sequence b with pref[b] <= key < pref[b+1] (pref strictly increases: every
+// sequence has at least one position).
+__device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t batch, uint64_t key) {
+    uint32_t lo = 0, hi = batch;   // pref[lo] <= key < pref[hi]
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (pref[mid] <= key) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Balanced grid for per-sequence lengths: the batch's work, laid out as
+// segments (b, hb) of L_b positions each in order s = b*n_hb + hb, is cut into
+// `grid` equal ranges, one per workgroup.  A workgroup writes one partial per
+// segment piece it covers, at slot w + s; o [slots, hpb, D], (m, l)
+// [slots, hpb, 2] with slots = grid + batch*n_hb.
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP>
+__global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs a) {
+    ATTN_SPLIT_LDS
+    write_header(a, 1);
+    __shared__ uint64_t sm_pref[kBalancedMaxBatch + 1];
+    __shared__ uint64_t sm_tmp[kThreads];
+    length_prefix<kThreads>(a.cp_dev, a.S, a.batch, sm_pref, sm_tmp);
+    if (blockIdx.x == 0) {   // publish the prefix for the combine launch
+        uint64_t *hp = reinterpret_cast<uint64_t *>(a.header + kHdrPrefixWord);
+        for (uint32_t i = threadIdx.x; i <= a.batch; i += kThreads) hp[i] = sm_pref[i];
+    }
+    const uint64_t n_hb = a.n_hb;
+    const uint64_t W = n_hb * sm_pref[a.batch];
+    const uint64_t w = blockIdx.x;
+    // the host only picks this grid when W * grid < 2^63
+    const uint64_t lo = w * W / a.grid;
+    const uint64_t hi = (w + 1) * W / a.grid;
+    uint64_t x = lo;
+    while (x < hi) {
+        const uint32_t b = find_sequence(sm_pref, a.batch, x / n_hb);
+        const uint64_t L = sm_pref[b + 1] - sm_pref[b];
+        const uint64_t off = x - n_hb * sm_pref[b];
+        const uint32_t hb = (uint32_t)(off / L);
+        const uint64_t seg_end = n_hb * sm_pref[b] + (hb + 1) * L;
+        const uint64_t x_end = hi < seg_end ? hi : seg_end;
+        const uint32_t c0 = (uint32_t)(off % L);
+        const uint32_t c_end = c0 + (uint32_t)(x_end - x);
+        const uint64_t slot = w + (uint64_t)b * n_hb + hb;
+        PieceDst dst;
+        dst.po = a.part_o + slot * a.hpb * a.D;
+        dst.po_hs = a.D;
+        dst.pml = a.part_ml + slot * a.hpb * 2;
+        dst.pml_hs = 2;
+        dst.out = nullptr;
+        split_piece<VEC, GL, NV, FULL, U, PF, DUMP>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+        x = x_end;
     }
 }
 
@@ -347,7 +485,8 @@ struct CombineArgs {
     const float *part_ml;
     const uint32_t *cp_dev;
     uint32_t cp_host;
-    uint32_t H, D, S, chunk, nc_stride;
+    uint32_t H, D, S, batch;
+    const uint32_t *header;   // written by the split launch
     uint16_t *out;
 };
 
@@ -360,8 +499,9 @@ struct CombineArgs {
 // exactly 1.
 constexpr int kCombineRegs = 8;   // chunk values per thread held in registers
 
+template <int NT>
 __device__ __forceinline__ float block_max(float x, float *sm_red) {
-    constexpr int NW = kCombineThreads / 64;
+    constexpr int NW = NT / 64;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
     if ((threadIdx.x & 63) == 0) sm_red[threadIdx.x >> 6] = x;
@@ -372,39 +512,70 @@ __device__ __forceinline__ float block_max(float x, float *sm_red) {
     return M;
 }
 
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineArgs a) {
-    __shared__ float sm_w[kCombineThreads];
-    __shared__ float sm_lc[kCombineThreads];
-    __shared__ float sm_red[kCombineThreads / 64];
-    __shared__ float sm_o[kCombineThreads];
-    __shared__ float sm_l[kCombineThreads];
+// NT threads per workgroup: 1024 when there are few (sequence, head) pairs,
+// 256 when there are enough workgroups to fill the chip in one dispatch round.
+template <int NT>
+__global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
+    __shared__ float sm_w[NT];
+    __shared__ float sm_lc[NT];
+    __shared__ float sm_red[NT / 64];
+    __shared__ float sm_o[NT];
+    __shared__ float sm_l[NT];
 
     const uint32_t h = blockIdx.x;
     const uint32_t b = blockIdx.y;
-    const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
-    const uint32_t L = valid_len(cp, a.S);
-    const uint32_t nc = (L + a.chunk - 1) / a.chunk;
     const size_t bh = (size_t)b * a.H + h;
-    const float *ml = a.part_ml + bh * a.nc_stride * 2;
-    const float *po = a.part_o + bh * a.nc_stride * a.D;
     const uint32_t tid = threadIdx.x;
-    const uint32_t G = kCombineThreads / a.D;   // chunk groups (D <= 256)
+    uint32_t nc;              // partials of this (sequence, head)
+    const float *ml, *po;     // first partial's (m, l) and o row
+    size_t ml_cs, po_cs;      // strides between consecutive partials
+    if (!a.header[kHdrBalanced]) {
+        const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
+        const uint32_t L = valid_len(cp, a.S);
+        const uint32_t chunk = a.header[kHdrChunk];
+        const size_t nc_stride = a.header[kHdrNcStride];
+        nc = (L + chunk - 1) / chunk;
+        ml = a.part_ml + bh * nc_stride * 2;
+        po = a.part_o + bh * nc_stride * a.D;
+        ml_cs = 2;
+        po_cs = a.D;
+    } else {
+        // the split grid's workgroups w_first..w_last covered segment
+        // s = b*n_hb + hb; workgroup w left its piece at slot w + s
+        const uint64_t *pref = reinterpret_cast<const uint64_t *>(a.header + kHdrPrefixWord);
+        const uint32_t hpb = a.header[kHdrHpb];
+        const uint64_t n_hb = a.header[kHdrNHb], G = a.header[kHdrGrid];
+        const uint64_t W = n_hb * pref[a.batch];
+        const uint32_t hb = h / hpb, ho = h % hpb;
+        const uint64_t L = pref[b + 1] - pref[b];
+        const uint64_t first = n_hb * pref[b] + hb * L;
+        const uint64_t last = first + L - 1;
+        const uint64_t w_first = ((first + 1) * G - 1) / W;   // W * G < 2^63
+        const uint64_t w_last = ((last + 1) * G - 1) / W;
+        nc = (uint32_t)(w_last - w_first + 1);
+        const uint64_t slot0 = w_first + (uint64_t)b * n_hb + hb;
+        ml = a.part_ml + (slot0 * hpb + ho) * 2;
+        po = a.part_o + (slot0 * hpb + ho) * a.D;
+        ml_cs = (size_t)hpb * 2;
+        po_cs = (size_t)hpb * a.D;
+    }
+    const uint32_t G = NT / a.D;   // chunk groups (D <= 256)
     const uint32_t cg = tid / a.D;
     const uint32_t d = tid % a.D;
     const bool active = cg < G;
     float o = 0.f, lsum = 0.f;
 
-    if (nc <= G * kCombineRegs && nc <= (uint32_t)kCombineThreads) {
+    if (nc <= G * kCombineRegs && nc <= (uint32_t)NT) {
         // one round of loads
-        const float mc = tid < nc ? ml[2 * tid] : -INFINITY;
-        const float lc = tid < nc ? ml[2 * tid + 1] : 0.f;
+        const float mc = tid < nc ? ml[tid * ml_cs] : -INFINITY;
+        const float lc = tid < nc ? ml[tid * ml_cs + 1] : 0.f;
         float ov[kCombineRegs];
 #pragma unroll
         for (int j = 0; j < kCombineRegs; ++j) {
             const uint32_t c = cg + j * G;
-            ov[j] = (active && c < nc) ? po[(size_t)c * a.D + d] : 0.f;
+            ov[j] = (active && c < nc) ? po[c * po_cs + d] : 0.f;
         }
-        const float M = block_max(mc, sm_red);
+        const float M = block_max<NT>(mc, sm_red);
         if (tid < nc) {
             sm_w[tid] = __builtin_amdgcn_exp2f(mc - M);
             sm_lc[tid] = lc;
@@ -421,14 +592,14 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineAr
         }
     } else {
         float mx = -INFINITY;
-        for (uint32_t c = tid; c < nc; c += kCombineThreads) mx = fmaxf(mx, ml[2 * c]);
-        const float M = block_max(mx, sm_red);
-        for (uint32_t t0 = 0; t0 < nc; t0 += kCombineThreads) {
-            const uint32_t tn = min(nc - t0, (uint32_t)kCombineThreads);
+        for (uint32_t c = tid; c < nc; c += NT) mx = fmaxf(mx, ml[c * ml_cs]);
+        const float M = block_max<NT>(mx, sm_red);
+        for (uint32_t t0 = 0; t0 < nc; t0 += NT) {
+            const uint32_t tn = min(nc - t0, (uint32_t)NT);
             __syncthreads();   // previous tile's weights are consumed
             if (tid < tn) {
-                sm_w[tid] = __builtin_amdgcn_exp2f(ml[2 * (t0 + tid)] - M);
-                sm_lc[tid] = ml[2 * (t0 + tid) + 1];
+                sm_w[tid] = __builtin_amdgcn_exp2f(ml[(t0 + tid) * ml_cs] - M);
+                sm_lc[tid] = ml[(t0 + tid) * ml_cs + 1];
             }
             __syncthreads();
             if (active) {
@@ -436,7 +607,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineAr
                 for (; c + 3 * G < tn; c += 4 * G) {
                     float ov[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) ov[u] = po[(size_t)(t0 + c + u * G) * a.D + d];
+                    for (int u = 0; u < 4; ++u) ov[u] = po[(t0 + c + u * G) * po_cs + d];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const float w = sm_w[c + u * G];
@@ -446,7 +617,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(CombineAr
                 }
                 for (; c < tn; c += G) {
                     const float w = sm_w[c];
-                    o = fmaf(po[(size_t)(t0 + c) * a.D + d], w, o);
+                    o = fmaf(po[(t0 + c) * po_cs + d], w, o);
                     lsum = fmaf(sm_lc[c], w, lsum);
                 }
             }
@@ -499,7 +670,7 @@ attn_status_t ok() {
 // best head blocking makes each position's read 512 contiguous bytes or
 // more, and about 1024 workgroups (4 per CU) keep enough loads in flight.
 // The ATTN_DECODE_TUNE environment variable
-// ("wgs=N,cmax=N,hpb=N,unroll=N,pf=N") overrides them for tuning sweeps; it
+// ("wgs=N,cmax=N,hpb=N,unroll=N,pf=N,bal=N") overrides them for tuning sweeps; it
 // is read once per process.
 struct Knobs {
     uint32_t wgs;      // target workgroups per call
@@ -507,13 +678,14 @@ struct Knobs {
     uint32_t hpb;      // requested heads per workgroup
     uint32_t unroll;   // positions per row group per block (2, 4, 8)
     uint32_t pf;       // double-buffered blocks
+    uint32_t bal;      // per-sequence lengths: balanced grid (equal work per workgroup)
 };
 constexpr uint32_t kChunkGranule = 16;
 constexpr uint32_t kMaxHeadsPerWG = kWaves * 64 / 8;   // row groups at 8 lanes per row
 
 const Knobs &env_knobs() {
     static const Knobs t = [] {
-        Knobs r{0, 0, 0, 0, 2};
+        Knobs r{0, 0, 0, 0, 2, 2};
         const char *env = getenv("ATTN_DECODE_TUNE");
         if (env) {
             char buf[256];
@@ -527,6 +699,7 @@ const Knobs &env_knobs() {
                 else if (sscanf(tok, "unroll=%u", &v) == 1 && (v == 2 || v == 4 || v == 8))
                     r.unroll = v;
                 else if (sscanf(tok, "pf=%u", &v) == 1) r.pf = v ? 1 : 0;
+                else if (sscanf(tok, "bal=%u", &v) == 1) r.bal = v ? 1 : 0;
             }
         }
         return r;
@@ -537,15 +710,16 @@ const Knobs &env_knobs() {
 // Defaults by row size (head_dim) and by whether current_pos is per sequence.
 Knobs knobs(uint32_t D, bool batched) {
     Knobs k;
-    if (batched) k = Knobs{1792, 8192, 8, 4, 1};          // ragged batches
-    else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0};    // 128-byte rows
-    else k = Knobs{512, 8192, 2, 2, 1};                  // 256-byte rows and wider
+    if (batched) k = Knobs{1024, 8192, 8, 2, 1, 1};       // ragged batches
+    else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};  // 128-byte rows
+    else k = Knobs{512, 8192, 2, 2, 1, 0};                // 256-byte rows and wider
     const Knobs &e = env_knobs();
     if (e.wgs) k.wgs = e.wgs;
     if (e.cmax) k.cmax = e.cmax;
     if (e.hpb) k.hpb = e.hpb;
     if (e.unroll) k.unroll = e.unroll;
     if (e.pf != 2) k.pf = e.pf;
+    if (e.bal != 2) k.bal = e.bal;
     return k;
 }
 
@@ -640,17 +814,29 @@ Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span
     return p;
 }
 
-// Workspace: [o: B*H*nc_stride*D fp32][(m,l): B*H*nc_stride*2 fp32], each
-// region 256-byte aligned.
+// Workspace: [header: kHeaderBytes][o rows fp32][(m, l) pairs fp32], each region
+// 256-byte aligned.  It holds whichever partial layout the split launch
+// picks: chunked, B*H*nc_stride slots, or balanced, grid*hpb + B*H slots
+// (per-sequence lengths, batch <= kBalancedMaxBatch).
 struct WsLayout {
     size_t o_off, ml_off, total;
 };
 
+size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
+    if (batch > kBalancedMaxBatch) return 0;
+    const Knobs k = knobs(D, true);
+    const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
+    return (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
+}
+
 WsLayout workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
-    const size_t slots = (size_t)batch * H * chunk_bound(batch, H, D, S);
+    size_t slots = (size_t)batch * H * chunk_bound(batch, H, D, S);
+    const size_t bal = balanced_slots(batch, H, D);
+    if (bal > slots) slots = bal;
+    const size_t hdr = kHeaderBytes;
     const size_t o_bytes = (slots * D * sizeof(float) + 255) / 256 * 256;
     const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
-    return WsLayout{0, o_bytes, o_bytes + ml_bytes};
+    return WsLayout{hdr, hdr + o_bytes, hdr + o_bytes + ml_bytes};
 }
 
 attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
@@ -676,24 +862,30 @@ attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
 
 using SplitFn = void (*)(SplitArgs);
 
+template <int V, int G, int N, bool F, int U, bool PF, bool DUMP>
+SplitFn kernel_for(bool bal) {
+    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP>
+               : attn_split_kernel<V, G, N, F, U, PF, DUMP>;
+}
+
 template <int V, int G, int N, bool F, bool DUMP>
-SplitFn pick_unroll(const Knobs &t) {
-    if (t.unroll == 2) return t.pf ? attn_split_kernel<V, G, N, F, 2, true, DUMP>
-                                   : attn_split_kernel<V, G, N, F, 2, false, DUMP>;
-    if (t.unroll == 8) return t.pf ? attn_split_kernel<V, G, N, F, 8, true, DUMP>
-                                   : attn_split_kernel<V, G, N, F, 8, false, DUMP>;
-    return t.pf ? attn_split_kernel<V, G, N, F, 4, true, DUMP>
-                : attn_split_kernel<V, G, N, F, 4, false, DUMP>;
+SplitFn pick_unroll(const Knobs &t, bool bal) {
+    if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP>(bal)
+                                   : kernel_for<V, G, N, F, 2, false, DUMP>(bal);
+    if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP>(bal)
+                                   : kernel_for<V, G, N, F, 8, false, DUMP>(bal);
+    return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP>(bal)
+                : kernel_for<V, G, N, F, 4, false, DUMP>(bal);
 }
 
 template <bool DUMP>
-SplitFn pick_split(const Layout &ly, const Knobs &k) {
+SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     // fast paths: head_dim 64 and 128 with 16-byte rows
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP>(k);
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP>(k);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP>(k, bal);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP>(k, bal);
 #define ATTN_CASE(V, G, N, F)                                                          \
     if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
-        return attn_split_kernel<V, G, N, F, 4, true, DUMP>;
+        return kernel_for<V, G, N, F, 4, true, DUMP>(bal);
     ATTN_CASE(8, 32, 1, true)
     ATTN_CASE(8, 8, 1, false)
     ATTN_CASE(8, 16, 1, false)
@@ -758,9 +950,12 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
                            hipStream_t stream, bool *wrote_out) {
     const Layout ly = choose_layout(D, q, k, v);
     const Knobs kn = knobs(D, cp_dev != nullptr);
-    const SplitFn fn = dump ? pick_split<true>(ly, kn) : pick_split<false>(ly, kn);
-    if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
     const uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
+    // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
+    const bool bal = cp_dev != nullptr && kn.bal && batch <= kBalancedMaxBatch &&
+                     (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
+    const SplitFn fn = dump ? pick_split<true>(ly, kn, bal) : pick_split<false>(ly, kn, bal);
+    if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
     // host current_pos: plan the exact span; device array: plan the capacity
     const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
     const Plan plan = make_plan(batch, H, D, S, span, cp_dev != nullptr);
@@ -781,11 +976,16 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.nc_stride = plan.nc_stride;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     a.scale = (float)(1.0 / sqrt((double)D));
+    a.header = static_cast<uint32_t *>(ws);
     a.part_o = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.o_off);
     a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.ml_off);
-    a.direct = (out && plan.n_chunks == 1) ? 1 : 0;
+    a.direct = (!bal && out && plan.n_chunks == 1) ? 1 : 0;
     a.out = out;
     a.dump = dump;
+    a.batch = batch;
+    // balanced: at most one workgroup per unit of work, so none is empty
+    const uint64_t units_min = (uint64_t)batch * a.n_hb;
+    a.grid = bal ? (uint32_t)(kn.wgs < units_min ? kn.wgs : units_min) : 0;
     *wrote_out = a.direct != 0;
 
     if (dump) {
@@ -796,7 +996,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
         attn_status_t s = hip_check("dump fill launch");
         if (s != ATTN_OK) return s;
     }
-    dim3 grid(a.n_hb * plan.n_chunks, batch);
+    const dim3 grid = bal ? dim3(a.grid) : dim3(a.n_hb * plan.n_chunks, batch);
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, a);
     return hip_check("split kernel launch");
 }
@@ -804,10 +1004,9 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
 attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_host,
                              uint32_t batch, uint32_t H, uint32_t D, uint32_t S, const void *ws,
                              hipStream_t stream) {
-    const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
-    const Plan plan = make_plan(batch, H, D, S, span, cp_dev != nullptr);
     const WsLayout wl = workspace_layout(batch, H, D, S);
     CombineArgs c;
+    c.header = static_cast<const uint32_t *>(ws);
     c.part_o = reinterpret_cast<const float *>(static_cast<const char *>(ws) + wl.o_off);
     c.part_ml = reinterpret_cast<const float *>(static_cast<const char *>(ws) + wl.ml_off);
     c.cp_dev = cp_dev;
@@ -815,10 +1014,12 @@ attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_
     c.H = H;
     c.D = D;
     c.S = S;
-    c.chunk = plan.chunk;
-    c.nc_stride = plan.nc_stride;
+    c.batch = batch;
     c.out = out;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(H, batch), dim3(kCombineThreads), 0, stream, c);
+    if ((uint64_t)batch * H < kCombineWide)
+        hipLaunchKernelGGL(attn_combine_kernel<1024>, dim3(H, batch), dim3(1024), 0, stream, c);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<256>, dim3(H, batch), dim3(256), 0, stream, c);
     return hip_check("combine kernel launch");
 }
 

@@ -436,3 +436,34 @@ def test_combine_with_many_chunks(S, D):
     torch.cuda.synchronize()
     ref, _, _ = oracle.decode(q[0], k[0], v[0], S - 3)
     assert_close(out[0], ref, "S=%d D=%d" % (S, D))
+
+
+def test_batched_extreme_ragged_lengths():
+    """One long sequence among many of length 1 and a few in between: the
+    balanced grid splits the long one across many workgroups."""
+    rng = np.random.default_rng(31)
+    B, S, H, D = 40, 5000, 8, 128
+    q, k, v = randn16(rng, (B, H, D), 2.0), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = np.zeros(B, dtype=np.int64)
+    pos[3], pos[17], pos[39] = 4999, 2500, 63
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    out, dump = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp, dump=True)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.decode_batched(q, k, v, pos, want_scores=True)
+    assert_close(out, ref, "extreme ragged")
+    for b in (0, 3, 17, 39):
+        assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "b=%d" % b)
+
+
+def test_batched_more_sequences_than_balanced_grid_handles():
+    """1100 short sequences: past the balanced grid's batch limit the chunked
+    grid serves the call."""
+    rng = np.random.default_rng(32)
+    B, S, H, D = 1100, 24, 2, 16
+    q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, 30, B)
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_batched(q, k, v, pos)
+    assert_close(out, ref, "1100 sequences")
