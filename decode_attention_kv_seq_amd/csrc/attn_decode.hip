@@ -396,14 +396,14 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
 // L_0..L_b, for batch <= kBalancedMaxBatch.  Hillis-Steele scan in LDS over
 // per-thread sums of consecutive sequences.  Every thread must call it.
 template <int NT>
-__device__ __forceinline__ void length_prefix(const uint32_t *cp, uint32_t S, uint32_t batch,
-                                              uint64_t *pref, uint64_t *tmp) {
+__device__ __forceinline__ void length_prefix(const uint32_t *cp, uint32_t cp_host, uint32_t S,
+                                              uint32_t batch, uint64_t *pref, uint64_t *tmp) {
     const uint32_t tid = threadIdx.x;
     const uint32_t per = (batch + NT - 1) / NT;   // <= kBalancedMaxBatch / NT
     const uint32_t b0 = tid * per;
     uint64_t sum = 0;
     for (uint32_t i = 0; i < per; ++i)
-        if (b0 + i < batch) sum += valid_len(cp[b0 + i], S);
+        if (b0 + i < batch) sum += valid_len(cp ? cp[b0 + i] : cp_host, S);
     tmp[tid] = sum;
     __syncthreads();
     for (uint32_t off = 1; off < NT; off <<= 1) {
@@ -416,7 +416,7 @@ __device__ __forceinline__ void length_prefix(const uint32_t *cp, uint32_t S, ui
     if (tid == 0) pref[0] = 0;
     for (uint32_t i = 0; i < per; ++i)
         if (b0 + i < batch) {
-            run += valid_len(cp[b0 + i], S);
+            run += valid_len(cp ? cp[b0 + i] : cp_host, S);
             pref[b0 + i + 1] = run;
         }
     __syncthreads();
@@ -445,17 +445,20 @@ __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs
     write_header(a, 1);
     __shared__ uint64_t sm_pref[kBalancedMaxBatch + 1];
     __shared__ uint64_t sm_tmp[kThreads];
-    length_prefix<kThreads>(a.cp_dev, a.S, a.batch, sm_pref, sm_tmp);
+    length_prefix<kThreads>(a.cp_dev, a.cp_host, a.S, a.batch, sm_pref, sm_tmp);
     if (blockIdx.x == 0) {   // publish the prefix for the combine launch
         uint64_t *hp = reinterpret_cast<uint64_t *>(a.header + kHdrPrefixWord);
         for (uint32_t i = threadIdx.x; i <= a.batch; i += kThreads) hp[i] = sm_pref[i];
     }
     const uint64_t n_hb = a.n_hb;
     const uint64_t W = n_hb * sm_pref[a.batch];
+    // at most one workgroup per unit of work, so every range is non-empty
+    const uint64_t G = a.grid < W ? a.grid : W;
     const uint64_t w = blockIdx.x;
+    if (w >= G) return;
     // the host only picks this grid when W * grid < 2^63
-    const uint64_t lo = w * W / a.grid;
-    const uint64_t hi = (w + 1) * W / a.grid;
+    const uint64_t lo = w * W / G;
+    const uint64_t hi = (w + 1) * W / G;
     uint64_t x = lo;
     while (x < hi) {
         const uint32_t b = find_sequence(sm_pref, a.batch, x / n_hb);
@@ -544,8 +547,9 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
         // s = b*n_hb + hb; workgroup w left its piece at slot w + s
         const uint64_t *pref = reinterpret_cast<const uint64_t *>(a.header + kHdrPrefixWord);
         const uint32_t hpb = a.header[kHdrHpb];
-        const uint64_t n_hb = a.header[kHdrNHb], G = a.header[kHdrGrid];
+        const uint64_t n_hb = a.header[kHdrNHb];
         const uint64_t W = n_hb * pref[a.batch];
+        const uint64_t G = a.header[kHdrGrid] < W ? a.header[kHdrGrid] : W;   // as the split did
         const uint32_t hb = h / hpb, ho = h % hpb;
         const uint64_t L = pref[b + 1] - pref[b];
         const uint64_t first = n_hb * pref[b] + hb * L;
@@ -710,7 +714,7 @@ const Knobs &env_knobs() {
 // Defaults by row size (head_dim) and by whether current_pos is per sequence.
 Knobs knobs(uint32_t D, bool batched) {
     Knobs k;
-    if (batched) k = Knobs{1024, 8192, 8, 2, 1, 1};       // ragged batches
+    if (batched) k = Knobs{256, 8192, 8, 2, 1, 1};        // ragged batches
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};  // 128-byte rows
     else k = Knobs{512, 8192, 2, 2, 1, 0};                // 256-byte rows and wider
     const Knobs &e = env_knobs();
@@ -952,7 +956,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     const Knobs kn = knobs(D, cp_dev != nullptr);
     const uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
-    const bool bal = cp_dev != nullptr && kn.bal && batch <= kBalancedMaxBatch &&
+    const bool bal = kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
     const SplitFn fn = dump ? pick_split<true>(ly, kn, bal) : pick_split<false>(ly, kn, bal);
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
@@ -983,9 +987,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.out = out;
     a.dump = dump;
     a.batch = batch;
-    // balanced: at most one workgroup per unit of work, so none is empty
-    const uint64_t units_min = (uint64_t)batch * a.n_hb;
-    a.grid = bal ? (uint32_t)(kn.wgs < units_min ? kn.wgs : units_min) : 0;
+    a.grid = bal ? kn.wgs : 0;
     *wrote_out = a.direct != 0;
 
     if (dump) {
