@@ -76,8 +76,10 @@ def cpu_baseline(w, seconds: float):
     order = rng.permutation(len(units))
     units = [units[i] for i in order]
 
+    bt = w.block_table() if w.paged else None
+
     def one(b, h):
-        q, k, v = wl.head_slice(w, b, h)
+        q, k, v = wl.head_slice_paged(w, b, h, bt) if w.paged else wl.head_slice(w, b, h)
         return q[0], k, v, int(pos[b]), k.shape[0] * w.head_dim * 2 * 2
 
     # estimate the rate on one unit, then size a sample of ~`seconds`
@@ -148,7 +150,7 @@ def main():
 
     t0 = time.perf_counter()
     q = wl.make_q(w, dev)
-    k0, v0 = wl.make_kv(w, dev)
+    k0, v0 = wl.make_kv_paged(w, dev) if w.paged else wl.make_kv(w, dev)
     kv_alloc = 2 * k0.numel() * 2
     copies = args.rotate or max(1, math.ceil((2 << 30) / kv_alloc))
     ks, vs = [k0], [v0]
@@ -159,7 +161,10 @@ def main():
     log("inputs: %s, %d cop%s of %.1f MiB K+V, generated in %.1f s"
         % (name, copies, "y" if copies == 1 else "ies", kv_alloc / 2 ** 20, time.perf_counter() - t0))
 
-    B, S, H, D = w.kv_shape
+    B, S, H, D = w.kv_shape   # S: capacity per sequence (max_blocks * page_size when paged)
+    if w.paged:
+        S = w.max_blocks * w.page_size
+        bt = w.block_table().to(torch.int32).to(dev)
     out = torch.empty(w.q_shape, dtype=torch.float16, device=dev)
     ws = ad.alloc_workspace(B, H, D, S, dev)
     ws_bytes = ws.numel()
@@ -177,6 +182,13 @@ def main():
     # pre-marshalled arguments: the timed loop is one ctypes call per step
     full_args, split_args = [], []
     for r in range(copies):
+        if w.paged:
+            common = (vp(q.data_ptr()), vp(ks[r].data_ptr()), vp(vs[r].data_ptr()))
+            tail = (vp(bt.data_ptr()), vp(cp_dev.data_ptr()), B, H, D, w.page_size, w.max_blocks,
+                    w.num_blocks, None, vp(ws.data_ptr()), ws_bytes, sh)
+            full_args.append(common + (vp(out.data_ptr()),) + tail)
+            split_args.append(common + tail)
+            continue
         if w.batched:
             full_args.append((vp(q.data_ptr()), vp(ks[r].data_ptr()), vp(vs[r].data_ptr()),
                               vp(out.data_ptr()), vp(cp_dev.data_ptr()), B, H, D, S, None,
@@ -190,7 +202,9 @@ def main():
                            B, H, D, S, None, vp(ws.data_ptr()), ws_bytes, sh))
     combine_args = (vp(out.data_ptr()), vp(cp_dev.data_ptr()) if cp_dev is not None else None,
                     cp_host, B, H, D, S, vp(ws.data_ptr()), ws_bytes, sh)
-    full = lib.attn_decode_f16_batched if w.batched else lib.attn_decode_f16
+    full = (lib.attn_decode_f16_paged if w.paged else
+            lib.attn_decode_f16_batched if w.batched else lib.attn_decode_f16)
+    split = lib.attn_decode_f16_paged_split if w.paged else lib.attn_decode_f16_split
 
     def check(rc):
         if rc != 0:
@@ -222,7 +236,7 @@ def main():
            for _ in range(n_split)]
     for i in range(n_split):
         evs[i][0].record(stream)
-        check(lib.attn_decode_f16_split(*split_args[i % copies]))
+        check(split(*split_args[i % copies]))
         evs[i][1].record(stream)
         check(lib.attn_decode_f16_combine(*combine_args))
     torch.cuda.synchronize()
@@ -254,6 +268,7 @@ def main():
         "workload": name,
         "batch": B, "n_heads": H, "head_dim": D, "seq_len": S,
         "current_pos": w.cur_pos if not w.batched else "per-sequence U[0,%d]" % (S - 1),
+        "page_size": w.page_size or None,
         "kv_bytes_per_step": nbytes,
         "kv_copies_rotated": copies,
         "us_per_step": round(ms * 1e3, 3),

@@ -59,6 +59,12 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_f16_split.restype = ctypes.c_int
     lib.attn_decode_f16_combine.argtypes = [vp, vp, u32, u32, u32, u32, u32, vp, sz, vp]
     lib.attn_decode_f16_combine.restype = ctypes.c_int
+    lib.attn_decode_f16_paged.argtypes = [vp, vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32,
+                                          vp, vp, sz, vp]
+    lib.attn_decode_f16_paged.restype = ctypes.c_int
+    lib.attn_decode_f16_paged_split.argtypes = [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32,
+                                                vp, vp, sz, vp]
+    lib.attn_decode_f16_paged_split.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -214,3 +220,56 @@ def combine(out, current_pos, batch, n_heads, head_dim, seq_len, workspace, *, s
                                        workspace.numel() * workspace.element_size(),
                                        _stream_handle(stream)))
     return out
+
+
+def _paged_args(q, k_pool, v_pool, block_table, current_pos):
+    _req(k_pool, "k_pool", torch.float16)
+    dev = k_pool.device
+    _req(q, "q", torch.float16, dev)
+    _req(v_pool, "v_pool", torch.float16, dev)
+    if k_pool.dim() != 4 or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool must be [num_blocks, page_size, n_heads, head_dim]")
+    NB, P, H, D = k_pool.shape
+    if q.dim() != 3 or tuple(q.shape[1:]) != (H, D):
+        raise ValueError("q must be [batch, n_heads, head_dim]")
+    B = q.shape[0]
+    if not isinstance(block_table, torch.Tensor) or block_table.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("block_table must be an int32/uint32 GPU tensor")
+    _req(block_table, "block_table", block_table.dtype, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [batch, max_blocks]")
+    cp = _cp_tensor(current_pos, B, dev)
+    return B, H, D, P, block_table.shape[1], NB, cp
+
+
+def decode_paged(q, k_pool, v_pool, block_table, current_pos, *, out=None, dump=False,
+                 workspace=None, stream=None):
+    """Paged cache: q [B, H, D]; k/v pools [num_blocks, page_size, H, D];
+    block_table int32 [B, max_blocks]; current_pos int32 [B] (GPU tensors)."""
+    lib = load_library()
+    B, H, D, P, MB, NB, cp = _paged_args(q, k_pool, v_pool, block_table, current_pos)
+    dev = k_pool.device
+    cap = P * MB
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float16, device=dev)
+    _req(out, "out", torch.float16, dev)
+    sc = torch.empty((B, H, cap), dtype=torch.float32, device=dev) if dump else None
+    if workspace is None:
+        workspace = alloc_workspace(B, H, D, cap, dev)
+    _check(lib.attn_decode_f16_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+                                     _ptr(block_table), _ptr(cp), B, H, D, P, MB, NB, _ptr(sc),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream)))
+    return (out, sc) if dump else out
+
+
+def split_paged(q, k_pool, v_pool, block_table, current_pos, workspace, *, dump=None, stream=None):
+    """First launch of a paged decode; `combine(out, current_pos, B, H, D,
+    max_blocks * page_size, workspace)` is the second."""
+    lib = load_library()
+    B, H, D, P, MB, NB, cp = _paged_args(q, k_pool, v_pool, block_table, current_pos)
+    _check(lib.attn_decode_f16_paged_split(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                           _ptr(cp), B, H, D, P, MB, NB, _ptr(dump),
+                                           _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream_handle(stream)))

@@ -160,6 +160,10 @@ struct SplitArgs {
     uint32_t batch;           // sequences (balanced grid)
     uint32_t grid;            // workgroups launched (balanced grid)
     uint32_t *header;         // workspace header: how the partials are laid out
+    const uint32_t *block_table;  // paged cache: [batch, max_blocks] page ids, or null
+    uint32_t max_blocks;      // block-table row length
+    uint32_t num_blocks;      // pages in the pool
+    uint32_t page_shift;      // log2(positions per page)
 };
 
 // Workspace header written by the split launch and read by the combine.
@@ -192,7 +196,7 @@ struct PieceDst {
 // Stream positions [c0, c_end) of head block hb of sequence b through the
 // online softmax and leave one merged state per head at `dst`.  The caller
 // guarantees c0 < c_end.  LDS is free again when this returns.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED>
 __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint32_t hb,
                                             uint32_t c0, uint32_t c_end, const PieceDst &dst,
                                             float *sm_o, float *sm_m, float *sm_l) {
@@ -226,9 +230,14 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     for (int j = 0; j < NV; ++j)
         qp[j] = eok[j] ? load_pack<VEC>(qrow + eoff[j]) : zero_pack<VEC>();
 
-    const size_t seq_base = (size_t)b * a.S * HD + (size_t)h * D;
+    // dense: sequence b's rows start at b*S*H*D; paged: rows live in pool
+    // pages [num_blocks, page, H, D] named by the sequence's block-table row
+    const uint32_t *bt = PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr;
+    const size_t seq_base = (PAGED ? 0 : (size_t)b * a.S * HD) + (size_t)h * D;
     const uint16_t *kbase = a.k + seq_base;
     const uint16_t *vbase = a.v + seq_base;
+    auto row_of = [&](uint32_t p) -> size_t { return (size_t)p * HD; };
+    // paged rows: any table entry >= num_blocks reads the last page (in bounds)
 
     float m = -INFINITY, l = 0.f;
     float acc[NV][VEC];
@@ -242,11 +251,33 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     struct Block {
         Pack<VEC> k[U][NV], v[U][NV];
     };
-    auto load_block = [&](Block &blk, uint32_t base) {
+    // Page ids of a block's positions (paged caches).  They are fetched one
+    // block ahead of the K/V loads that need them, and before the K/V loads of
+    // the block in between, so waiting for them never waits for K/V data.
+    struct Pids {
+        uint32_t id[U];
+    };
+    auto fetch_pids = [&](Pids &pi, uint32_t base) {
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t p = base + u * pps + pg;
+                pi.id[u] = bt[(p < c_end ? p : c0) >> a.page_shift];
+            }
+        }
+    };
+    auto load_rows = [&](Block &blk, uint32_t base, const Pids &pi) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t p = base + u * pps + pg;
-            const size_t row = (size_t)(p < c_end ? p : c0) * HD;
+            const uint32_t pc = p < c_end ? p : c0;
+            size_t row;
+            if constexpr (PAGED) {
+                const uint32_t page = pi.id[u] < a.num_blocks ? pi.id[u] : a.num_blocks - 1;
+                row = ((size_t)page << a.page_shift | (pc & ((1u << a.page_shift) - 1u))) * HD;
+            } else {
+                row = row_of(pc);
+            }
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 blk.k[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
@@ -293,30 +324,43 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 
     const uint32_t step = pps * U;
     if constexpr (PF) {
-        // two register blocks: the next block's loads are in flight while the
-        // current one is reduced
+        // Two register blocks: the next block's loads are in flight while the
+        // current one is reduced.  The steady-state loop issues its loads
+        // unconditionally (the last one or two blocks are peeled off), so the
+        // compiler's wait counts cover only the block being reduced.
         Block A, B;
+        Pids P0{}, P1{};
+        const uint32_t n = (c_end - c0 + step - 1) / step;   // blocks, >= 1
         uint32_t base = c0;
-        load_block(A, base);
-        while (true) {
-            uint32_t nb = base + step;
-            const bool more = nb < c_end;
-            if (more) load_block(B, nb);
+        fetch_pids(P0, base);
+        fetch_pids(P1, base + step);
+        load_rows(A, base, P0);
+        uint32_t i = 0;
+        for (; i + 2 < n; i += 2) {
+            fetch_pids(P0, base + 2 * step);
+            load_rows(B, base + step, P1);
             consume(A, base);
-            if (!more) break;
-            base = nb;
-            nb = base + step;
-            const bool more2 = nb < c_end;
-            if (more2) load_block(A, nb);
-            consume(B, base);
-            if (!more2) break;
-            base = nb;
+            fetch_pids(P1, base + 3 * step);
+            load_rows(A, base + 2 * step, P0);
+            consume(B, base + step);
+            base += 2 * step;
+        }
+        if (i + 1 < n) {
+            load_rows(B, base + step, P1);
+            consume(A, base);
+            consume(B, base + step);
+        } else {
+            consume(A, base);
         }
     } else {
+        Pids P0{}, P1{};
+        fetch_pids(P0, c0);
         for (uint32_t base = c0; base < c_end; base += step) {
             Block A;
-            load_block(A, base);
+            fetch_pids(P1, base + step);
+            load_rows(A, base, P0);
             consume(A, base);
+            P0 = P1;
         }
     }
 
@@ -370,7 +414,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 // Chunked grid: workgroup (hb + n_hb*chunk, b) takes positions
 // [chunk*C, (chunk+1)*C) of head block hb.  Partials: o [B, H, nc_stride, D],
 // (m, l) [B, H, nc_stride, 2].
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     write_header(a, 0);
@@ -389,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     dst.pml = a.part_ml + (bh0 * a.nc_stride + chunk) * 2;
     dst.pml_hs = (size_t)a.nc_stride * 2;
     dst.out = a.direct ? a.out + bh0 * a.D : nullptr;
-    split_piece<VEC, GL, NV, FULL, U, PF, DUMP>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+    split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
 }
 
 // Inclusive prefix of the valid lengths: pref[0] = 0, pref[b+1] = sum of
@@ -439,7 +483,7 @@ __device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t
 // `grid` equal ranges, one per workgroup.  A workgroup writes one partial per
 // segment piece it covers, at slot w + s; o [slots, hpb, D], (m, l)
 // [slots, hpb, 2] with slots = grid + batch*n_hb.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED>
 __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     write_header(a, 1);
@@ -476,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs
         dst.pml = a.part_ml + slot * a.hpb * 2;
         dst.pml_hs = 2;
         dst.out = nullptr;
-        split_piece<VEC, GL, NV, FULL, U, PF, DUMP>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+        split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
         x = x_end;
     }
 }
@@ -711,12 +755,15 @@ const Knobs &env_knobs() {
     return t;
 }
 
-// Defaults by row size (head_dim) and by whether current_pos is per sequence.
-Knobs knobs(uint32_t D, bool batched) {
+// Defaults by row size (head_dim) and by call kind: one sequence (host
+// current_pos), a batch with per-sequence lengths, or a paged batch.
+enum class Kind { single, batched, paged };
+
+Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
-    if (batched) k = Knobs{256, 8192, 8, 2, 1, 1};        // ragged batches
-    else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};  // 128-byte rows
-    else k = Knobs{512, 8192, 2, 2, 1, 0};                // 256-byte rows and wider
+    if (kind != Kind::single) k = Knobs{256, 8192, 8, 4, 1, 1};        // batches, dense or paged
+    else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
+    else k = Knobs{512, 8192, 2, 2, 1, 0};                             // 256-byte rows and wider
     const Knobs &e = env_knobs();
     if (e.wgs) k.wgs = e.wgs;
     if (e.cmax) k.cmax = e.cmax;
@@ -795,16 +842,19 @@ uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S)
 // Workspace chunk stride: covers single-sequence and batched plans, so it
 // depends on sizes only.
 uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
-    const uint32_t a = chunk_bound_for(knobs(D, false), batch, H, S);
-    const uint32_t b = chunk_bound_for(knobs(D, true), batch, H, S);
-    return a > b ? a : b;
+    uint32_t m = 0;
+    for (Kind kd : {Kind::single, Kind::batched, Kind::paged}) {
+        const uint32_t c = chunk_bound_for(knobs(D, kd), batch, H, S);
+        if (c > m) m = c;
+    }
+    return m;
 }
 
 // Chunk size for `span` positions.  The head blocking assumed here is the
 // one of the widest-load layout for this head_dim, so the plan depends on
 // sizes only (the combine launch recomputes it without the cache pointers).
-Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span, bool batched) {
-    const Knobs k = knobs(D, batched);
+Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span, Kind kind) {
+    const Knobs k = knobs(D, kind);
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     const uint64_t n_hb = H / heads_per_wg(H, best, k.hpb);
     const uint64_t nt = cdiv(k.wgs, (uint64_t)batch * n_hb);
@@ -828,9 +878,14 @@ struct WsLayout {
 
 size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
     if (batch > kBalancedMaxBatch) return 0;
-    const Knobs k = knobs(D, true);
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
-    return (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
+    size_t m = 0;
+    for (Kind kd : {Kind::single, Kind::batched, Kind::paged}) {
+        const Knobs k = knobs(D, kd);
+        const size_t n = (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
+        if (n > m) m = n;
+    }
+    return m;
 }
 
 WsLayout workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
@@ -866,30 +921,37 @@ attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
 
 using SplitFn = void (*)(SplitArgs);
 
-template <int V, int G, int N, bool F, int U, bool PF, bool DUMP>
+template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED>
 SplitFn kernel_for(bool bal) {
-    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP>
-               : attn_split_kernel<V, G, N, F, U, PF, DUMP>;
+    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED>
+               : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED>;
 }
 
-template <int V, int G, int N, bool F, bool DUMP>
+// Dense caches honour the unroll/prefetch knobs on the fast layouts; paged
+// caches are double-buffered with U=2 or U=4.
+template <int V, int G, int N, bool F, bool DUMP, bool PAGED>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
-    if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP>(bal)
-                                   : kernel_for<V, G, N, F, 2, false, DUMP>(bal);
-    if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP>(bal)
-                                   : kernel_for<V, G, N, F, 8, false, DUMP>(bal);
-    return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP>(bal)
-                : kernel_for<V, G, N, F, 4, false, DUMP>(bal);
+    if constexpr (PAGED) {
+        return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED>(bal)
+                             : kernel_for<V, G, N, F, 2, true, DUMP, PAGED>(bal);
+    } else {
+        if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP, PAGED>(bal)
+                                       : kernel_for<V, G, N, F, 2, false, DUMP, PAGED>(bal);
+        if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP, PAGED>(bal)
+                                       : kernel_for<V, G, N, F, 8, false, DUMP, PAGED>(bal);
+        return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED>(bal)
+                    : kernel_for<V, G, N, F, 4, false, DUMP, PAGED>(bal);
+    }
 }
 
-template <bool DUMP>
+template <bool DUMP, bool PAGED>
 SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     // fast paths: head_dim 64 and 128 with 16-byte rows
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP>(k, bal);
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP>(k, bal);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP, PAGED>(k, bal);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP, PAGED>(k, bal);
 #define ATTN_CASE(V, G, N, F)                                                          \
     if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
-        return kernel_for<V, G, N, F, 4, true, DUMP>(bal);
+        return kernel_for<V, G, N, F, 4, true, DUMP, PAGED>(bal);
     ATTN_CASE(8, 32, 1, true)
     ATTN_CASE(8, 8, 1, false)
     ATTN_CASE(8, 16, 1, false)
@@ -948,21 +1010,29 @@ attn_status_t check_workspace(const void *ws, size_t ws_bytes, uint32_t batch, u
 
 // Enqueue the split kernel (and the dump fill).  `out` non-null and a single
 // chunk per sequence: the split kernel writes the final rows itself.
+// A paged cache: pool pages [num_blocks, page, H, D] and a device block table.
+struct Paging {
+    const uint32_t *block_table;
+    uint32_t max_blocks, num_blocks, page_shift;
+};
+
 attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
                            uint32_t D, uint32_t S, float *dump, void *ws, uint16_t *out,
-                           hipStream_t stream, bool *wrote_out) {
+                           const Paging *pg, hipStream_t stream, bool *wrote_out) {
     const Layout ly = choose_layout(D, q, k, v);
-    const Knobs kn = knobs(D, cp_dev != nullptr);
+    const Kind kind = pg ? Kind::paged : cp_dev ? Kind::batched : Kind::single;
+    const Knobs kn = knobs(D, kind);
     const uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
-    const SplitFn fn = dump ? pick_split<true>(ly, kn, bal) : pick_split<false>(ly, kn, bal);
+    const SplitFn fn = pg ? (dump ? pick_split<true, true>(ly, kn, bal) : pick_split<false, true>(ly, kn, bal))
+                          : (dump ? pick_split<true, false>(ly, kn, bal) : pick_split<false, false>(ly, kn, bal));
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
     // host current_pos: plan the exact span; device array: plan the capacity
     const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
-    const Plan plan = make_plan(batch, H, D, S, span, cp_dev != nullptr);
+    const Plan plan = make_plan(batch, H, D, S, span, kind);
     const WsLayout wl = workspace_layout(batch, H, D, S);
 
     SplitArgs a;
@@ -988,6 +1058,10 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.dump = dump;
     a.batch = batch;
     a.grid = bal ? kn.wgs : 0;
+    a.block_table = pg ? pg->block_table : nullptr;
+    a.max_blocks = pg ? pg->max_blocks : 0;
+    a.num_blocks = pg ? pg->num_blocks : 0;
+    a.page_shift = pg ? pg->page_shift : 0;
     *wrote_out = a.direct != 0;
 
     if (dump) {
@@ -1028,7 +1102,7 @@ attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_
 attn_status_t decode_full(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                           const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
                           uint32_t D, uint32_t S, float *dump, void *ws, size_t ws_bytes,
-                          void *stream) {
+                          const Paging *pg, void *stream) {
     attn_status_t s = check_split(q, k, v, cp_dev, batch, H, D, S, dump);
     if (s != ATTN_OK) return s;
     if (!out) return fail(ATTN_ERR_NULL, "out must be non-NULL");
@@ -1037,9 +1111,32 @@ attn_status_t decode_full(const uint16_t *q, const uint16_t *k, const uint16_t *
     if (s != ATTN_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool wrote = false;
-    s = launch_split(q, k, v, cp_dev, cp_host, batch, H, D, S, dump, ws, out, st, &wrote);
+    s = launch_split(q, k, v, cp_dev, cp_host, batch, H, D, S, dump, ws, out, pg, st, &wrote);
     if (s != ATTN_OK || wrote) return s;
     return launch_combine(out, cp_dev, cp_host, batch, H, D, S, ws, st);
+}
+
+// Checks of a paged cache's description; fills `pg` and the capacity.
+attn_status_t check_paging(const uint32_t *block_table, const uint32_t *cp_dev, uint32_t batch,
+                           uint32_t H, uint32_t D, uint32_t page_size, uint32_t max_blocks,
+                           uint32_t num_blocks, Paging *pg, uint32_t *capacity) {
+    if (!block_table || !cp_dev)
+        return fail(ATTN_ERR_NULL, "block_table and current_pos must be non-NULL");
+    if (!aligned(block_table, 4)) return fail(ATTN_ERR_ALIGN, "block_table must be 4-byte aligned");
+    if (page_size == 0 || (page_size & (page_size - 1)) || page_size > 65536u)
+        return fail(ATTN_ERR_DIM, "page_size=%u must be a power of two <= 65536", page_size);
+    if (max_blocks == 0 || num_blocks == 0)
+        return fail(ATTN_ERR_DIM, "max_blocks and num_blocks must be nonzero");
+    const uint64_t cap = (uint64_t)max_blocks * page_size;
+    if (cap > (1ull << 31)) return fail(ATTN_ERR_DIM, "max_blocks*page_size exceeds 2^31");
+    const unsigned __int128 pool = (unsigned __int128)num_blocks * page_size * H * D;
+    if (pool > ((unsigned __int128)1 << 60)) return fail(ATTN_ERR_DIM, "page pool too large");
+    if ((uint64_t)batch * max_blocks > (1ull << 40)) return fail(ATTN_ERR_DIM, "block table too large");
+    uint32_t shift = 0;
+    while ((1u << shift) < page_size) ++shift;
+    *pg = Paging{block_table, max_blocks, num_blocks, shift};
+    *capacity = (uint32_t)cap;
+    return ok();
 }
 
 }  // namespace
@@ -1059,7 +1156,7 @@ attn_status_t attn_decode_f16(const uint16_t *q, const uint16_t *k_cache, const 
                               uint32_t current_pos, float *scores_dump, void *workspace,
                               size_t workspace_bytes, void *stream) {
     return decode_full(q, k_cache, v_cache, out, nullptr, current_pos, 1, n_heads, head_dim,
-                       seq_len, scores_dump, workspace, workspace_bytes, stream);
+                       seq_len, scores_dump, workspace, workspace_bytes, nullptr, stream);
 }
 
 attn_status_t attn_decode_f16_batched(const uint16_t *q, const uint16_t *k_cache,
@@ -1070,7 +1167,7 @@ attn_status_t attn_decode_f16_batched(const uint16_t *q, const uint16_t *k_cache
                                       size_t workspace_bytes, void *stream) {
     if (!current_pos) return fail(ATTN_ERR_NULL, "current_pos must be non-NULL");
     return decode_full(q, k_cache, v_cache, out, current_pos, 0, batch, n_heads, head_dim,
-                       capacity, scores_dump, workspace, workspace_bytes, stream);
+                       capacity, scores_dump, workspace, workspace_bytes, nullptr, stream);
 }
 
 attn_status_t attn_decode_f16_split(const uint16_t *q, const uint16_t *k_cache,
@@ -1085,7 +1182,7 @@ attn_status_t attn_decode_f16_split(const uint16_t *q, const uint16_t *k_cache,
     if (s != ATTN_OK) return s;
     bool wrote = false;
     return launch_split(q, k_cache, v_cache, current_pos_dev, current_pos, batch, n_heads,
-                        head_dim, seq_len, scores_dump, workspace, nullptr,
+                        head_dim, seq_len, scores_dump, workspace, nullptr, nullptr,
                         static_cast<hipStream_t>(stream), &wrote);
 }
 
@@ -1103,6 +1200,47 @@ attn_status_t attn_decode_f16_combine(uint16_t *out, const uint32_t *current_pos
     if (s != ATTN_OK) return s;
     return launch_combine(out, current_pos_dev, current_pos, batch, n_heads, head_dim, seq_len,
                           workspace, static_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_decode_f16_paged(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                    uint16_t *out, const uint32_t *block_table,
+                                    const uint32_t *current_pos, uint32_t batch, uint32_t n_heads,
+                                    uint32_t head_dim, uint32_t page_size, uint32_t max_blocks,
+                                    uint32_t num_blocks, float *scores_dump, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    attn_status_t s = check_sizes(batch, n_heads, head_dim, 1);
+    if (s != ATTN_OK) return s;
+    Paging pg;
+    uint32_t cap = 0;
+    s = check_paging(block_table, current_pos, batch, n_heads, head_dim, page_size, max_blocks,
+                     num_blocks, &pg, &cap);
+    if (s != ATTN_OK) return s;
+    return decode_full(q, k_pool, v_pool, out, current_pos, 0, batch, n_heads, head_dim, cap,
+                       scores_dump, workspace, workspace_bytes, &pg, stream);
+}
+
+attn_status_t attn_decode_f16_paged_split(const uint16_t *q, const uint16_t *k_pool,
+                                          const uint16_t *v_pool, const uint32_t *block_table,
+                                          const uint32_t *current_pos, uint32_t batch,
+                                          uint32_t n_heads, uint32_t head_dim, uint32_t page_size,
+                                          uint32_t max_blocks, uint32_t num_blocks,
+                                          float *scores_dump, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+    attn_status_t s = check_sizes(batch, n_heads, head_dim, 1);
+    if (s != ATTN_OK) return s;
+    Paging pg;
+    uint32_t cap = 0;
+    s = check_paging(block_table, current_pos, batch, n_heads, head_dim, page_size, max_blocks,
+                     num_blocks, &pg, &cap);
+    if (s != ATTN_OK) return s;
+    s = check_split(q, k_pool, v_pool, current_pos, batch, n_heads, head_dim, cap, scores_dump);
+    if (s != ATTN_OK) return s;
+    s = check_workspace(workspace, workspace_bytes, batch, n_heads, head_dim, cap);
+    if (s != ATTN_OK) return s;
+    bool wrote = false;
+    return launch_split(q, k_pool, v_pool, current_pos, 0, batch, n_heads, head_dim, cap,
+                        scores_dump, workspace, nullptr, &pg, static_cast<hipStream_t>(stream),
+                        &wrote);
 }
 
 const char *attn_status_string(attn_status_t status) {

@@ -156,6 +156,7 @@ class Workload:
     garbage_sigma: Optional[float] = None   # K/V rows beyond cur_pos
     spike_fraction: float = 0.0             # share of K rows scaled
     spike_scale: float = 8.0
+    page_size: int = 0                      # > 0: the cache lives in a paged pool
 
     @property
     def batched(self) -> bool:
@@ -195,6 +196,31 @@ class Workload:
     def q_shape(self):
         return (self.batch, self.n_heads, self.head_dim)
 
+    @property
+    def paged(self) -> bool:
+        return self.page_size > 0
+
+    @property
+    def max_blocks(self) -> int:
+        return -(-self.seq_len // self.page_size)
+
+    @property
+    def num_blocks(self) -> int:
+        """Pool pages: exactly enough for every sequence's full capacity."""
+        return self.batch * self.max_blocks
+
+    @property
+    def pool_shape(self):
+        return (self.num_blocks, self.page_size, self.n_heads, self.head_dim)
+
+    def block_table(self) -> torch.Tensor:
+        """int64 [batch, max_blocks]: a seeded permutation of all pool pages,
+        so each sequence's pages are scattered through the pool."""
+        n = self.num_blocks
+        w = uniform_u64(self.seed, STREAM_EXTRA, torch.arange(n, dtype=torch.int64) + (1 << 41))
+        order = torch.argsort(torch.bitwise_xor(w, -(1 << 63)), stable=True)
+        return order.view(self.batch, self.max_blocks)
+
     def kv_bytes_read(self) -> int:
         """Algorithmic K+V bytes: rows p <= current_pos of every head."""
         lens = torch.clamp(self.positions(), max=self.seq_len - 1) + 1
@@ -227,6 +253,34 @@ def make_kv(w: Workload, device="cpu"):
     _fill_kv(k, w, STREAM_K, device)
     _fill_kv(v, w, STREAM_V, device)
     return k, v
+
+
+def make_kv_paged(w: Workload, device="cpu"):
+    """K and V page pools [num_blocks, page_size, n_heads, head_dim] fp16;
+    element i of a pool gets value(i) of its stream."""
+    assert w.paged
+    k = torch.empty(w.pool_shape, dtype=torch.float16, device=device)
+    v = torch.empty(w.pool_shape, dtype=torch.float16, device=device)
+    fill_normal_(k, w.seed, STREAM_K, w.sigma_kv)
+    fill_normal_(v, w.seed, STREAM_V, w.sigma_kv)
+    return k, v
+
+
+def head_slice_paged(w: Workload, b: int, h: int, block_table: Optional[torch.Tensor] = None):
+    """Host copies of one (sequence, head) of a paged workload, gathered
+    through the block table into the dense layout: q [1,1,D], k/v [L,1,D]."""
+    H, D, P = w.n_heads, w.head_dim, w.page_size
+    if block_table is None:
+        block_table = w.block_table()
+    L = w.valid_len(b)
+    d = torch.arange(D, dtype=torch.int64)
+    q = normal_f16(w.seed, STREAM_Q, (b * H + h) * D + d, w.sigma_q).view(1, 1, D)
+    p = torch.arange(L, dtype=torch.int64)
+    page = block_table[b, p // P]
+    idx = (((page * P + p % P) * H + h) * D)[:, None] + d[None, :]
+    k = normal_f16(w.seed, STREAM_K, idx, w.sigma_kv).view(L, 1, D)
+    v = normal_f16(w.seed, STREAM_V, idx, w.sigma_kv).view(L, 1, D)
+    return q, k, v
 
 
 def head_slice(w: Workload, b: int, h: int, n_rows: Optional[int] = None):
@@ -271,6 +325,10 @@ WORKLOADS = {
                  seq_len=8192, cur_pos=None, seed=4, batch=64),
         Workload("h64_d64_s131072_spikes", n_heads=64, head_dim=64,
                  seq_len=131072, cur_pos=131071, seed=5, spike_fraction=0.01),
+        # the ragged batch again, its caches cut into 16-position pages
+        # scattered through one pool
+        Workload("b64_h32_d128_cap8192_ragged_paged16", n_heads=32, head_dim=128,
+                 seq_len=8192, cur_pos=None, seed=4, batch=64, page_size=16),
     ]
 }
 

@@ -140,6 +140,46 @@ attn_status_t attn_decode_f16_combine(uint16_t *out, const uint32_t *current_pos
                                       const void *workspace, size_t workspace_bytes,
                                       void *stream);
 
+/*
+ * A batch whose K/V caches live in a paged pool.  The page "Tutorial 16:
+ * Writing Custom Metal Kernels" (section "Performance Impact") names paged
+ * attention that reads pages directly instead of gathering them first; the
+ * page "Developing Apple Metal Kernels in Rust - A Deep Dive Through
+ * Attention" (section "setBuffer_offset_atIndex and unified memory") keeps
+ * tensors as sub-regions of one pool handed out by a paged block allocator.
+ * Each page holds page_size consecutive positions of one sequence in the
+ * dense row layout, and a block table names the pages of each sequence:
+ *   k_pool, v_pool  [num_blocks, page_size, n_heads, head_dim] fp16
+ *   block_table     DEVICE [batch, max_blocks] uint32: position p of sequence
+ *                   b is row p % page_size of page block_table[b][p / page_size].
+ *                   Only entries for positions <= current_pos are read;
+ *                   several sequences may share a page.  An entry >=
+ *                   num_blocks is read as num_blocks - 1 (in bounds, output
+ *                   meaningless).
+ *   current_pos     DEVICE [batch] uint32; capacity = max_blocks * page_size
+ *   page_size       a power of two, 1..65536
+ *   q, out          [batch, n_heads, head_dim] fp16; scores_dump NULL or
+ *                   [batch, n_heads, capacity] fp32
+ *   workspace       >= attn_decode_workspace_bytes(batch, n_heads, head_dim, capacity)
+ * attn_decode_f16_paged_split is its first launch; attn_decode_f16_combine
+ * (with current_pos_dev = current_pos and seq_len = capacity) is the second.
+ */
+attn_status_t attn_decode_f16_paged(const uint16_t *q, const uint16_t *k_pool,
+                                    const uint16_t *v_pool, uint16_t *out,
+                                    const uint32_t *block_table, const uint32_t *current_pos,
+                                    uint32_t batch, uint32_t n_heads, uint32_t head_dim,
+                                    uint32_t page_size, uint32_t max_blocks, uint32_t num_blocks,
+                                    float *scores_dump, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+attn_status_t attn_decode_f16_paged_split(const uint16_t *q, const uint16_t *k_pool,
+                                          const uint16_t *v_pool, const uint32_t *block_table,
+                                          const uint32_t *current_pos, uint32_t batch,
+                                          uint32_t n_heads, uint32_t head_dim, uint32_t page_size,
+                                          uint32_t max_blocks, uint32_t num_blocks,
+                                          float *scores_dump, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(attn_status_t status);
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -113,3 +113,42 @@ def test_binding_rejects_cpu_tensors():
         ad.decode(q, k, k, 100)
     with pytest.raises(TypeError):
         ad.decode(q, k.float(), k, 100)
+
+
+def test_paged_rejects_bad_arguments(lib):
+    f = lib.attn_decode_f16_paged
+    ok_args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, bt=FAKE, cp=FAKE, B=2, H=4, D=64, P=16,
+                   MB=8, NB=16, dump=None, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return f(a["q"], a["k"], a["v"], a["out"], a["bt"], a["cp"], a["B"], a["H"], a["D"],
+                 a["P"], a["MB"], a["NB"], a["dump"], a["ws"], a["wsb"], None)
+
+    assert call(bt=None) == NULL
+    assert call(cp=None) == NULL
+    assert call(bt=FAKE + 2) == ALIGN
+    assert call(P=12) == DIM
+    assert call(P=0) == DIM
+    assert call(MB=0) == DIM
+    assert call(NB=0) == DIM
+    assert call(P=65536, MB=1 << 16) == DIM        # capacity 2^32
+    assert call(wsb=16) == WS
+    assert call(D=300) == DIM
+
+
+def test_paged_generator_gathers_the_pool():
+    from decode_attention_kv_seq_amd import workloads as wl
+    import torch
+    w = wl.Workload("t", n_heads=3, head_dim=8, seq_len=64, cur_pos=None, seed=9, batch=4,
+                    page_size=8)
+    kp, vp = wl.make_kv_paged(w)
+    bt = w.block_table()
+    assert sorted(bt.view(-1).tolist()) == list(range(w.num_blocks))
+    for b in range(4):
+        for h in range(3):
+            _, k, v = wl.head_slice_paged(w, b, h)
+            L = w.valid_len(b)
+            dk = torch.stack([kp[bt[b, p // 8], p % 8, h] for p in range(L)])
+            dv = torch.stack([vp[bt[b, p // 8], p % 8, h] for p in range(L)])
+            assert torch.equal(dk, k.view(L, 8)) and torch.equal(dv, v.view(L, 8))

@@ -467,3 +467,105 @@ def test_batched_more_sequences_than_balanced_grid_handles():
     torch.cuda.synchronize()
     ref, _ = oracle.decode_batched(q, k, v, pos)
     assert_close(out, ref, "1100 sequences")
+
+
+# ------------------------------------------------------------ paged cache
+
+
+def page_dense_cache(k, v, page_size, rng, extra_pages=3):
+    """Scatter dense [B, S, H, D] caches into a shuffled page pool.
+    Returns k_pool, v_pool [NB, P, H, D] and the block table [B, S/P] (int32)."""
+    B, S, H, D = k.shape
+    mb = S // page_size
+    nb = B * mb + extra_pages
+    perm = rng.permutation(nb)[: B * mb].reshape(B, mb)
+    kp = np.zeros((nb, page_size, H, D), np.float16)
+    vp = np.zeros((nb, page_size, H, D), np.float16)
+    for b in range(B):
+        for j in range(mb):
+            kp[perm[b, j]] = k[b, j * page_size:(j + 1) * page_size]
+            vp[perm[b, j]] = v[b, j * page_size:(j + 1) * page_size]
+    return kp, vp, perm.astype(np.int32)
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 16, 64, 512, 2048])
+def test_paged_equals_dense_batched(page_size):
+    """The same caches, dense or cut into shuffled pages: identical bits, and
+    both match the oracle."""
+    rng = np.random.default_rng(40 + page_size)
+    B, S, H, D = 5, 2048, 8, 128
+    q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = np.array([2047, 0, 1000, 15, 1536], dtype=np.int64)
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    dense = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    kp, vp, bt = page_dense_cache(k, v, page_size, rng)
+    paged, dump = ad.decode_paged(to_dev(q), to_dev(kp), to_dev(vp), to_dev(bt), cp, dump=True)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.decode_batched(q, k, v, pos, want_scores=True)
+    assert_close(paged, ref, "page %d" % page_size)
+    assert torch.equal(paged, dense)
+    for b in range(B):
+        assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "page %d b=%d" % (page_size, b))
+
+
+def test_paged_workload_sampled():
+    """64 ragged sequences in 16-position pages scattered through one pool:
+    16 sampled (sequence, head) pairs against the oracle."""
+    w = wl.WORKLOADS["b64_h32_d128_cap8192_ragged_paged16"]
+    q = wl.make_q(w, DEV)
+    kp, vp = wl.make_kv_paged(w, DEV)
+    bt_h = w.block_table()
+    bt = bt_h.to(torch.int32).to(DEV)
+    pos = w.positions()
+    cp = pos.to(torch.int32).to(DEV)
+    out = ad.decode_paged(q, kp, vp, bt, cp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    picks = [(int(b), int(rng.integers(0, w.n_heads))) for b in rng.choice(w.batch, 16, replace=False)]
+    picks[0] = (int(torch.argmax(pos)), 5)
+    for b, h in picks:
+        qs, ks, vs = wl.head_slice_paged(w, b, h, bt_h)
+        ref, _, _ = oracle.decode(qs[0], ks, vs, int(pos[b]))
+        assert_close(out[b, h:h + 1], ref, "b=%d h=%d" % (b, h))
+
+
+def test_paged_shared_pages_and_unused_table_entries():
+    """Two sequences share their first pages (a common prefix); table entries
+    past each sequence's last position hold 0xFFFFFFFF and are never used."""
+    rng = np.random.default_rng(43)
+    P, H, D, mb = 16, 4, 64, 64
+    q = randn16(rng, (3, H, D))
+    prefix_k, prefix_v = randn16(rng, (10 * P, H, D)), randn16(rng, (10 * P, H, D))
+    k = randn16(rng, (3, mb * P, H, D))
+    v = randn16(rng, (3, mb * P, H, D))
+    k[0, :10 * P], v[0, :10 * P] = prefix_k, prefix_v
+    k[1, :10 * P], v[1, :10 * P] = prefix_k, prefix_v
+    kp, vp, bt = page_dense_cache(k, v, P, rng)
+    bt[1, :10] = bt[0, :10]          # sequence 1 reads sequence 0's prefix pages
+    pos = np.array([300, 10 * P + 40, 17], dtype=np.int64)
+    for b in range(3):
+        bt[b, pos[b] // P + 1:] = -1     # 0xFFFFFFFF as uint32
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    out = ad.decode_paged(to_dev(q), to_dev(kp), to_dev(vp), to_dev(bt), cp)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_batched(q, k, v, pos)
+    assert_close(out, ref, "shared pages")
+
+
+def test_paged_split_then_combine_and_many_sequences():
+    rng = np.random.default_rng(44)
+    B, S, H, D, P = 1030, 32, 2, 64, 8   # past the balanced grid's batch limit
+    q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, 40, B)
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    kp, vp, bt = page_dense_cache(k, v, P, rng)
+    qd, kpd, vpd, btd = to_dev(q), to_dev(kp), to_dev(vp), to_dev(bt)
+    one = ad.decode_paged(qd, kpd, vpd, btd, cp)
+    ws = ad.alloc_workspace(B, H, D, S, DEV)
+    two = torch.empty_like(one)
+    ad.split_paged(qd, kpd, vpd, btd, cp, ws)
+    ad.combine(two, cp, B, H, D, S, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    ref, _ = oracle.decode_batched(q, k, v, pos)
+    assert_close(one, ref, "1030 paged sequences")
