@@ -52,6 +52,8 @@ class OracleLib:
         lib.oracle_attn_decode.argtypes = [u16p, u16p, u16p, u32, u32, u32, u32, u32, u32,
                                            f64p, f64p, f64p]
         lib.oracle_attn_decode.restype = ctypes.c_int
+        lib.oracle_attn_pv_from_scores.argtypes = [u16p, u16p, u32, u32, u32, u32, u32, u32, f64p]
+        lib.oracle_attn_pv_from_scores.restype = ctypes.c_int
         self.path = path
         self.lib = lib
 
@@ -103,6 +105,21 @@ class OracleLib:
                 list(ex.map(run, bounds))
         return out, scores, weights
 
+    def pv_from_scores(self, scores, v, current_pos: int):
+        """Second kernel of the page's two-dispatch form: scores [H, S] fp16
+        bits, v [S, H, D] -> out [H, D] float64."""
+        S, H, D = tuple(v.shape)
+        if tuple(scores.shape) != (H, S):
+            raise ValueError("scores must be [n_heads, seq_len]")
+        sb, vb = _bits(scores), _bits(v)
+        out = np.zeros((H, D), dtype=np.float64)
+        rc = self.lib.oracle_attn_pv_from_scores(_ptr(sb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
+                                                 H, D, S, min(int(current_pos), 0xFFFFFFFF), 0, H,
+                                                 _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise RuntimeError("oracle_attn_pv_from_scores failed")
+        return out
+
     def decode_batched(self, q, k, v, current_pos, *, want_scores=False, threads: int = 1):
         """Independent sequences: q [B, H, D], k/v [B, S, H, D], current_pos [B].
 
@@ -142,3 +159,7 @@ def decode(q, k, v, current_pos, **kw):
 
 def decode_batched(q, k, v, current_pos, **kw):
     return load().decode_batched(q, k, v, current_pos, **kw)
+
+
+def pv_from_scores(scores, v, current_pos):
+    return load().pv_from_scores(scores, v, current_pos)

@@ -134,3 +134,56 @@ int oracle_attn_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(e);
     return 0;
 }
+
+/*
+ * The second kernel of the page's two-dispatch form (attention_pv_f16,
+ * section "The MSL, briefly") on its own: softmax of a stored fp16 score row
+ * (global max subtracted, shifted exponentials summed, each weight divided
+ * by the sum) and the weighted sum of V.  Scores are read as IEEE binary16
+ * bits; a score of -inf has weight exactly 0.  Positions after current_pos
+ * are skipped, as in oracle_attn_decode.
+ *   scores [n_heads, seq_len] binary16 bits; v [seq_len, n_heads, head_dim];
+ *   out [n_heads, head_dim] for heads head_lo..head_hi-1.
+ * Returns 0, or -1 on a bad argument, allocation failure or a head whose
+ * scores are all -inf.
+ */
+int oracle_attn_pv_from_scores(const uint16_t *scores, const uint16_t *v, uint32_t n_heads,
+                               uint32_t head_dim, uint32_t seq_len, uint32_t current_pos,
+                               uint32_t head_lo, uint32_t head_hi, double *out)
+{
+    if (!scores || !v || !out || n_heads == 0 || head_dim == 0 || seq_len == 0 ||
+        head_lo > head_hi || head_hi > n_heads)
+        return -1;
+    const size_t H = n_heads, D = head_dim, S = seq_len;
+    const size_t L = (current_pos < seq_len - 1 ? (size_t)current_pos : S - 1) + 1;
+    double *e = (double *)malloc(L * sizeof(double));
+    if (!e)
+        return -1;
+    int rc = 0;
+    for (size_t h = head_lo; h < head_hi && rc == 0; ++h) {
+        double m = -INFINITY;
+        for (size_t p = 0; p < L; ++p) {
+            const double s = oracle_half_to_double(scores[h * S + p]);
+            if (s > m)
+                m = s;
+        }
+        if (m == -INFINITY) {
+            rc = -1;
+            break;
+        }
+        double z = 0.0;
+        for (size_t p = 0; p < L; ++p) {
+            e[p] = exp(oracle_half_to_double(scores[h * S + p]) - m);
+            z += e[p];
+        }
+        for (size_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (size_t p = 0; p < L; ++p)
+                if (e[p] != 0.0)
+                    acc += (e[p] / z) * oracle_half_to_double(v[(p * H + h) * D + d]);
+            out[h * D + d] = acc;
+        }
+    }
+    free(e);
+    return rc;
+}

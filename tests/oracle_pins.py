@@ -332,6 +332,66 @@ def pin_heads_are_independent(orc):
     assert not np.array_equal(out[2], base[2])
 
 
+# ---------------------------------------------------------------- second dispatch
+
+
+def pin_pv_equals_decode_on_representable_scores(orc):
+    """With q one-hot and K on a 1/16 grid (D = 64), every score k/8 is an
+    fp16 value exactly, so softmax.V from the stored fp16 scores must equal
+    the one-pass oracle bit for bit."""
+    rng = _rng(20)
+    S, H, D, cp = 57, 3, 64, 44
+    q = np.zeros((H, D), np.float16)
+    for h, i in enumerate([3, 30, 63]):
+        q[h, i] = 1.0
+    k = (rng.integers(-64, 65, (S, H, D)) / 16.0).astype(np.float16)
+    v = _randn_f16(rng, (S, H, D))
+    out, s, _ = orc.decode(q, k, v, cp, want_scores=True)
+    s16 = s.astype(np.float16)
+    assert np.array_equal(s16[:, : cp + 1].astype(np.float64), s[:, : cp + 1])
+    assert np.array_equal(orc.pv_from_scores(s16, v, cp), out)
+
+
+def pin_pv_two_positions_closed_form(orc):
+    for a, b in [(0.5, 2.0), (-3.0, 1.25), (7.0, 7.0)]:
+        sc = np.array([[a, b]], np.float16)
+        v = np.zeros((2, 1, 3), np.float16)
+        v[0, 0] = [1, -2, 0.5]
+        v[1, 0] = [4, 0.25, -1]
+        out = orc.pv_from_scores(sc, v, 1)
+        w0 = 1.0 / (1.0 + math.exp(b - a))
+        ref = w0 * v[0, 0].astype(np.float64) + (1 - w0) * v[1, 0].astype(np.float64)
+        assert np.allclose(out[0], ref, rtol=0, atol=1e-15)
+
+
+def pin_pv_neg_inf_scores_have_zero_weight(orc):
+    """-inf scores inside the valid range weigh nothing, whatever V holds there."""
+    rng = _rng(21)
+    S, H, D, cp = 20, 2, 8, 15
+    sc = _randn_f16(rng, (H, S), 2.0)
+    v = _randn_f16(rng, (S, H, D))
+    drop = [2, 9, 15]
+    sc2, v2 = sc.copy(), v.copy()
+    sc2[:, drop] = -np.inf
+    v2[drop] = np.nan
+    keep = [p for p in range(cp + 1) if p not in drop]
+    ref = orc.pv_from_scores(sc[:, keep].copy(), v[keep].copy(), len(keep) - 1)
+    out = orc.pv_from_scores(sc2, v2, cp)
+    assert np.array_equal(out, ref)
+
+
+def pin_pv_direct_formula(orc):
+    rng = _rng(22)
+    for (S, H, D, cp) in [(9, 2, 16, 8), (40, 3, 48, 31), (100, 1, 128, 99)]:
+        sc = _randn_f16(rng, (H, S), 1.5)
+        v = _randn_f16(rng, (S, H, D))
+        out = orc.pv_from_scores(sc, v, cp)
+        e = np.exp(sc[:, : cp + 1].astype(np.float64))
+        w = e / e.sum(axis=1, keepdims=True)
+        ref = np.einsum("hp,phd->hd", w, v[: cp + 1].astype(np.float64))
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-13), (S, H, D)
+
+
 ALL_PINS = [
     pin_half_decoder_all_patterns,
     pin_one_hot_query_scores,
@@ -350,4 +410,8 @@ ALL_PINS = [
     pin_position_permutation_invariance,
     pin_linear_in_values,
     pin_heads_are_independent,
+    pin_pv_equals_decode_on_representable_scores,
+    pin_pv_two_positions_closed_form,
+    pin_pv_neg_inf_scores_have_zero_weight,
+    pin_pv_direct_formula,
 ]

@@ -29,6 +29,9 @@ MUTANTS = {
     "decoder_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
     "decoder_implicit_bit_dropped": ("(1024 + frac)", "(frac)"),
     "masked_score_zero": ("p < L ? s[p] : -INFINITY", "p < L ? s[p] : 0.0"),
+    "pv_scores_transposed": ("oracle_half_to_double(scores[h * S + p])", "oracle_half_to_double(scores[p * H + h])"),
+    "pv_max_is_min": ("            if (s > m)\n", "            if (s < m || m == -INFINITY)\n"),
+    "pv_neg_inf_not_skipped": ("                if (e[p] != 0.0)\n", ""),
 }
 
 
