@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
+    p.add_argument("--path", choices=["fused", "two_dispatch"], default="fused",
+                   help="two_dispatch: fp16 score row written then read back "
+                        "(attn_qk_f16 + attn_pv_f16), single-sequence workloads only")
     return p.parse_args()
 
 
@@ -204,6 +207,21 @@ def main():
                     cp_host, B, H, D, S, vp(ws.data_ptr()), ws_bytes, sh)
     full = (lib.attn_decode_f16_paged if w.paged else
             lib.attn_decode_f16_batched if w.batched else lib.attn_decode_f16)
+    if args.path == "two_dispatch":
+        if w.batched:
+            raise SystemExit("--path two_dispatch needs a single-sequence workload")
+        scores = torch.empty((H, S), dtype=torch.float16, device=dev)
+        qk_args = [(vp(q.data_ptr()), vp(ks[r].data_ptr()), vp(scores.data_ptr()), H, D, S,
+                    cp_host, sh) for r in range(copies)]
+        pv_args = [(vp(scores.data_ptr()), vp(vs[r].data_ptr()), vp(out.data_ptr()), H, D, S,
+                    cp_host, vp(ws.data_ptr()), ws_bytes, sh) for r in range(copies)]
+
+        def two_dispatch(r):
+            rc = lib.attn_qk_f16(*qk_args[r])
+            return rc if rc else lib.attn_pv_f16(*pv_args[r])
+        step_fns = [lambda r=r: two_dispatch(r) for r in range(copies)]
+    else:
+        step_fns = [lambda fa=fa: full(*fa) for fa in full_args]
     split = lib.attn_decode_f16_paged_split if w.paged else lib.attn_decode_f16_split
 
     def check(rc):
@@ -220,18 +238,18 @@ def main():
 
     # ---- whole steps
     for i in range(args.warmup):
-        check(full(*full_args[i % copies]))
+        check(step_fns[i % copies]())
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        check(full(*full_args[i % copies]))
+        check(step_fns[i % copies]())
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
     # ---- the split kernel alone, inside otherwise unchanged steps
-    n_split = max(20, min(args.steps, 500))
+    n_split = max(20, min(args.steps, 500)) if args.path == "fused" else 0
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_split)]
     for i in range(n_split):
@@ -240,7 +258,7 @@ def main():
         evs[i][1].record(stream)
         check(lib.attn_decode_f16_combine(*combine_args))
     torch.cuda.synchronize()
-    split_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    split_ms = sorted(a.elapsed_time(b) for a, b in evs) or [ms]
     split_avg = sum(split_ms) / len(split_ms)
 
     value = nbytes / (ms * 1e-3) / 1e9
@@ -274,6 +292,7 @@ def main():
         "us_per_step": round(ms * 1e3, 3),
         "split_kernel_us": round(split_avg * 1e3, 3),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "path": args.path,
     }
     line = {
         "metric": METRIC,

@@ -65,6 +65,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_f16_paged_split.argtypes = [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32,
                                                 vp, vp, sz, vp]
     lib.attn_decode_f16_paged_split.restype = ctypes.c_int
+    lib.attn_qk_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, vp]
+    lib.attn_qk_f16.restype = ctypes.c_int
+    lib.attn_pv_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, vp, sz, vp]
+    lib.attn_pv_f16.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -273,3 +277,43 @@ def split_paged(q, k_pool, v_pool, block_table, current_pos, workspace, *, dump=
                                            _ptr(workspace),
                                            workspace.numel() * workspace.element_size(),
                                            _stream_handle(stream)))
+
+
+def qk(q, k, current_pos: int, *, scores=None, stream=None):
+    """First dispatch: q [H, D], k [S, H, D] -> fp16 scores [H, S]
+    (scaled, -inf after current_pos)."""
+    lib = load_library()
+    _req(k, "k", torch.float16)
+    dev = k.device
+    _req(q, "q", torch.float16, dev)
+    S, H, D = k.shape
+    if tuple(q.shape) != (H, D):
+        raise ValueError("q must be [n_heads, head_dim]")
+    if scores is None:
+        scores = torch.empty((H, S), dtype=torch.float16, device=dev)
+    _req(scores, "scores", torch.float16, dev)
+    if tuple(scores.shape) != (H, S):
+        raise ValueError("scores must be [n_heads, seq_len]")
+    _check(lib.attn_qk_f16(_ptr(q), _ptr(k), _ptr(scores), H, D, S, int(current_pos),
+                           _stream_handle(stream)))
+    return scores
+
+
+def pv(scores, v, current_pos: int, *, out=None, workspace=None, stream=None):
+    """Second dispatch: fp16 scores [H, S], v [S, H, D] -> out [H, D]."""
+    lib = load_library()
+    _req(v, "v", torch.float16)
+    dev = v.device
+    _req(scores, "scores", torch.float16, dev)
+    S, H, D = v.shape
+    if tuple(scores.shape) != (H, S):
+        raise ValueError("scores must be [n_heads, seq_len]")
+    if out is None:
+        out = torch.empty((H, D), dtype=torch.float16, device=dev)
+    _req(out, "out", torch.float16, dev)
+    if workspace is None:
+        workspace = alloc_workspace(1, H, D, S, dev)
+    _check(lib.attn_pv_f16(_ptr(scores), _ptr(v), _ptr(out), H, D, S, int(current_pos),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream_handle(stream)))
+    return out

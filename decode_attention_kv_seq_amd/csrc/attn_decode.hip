@@ -160,6 +160,8 @@ struct SplitArgs {
     uint32_t batch;           // sequences (balanced grid)
     uint32_t grid;            // workgroups launched (balanced grid)
     uint32_t *header;         // workspace header: how the partials are laid out
+    const uint16_t *scores_in;    // second dispatch: stored fp16 scores [B, H, S]
+    uint16_t *scores_out;         // first dispatch: fp16 scores [H, S]
     const uint32_t *block_table;  // paged cache: [batch, max_blocks] page ids, or null
     uint32_t max_blocks;      // block-table row length
     uint32_t num_blocks;      // pages in the pool
@@ -196,7 +198,7 @@ struct PieceDst {
 // Stream positions [c0, c_end) of head block hb of sequence b through the
 // online softmax and leave one merged state per head at `dst`.  The caller
 // guarantees c0 < c_end.  LDS is free again when this returns.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC>
 __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint32_t hb,
                                             uint32_t c0, uint32_t c_end, const PieceDst &dst,
                                             float *sm_o, float *sm_m, float *sm_l) {
@@ -225,10 +227,14 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     }
 
     Pack<VEC> qp[NV];
-    const uint16_t *qrow = a.q + ((size_t)b * a.H + h) * D;
+    if constexpr (!SC) {
+        const uint16_t *qrow = a.q + ((size_t)b * a.H + h) * D;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        qp[j] = eok[j] ? load_pack<VEC>(qrow + eoff[j]) : zero_pack<VEC>();
+        for (int j = 0; j < NV; ++j)
+            qp[j] = eok[j] ? load_pack<VEC>(qrow + eoff[j]) : zero_pack<VEC>();
+    }
+    // stored scores (second dispatch of the two-launch form): row (b, h) of [B, H, S]
+    const uint16_t *srow = SC ? a.scores_in + ((size_t)b * a.H + h) * a.S : nullptr;
 
     // dense: sequence b's rows start at b*S*H*D; paged: rows live in pool
     // pages [num_blocks, page, H, D] named by the sequence's block-table row
@@ -250,6 +256,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     // the chunk's first row (always valid) and get weight 0.
     struct Block {
         Pack<VEC> k[U][NV], v[U][NV];
+        uint16_t sc[U];   // stored scores (SC)
     };
     // Page ids of a block's positions (paged caches).  They are fetched one
     // block ahead of the K/V loads that need them, and before the K/V loads of
@@ -278,9 +285,11 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
             } else {
                 row = row_of(pc);
             }
+            if constexpr (SC) blk.sc[u] = srow[pc];
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                blk.k[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
+                if constexpr (!SC)
+                    blk.k[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
                 blk.v[u][j] = eok[j] ? load_pack<VEC>(vbase + row + eoff[j]) : zero_pack<VEC>();
             }
         }
@@ -292,10 +301,15 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         for (int u = 0; u < U; ++u) {
             const uint32_t p = base + u * pps + pg;
             float dot = 0.f;
+            if constexpr (SC) {
+                // natural-log score from the buffer, in base-2 units
+                t[u] = p < c_end ? h2f(blk.sc[u]) * 1.4426950408889634f : -INFINITY;
+            } else {
 #pragma unroll
-            for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], blk.k[u][j], dot);
-            dot = group_sum<GL>(dot);
-            t[u] = p < c_end ? dot * a.scale_log2 : -INFINITY;
+                for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], blk.k[u][j], dot);
+                dot = group_sum<GL>(dot);
+                t[u] = p < c_end ? dot * a.scale_log2 : -INFINITY;
+            }
             tmax = fmaxf(tmax, t[u]);
             if constexpr (DUMP) {
                 if (p < c_end && gl == 0) a.dump[((size_t)b * a.H + h) * a.S + p] = dot * a.scale;
@@ -313,11 +327,13 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         for (int u = 0; u < U; ++u) {
             const float pw = __builtin_amdgcn_exp2f(t[u] - m_use);   // 0 for masked slots
             l += pw;
+            // a stored -inf score weighs nothing, whatever V holds at that row
+            const bool live = !SC || t[u] != -INFINITY;
 #pragma unroll
             for (int j = 0; j < NV; ++j)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    acc[j][e] = fmaf(pw, pack_elem<VEC>(blk.v[u][j], e), acc[j][e]);
+                    acc[j][e] = fmaf(pw, live ? pack_elem<VEC>(blk.v[u][j], e) : 0.f, acc[j][e]);
         }
         m = m_new;
     };
@@ -414,7 +430,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 // Chunked grid: workgroup (hb + n_hb*chunk, b) takes positions
 // [chunk*C, (chunk+1)*C) of head block hb.  Partials: o [B, H, nc_stride, D],
 // (m, l) [B, H, nc_stride, 2].
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     write_header(a, 0);
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     dst.pml = a.part_ml + (bh0 * a.nc_stride + chunk) * 2;
     dst.pml_hs = (size_t)a.nc_stride * 2;
     dst.out = a.direct ? a.out + bh0 * a.D : nullptr;
-    split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+    split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
 }
 
 // Inclusive prefix of the valid lengths: pref[0] = 0, pref[b+1] = sum of
@@ -483,7 +499,7 @@ __device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t
 // `grid` equal ranges, one per workgroup.  A workgroup writes one partial per
 // segment piece it covers, at slot w + s; o [slots, hpb, D], (m, l)
 // [slots, hpb, 2] with slots = grid + batch*n_hb.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC>
 __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     write_header(a, 1);
@@ -520,8 +536,75 @@ __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs
         dst.pml = a.part_ml + slot * a.hpb * 2;
         dst.pml_hs = 2;
         dst.out = nullptr;
-        split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+        split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
         x = x_end;
+    }
+}
+
+// ------------------------------------------------ first dispatch (scores)
+// The page's attention_qk_f16 as its own launch: the scaled score of every
+// position, rounded to fp16, -inf after current_pos (positions there are not
+// read).  Same lane layout as the split kernel; workgroup (hb + n_hb*chunk)
+// covers chunk*C .. (chunk+1)*C-1 of head block hb, over the whole cache.
+template <int VEC, int GL, int NV, bool FULL>
+__global__ __launch_bounds__(kThreads) void attn_qk_kernel(SplitArgs a) {
+    constexpr int RG = 64 / GL;
+    constexpr int NG = kWaves * RG;
+    constexpr int U = 4;
+    const uint32_t hb = blockIdx.x % a.n_hb;
+    const uint32_t chunk = blockIdx.x / a.n_hb;
+    const uint32_t L = valid_len(a.cp_host, a.S);
+    const uint32_t c0 = chunk * a.chunk;
+    const uint32_t c_end = min(c0 + a.chunk, a.S);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int g = (tid >> 6) * RG + lane / GL;
+    const int gl = lane % GL;
+    const uint32_t hg = (uint32_t)g % a.hpb;
+    const uint32_t pg = (uint32_t)g / a.hpb;
+    const uint32_t pps = NG / a.hpb;
+    const uint32_t h = hb * a.hpb + hg;
+    const size_t D = a.D;
+    const size_t HD = (size_t)a.H * D;
+    uint16_t *srow = a.scores_out + (size_t)h * a.S;
+    constexpr uint16_t kNegInfHalf = 0xFC00;
+    if (c0 >= L) {   // every position of this chunk is masked
+        for (uint32_t p = c0 + pg; p < c_end; p += pps)
+            if (gl == 0) srow[p] = kNegInfHalf;
+        return;
+    }
+    int eoff[NV];
+    bool eok[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        eoff[j] = (gl + GL * j) * VEC;
+        eok[j] = FULL || eoff[j] < (int)a.D;
+    }
+    Pack<VEC> qp[NV];
+    const uint16_t *qrow = a.q + (size_t)h * D;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        qp[j] = eok[j] ? load_pack<VEC>(qrow + eoff[j]) : zero_pack<VEC>();
+    const uint16_t *kbase = a.k + (size_t)h * D;
+    for (uint32_t base = c0; base < c_end; base += pps * U) {
+        Pack<VEC> kr[U][NV];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t p = base + u * pps + pg;
+            const size_t row = (size_t)(p < L ? p : L - 1) * HD;   // masked slots reread a valid row
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                kr[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t p = base + u * pps + pg;
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], kr[u][j], dot);
+            dot = group_sum<GL>(dot);
+            if (gl == 0 && p < c_end) srow[p] = p < L ? f2h_rne(dot * a.scale) : kNegInfHalf;
+        }
     }
 }
 
@@ -923,8 +1006,8 @@ using SplitFn = void (*)(SplitArgs);
 
 template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED>
 SplitFn kernel_for(bool bal) {
-    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED>
-               : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED>;
+    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, false>
+               : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, false>;
 }
 
 // Dense caches honour the unroll/prefetch knobs on the fast layouts; paged
@@ -976,6 +1059,33 @@ SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     return nullptr;
 }
 
+#define ATTN_ALL_LAYOUTS(X)                                                              \
+    X(8, 8, 1, true) X(8, 16, 1, true) X(8, 32, 1, true) X(8, 8, 1, false) X(8, 16, 1, false) \
+    X(8, 32, 1, false) X(4, 8, 1, false) X(4, 16, 1, false) X(4, 32, 1, false)            \
+    X(4, 64, 1, false) X(2, 8, 1, false) X(2, 16, 1, false) X(2, 32, 1, false)            \
+    X(2, 64, 1, false) X(2, 64, 2, false) X(1, 8, 1, false) X(1, 16, 1, false)            \
+    X(1, 32, 1, false) X(1, 64, 1, false) X(1, 64, 2, false) X(1, 64, 3, false)           \
+    X(1, 64, 4, false)
+
+// Second dispatch (softmax.V from stored scores): chunked grid, U=4, double-buffered.
+SplitFn pick_scores_split(const Layout &ly) {
+#define ATTN_SC(V, G, N, F)                                                            \
+    if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
+        return attn_split_kernel<V, G, N, F, 4, true, false, false, true>;
+    ATTN_ALL_LAYOUTS(ATTN_SC)
+#undef ATTN_SC
+    return nullptr;
+}
+
+using QkFn = void (*)(SplitArgs);
+QkFn pick_qk(const Layout &ly) {
+#define ATTN_QK(V, G, N, F)                                                            \
+    if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F) return attn_qk_kernel<V, G, N, F>;
+    ATTN_ALL_LAYOUTS(ATTN_QK)
+#undef ATTN_QK
+    return nullptr;
+}
+
 attn_status_t hip_check(const char *what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -1019,15 +1129,17 @@ struct Paging {
 attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
                            uint32_t D, uint32_t S, float *dump, void *ws, uint16_t *out,
-                           const Paging *pg, hipStream_t stream, bool *wrote_out) {
-    const Layout ly = choose_layout(D, q, k, v);
+                           const Paging *pg, hipStream_t stream, bool *wrote_out,
+                           const uint16_t *scores_in = nullptr) {
+    const Layout ly = scores_in ? choose_layout(D, v, v, v) : choose_layout(D, q, k, v);
     const Kind kind = pg ? Kind::paged : cp_dev ? Kind::batched : Kind::single;
     const Knobs kn = knobs(D, kind);
     const uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
-    const bool bal = kn.bal && batch <= kBalancedMaxBatch &&
+    const bool bal = !scores_in && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
-    const SplitFn fn = pg ? (dump ? pick_split<true, true>(ly, kn, bal) : pick_split<false, true>(ly, kn, bal))
+    const SplitFn fn = scores_in ? pick_scores_split(ly)
+                     : pg ? (dump ? pick_split<true, true>(ly, kn, bal) : pick_split<false, true>(ly, kn, bal))
                           : (dump ? pick_split<true, false>(ly, kn, bal) : pick_split<false, false>(ly, kn, bal));
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
     // host current_pos: plan the exact span; device array: plan the capacity
@@ -1058,6 +1170,8 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.dump = dump;
     a.batch = batch;
     a.grid = bal ? kn.wgs : 0;
+    a.scores_in = scores_in;
+    a.scores_out = nullptr;
     a.block_table = pg ? pg->block_table : nullptr;
     a.max_blocks = pg ? pg->max_blocks : 0;
     a.num_blocks = pg ? pg->num_blocks : 0;
@@ -1241,6 +1355,57 @@ attn_status_t attn_decode_f16_paged_split(const uint16_t *q, const uint16_t *k_p
     return launch_split(q, k_pool, v_pool, current_pos, 0, batch, n_heads, head_dim, cap,
                         scores_dump, workspace, nullptr, &pg, static_cast<hipStream_t>(stream),
                         &wrote);
+}
+
+attn_status_t attn_qk_f16(const uint16_t *q, const uint16_t *k_cache, uint16_t *scores,
+                          uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                          uint32_t current_pos, void *stream) {
+    if (!q || !k_cache || !scores) return fail(ATTN_ERR_NULL, "q, k_cache and scores must be non-NULL");
+    attn_status_t s = check_sizes(1, n_heads, head_dim, seq_len);
+    if (s != ATTN_OK) return s;
+    if (!aligned(q, 2) || !aligned(k_cache, 2) || !aligned(scores, 2))
+        return fail(ATTN_ERR_ALIGN, "fp16 tensors must be 2-byte aligned");
+    const Layout ly = choose_layout(head_dim, q, k_cache, k_cache);
+    const QkFn fn = pick_qk(ly);
+    if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", head_dim);
+    const Knobs kn = knobs(head_dim, Kind::single);
+    const uint32_t hpb = heads_per_wg(n_heads, ly, kn.hpb);
+    const Plan plan = make_plan(1, n_heads, head_dim, seq_len, seq_len, Kind::single);
+    SplitArgs a = {};
+    a.q = q;
+    a.k = k_cache;
+    a.cp_host = current_pos;
+    a.H = n_heads;
+    a.D = head_dim;
+    a.S = seq_len;
+    a.chunk = plan.chunk;
+    a.n_hb = n_heads / hpb;
+    a.hpb = hpb;
+    a.scale = (float)(1.0 / sqrt((double)head_dim));
+    a.scores_out = scores;
+    hipLaunchKernelGGL(fn, dim3(a.n_hb * plan.n_chunks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
+    return hip_check("score kernel launch");
+}
+
+attn_status_t attn_pv_f16(const uint16_t *scores, const uint16_t *v_cache, uint16_t *out,
+                          uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                          uint32_t current_pos, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    if (!scores || !v_cache || !out)
+        return fail(ATTN_ERR_NULL, "scores, v_cache and out must be non-NULL");
+    attn_status_t s = check_sizes(1, n_heads, head_dim, seq_len);
+    if (s != ATTN_OK) return s;
+    if (!aligned(scores, 2) || !aligned(v_cache, 2) || !aligned(out, 2))
+        return fail(ATTN_ERR_ALIGN, "fp16 tensors must be 2-byte aligned");
+    s = check_workspace(workspace, workspace_bytes, 1, n_heads, head_dim, seq_len);
+    if (s != ATTN_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool wrote = false;
+    s = launch_split(nullptr, nullptr, v_cache, nullptr, current_pos, 1, n_heads, head_dim,
+                     seq_len, nullptr, workspace, out, nullptr, st, &wrote, scores);
+    if (s != ATTN_OK || wrote) return s;
+    return launch_combine(out, nullptr, current_pos, 1, n_heads, head_dim, seq_len, workspace, st);
 }
 
 const char *attn_status_string(attn_status_t status) {

@@ -180,6 +180,35 @@ attn_status_t attn_decode_f16_paged_split(const uint16_t *q, const uint16_t *k_p
                                           float *scores_dump, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/*
+ * The page's own two-dispatch form (section "The MSL, briefly": kernels
+ * attention_qk_f16 then attention_pv_f16), for callers that need the score
+ * row itself.  One sequence.
+ *
+ * attn_qk_f16 writes, for every head h and position p < seq_len, the scaled
+ * score (sum_i q[h,i] k[p,h,i]) / sqrt(head_dim) accumulated in fp32 and
+ * rounded to fp16 (nearest even), or -inf for p > current_pos; masked
+ * positions are not read.
+ *   scores  [n_heads, seq_len] fp16, written
+ *
+ * attn_pv_f16 takes such a score row (from attn_qk_f16 or any other source):
+ * softmax over positions 0..current_pos, then the weighted sum of V.  Unlike
+ * the page's kernel, which weighs every position of the row, positions after
+ * current_pos are not read at all, and a stored score of -inf weighs exactly
+ * nothing whatever V holds there.
+ *   scores     [n_heads, seq_len] fp16; v_cache [seq_len, n_heads, head_dim]
+ *   out        [n_heads, head_dim] fp16, written
+ *   workspace  >= attn_decode_workspace_bytes(1, n_heads, head_dim, seq_len)
+ */
+attn_status_t attn_qk_f16(const uint16_t *q, const uint16_t *k_cache, uint16_t *scores,
+                          uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                          uint32_t current_pos, void *stream);
+
+attn_status_t attn_pv_f16(const uint16_t *scores, const uint16_t *v_cache, uint16_t *out,
+                          uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                          uint32_t current_pos, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(attn_status_t status);
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -152,3 +152,12 @@ def test_paged_generator_gathers_the_pool():
             dk = torch.stack([kp[bt[b, p // 8], p % 8, h] for p in range(L)])
             dv = torch.stack([vp[bt[b, p // 8], p % 8, h] for p in range(L)])
             assert torch.equal(dk, k.view(L, 8)) and torch.equal(dv, v.view(L, 8))
+
+
+def test_two_dispatch_rejects_bad_arguments(lib):
+    assert lib.attn_qk_f16(None, FAKE, FAKE, 4, 64, 128, 5, None) == NULL
+    assert lib.attn_qk_f16(FAKE, FAKE, FAKE + 1, 4, 64, 128, 5, None) == ALIGN
+    assert lib.attn_qk_f16(FAKE, FAKE, FAKE, 4, 0, 128, 5, None) == DIM
+    assert lib.attn_pv_f16(FAKE, FAKE, None, 4, 64, 128, 5, FAKE, 1 << 30, None) == NULL
+    assert lib.attn_pv_f16(FAKE, FAKE, FAKE, 4, 64, 128, 5, None, 1 << 30, None) == WS
+    assert lib.attn_pv_f16(FAKE, FAKE + 1, FAKE, 4, 64, 128, 5, FAKE, 1 << 30, None) == ALIGN

@@ -569,3 +569,72 @@ def test_paged_split_then_combine_and_many_sequences():
     assert torch.equal(one, two)
     ref, _ = oracle.decode_batched(q, k, v, pos)
     assert_close(one, ref, "1030 paged sequences")
+
+
+# ------------------------------------------------------------ two dispatches
+
+
+def f16_ulp(x):
+    """Spacing of fp16 values at |x| (subnormal spacing near zero)."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+@pytest.mark.parametrize("shape", [(64, 12, 64, 63), (64, 12, 64, 31), (35, 8, 48, 34),
+                                   (5000, 8, 128, 3333), (700, 3, 7, 699), (2049, 4, 256, 100)],
+                         ids=lambda s: "S%d_H%d_D%d_cp%d" % s)
+def test_qk_scores_round_the_exact_score(shape):
+    """First dispatch: every stored score is an fp16 neighbour of the exact
+    scaled dot product, up to fp32 accumulation error (at most D * 2^-24 of
+    sum_i |q_i k_i| / sqrt(D)); every masked one is exactly -inf."""
+    S, H, D, cp = shape
+    rng = np.random.default_rng(S + D)
+    q, k = randn16(rng, (H, D), 2.0), randn16(rng, (S, H, D))
+    _, s_ref, _ = oracle.decode(q, k, k, cp, want_scores=True)
+    sc = ad.qk(to_dev(q), to_dev(k), cp)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy().astype(np.float64)
+    L = min(cp, S - 1) + 1
+    assert np.all(got[:, L:] == -np.inf)
+    err = np.abs(got[:, :L] - s_ref[:, :L])
+    cond = np.einsum("hd,phd->hp", np.abs(q.astype(np.float64)),
+                     np.abs(k[:L].astype(np.float64))) / np.sqrt(D)
+    assert np.all(err < f16_ulp(s_ref[:, :L]) + D * 2.0 ** -24 * cond), err.max()
+
+
+@pytest.mark.parametrize("shape", [(64, 12, 64, 63), (5000, 8, 128, 4999), (300, 7, 48, 150),
+                                   (20000, 2, 64, 19999), (90, 3, 7, 50)],
+                         ids=lambda s: "S%d_H%d_D%d_cp%d" % s)
+def test_pv_from_stored_scores(shape):
+    """Second dispatch on seeded fp16 score rows (some -inf, with NaN V there)."""
+    S, H, D, cp = shape
+    rng = np.random.default_rng(S * 3 + D)
+    sc = randn16(rng, (H, S), 2.0)
+    v = randn16(rng, (S, H, D))
+    holes = rng.choice(min(cp, S - 1) + 1, size=min(5, cp), replace=False)
+    holes = holes[holes != 0]
+    sc[:, holes] = -np.inf
+    v[holes] = np.nan
+    ref = oracle.pv_from_scores(sc, v, cp)
+    out = ad.pv(to_dev(sc), to_dev(v), cp)
+    torch.cuda.synchronize()
+    assert_close(out, ref, str(shape))
+
+
+def test_two_dispatches_against_fp16_score_reading():
+    """QK then PV on the GPU equals softmax.V of the oracle's scores rounded to
+    fp16 (the page's two-dispatch design stores fp16 scores), within the bar."""
+    w = wl.WORKLOADS["h32_d128_s32768_cp20000_garbage"]
+    q_h = wl.make_q(w)[0]
+    k_h, v_h = wl.make_kv(w)
+    k_h, v_h = k_h[0], v_h[0]
+    _, s_ref, _ = oracle.decode(q_h, k_h, v_h, w.cur_pos, want_scores=True, threads=8)
+    ref = oracle.pv_from_scores(s_ref.astype(np.float16), v_h, w.cur_pos)
+    q, k, v = q_h.to(DEV), k_h.to(DEV), v_h.to(DEV)
+    sc = ad.qk(q, k, w.cur_pos)
+    out = ad.pv(sc, v, w.cur_pos)
+    fused = ad.decode(q, k, v, w.cur_pos)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "two dispatches")
+    print("two dispatches vs one pass: max |diff| %.3g" % float((out.float() - fused.float()).abs().max()))
