@@ -8,7 +8,10 @@ The arithmetic lives in ``attn_oracle.c`` (fp64 scalar loops, its own
 binary16 decoder); this module only marshals numpy arrays through ctypes.  It
 follows the page "Developing Apple Metal Kernels in Rust - A Deep Dive
 Through Attention", section "The MSL, briefly" (kernels attention_qk_f16 and
-attention_pv_f16).
+attention_pv_f16).  The decode step around it (rotary embedding of q and of
+the new key, the append of the new row, then attention) follows the page
+"Tutorial 16: Writing Custom Metal Kernels", section "5. Example: Fused RoPE
+Kernel", for the rotation.
 """
 from __future__ import annotations
 
@@ -54,6 +57,13 @@ class OracleLib:
         lib.oracle_attn_decode.restype = ctypes.c_int
         lib.oracle_attn_pv_from_scores.argtypes = [u16p, u16p, u32, u32, u32, u32, u32, u32, f64p]
         lib.oracle_attn_pv_from_scores.restype = ctypes.c_int
+        lib.oracle_double_to_half.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_half.restype = ctypes.c_uint16
+        lib.oracle_double_to_half_array.argtypes = [f64p, ctypes.c_size_t, u16p]
+        lib.oracle_double_to_half_array.restype = None
+        lib.oracle_rope.argtypes = [u16p, u32, u32, u32, ctypes.c_double, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_uint32), f64p]
+        lib.oracle_rope.restype = ctypes.c_int
         self.path = path
         self.lib = lib
 
@@ -120,6 +130,66 @@ class OracleLib:
             raise RuntimeError("oracle_attn_pv_from_scores failed")
         return out
 
+    def double_to_half(self, x) -> np.ndarray:
+        """fp64 values -> IEEE binary16 bits (uint16), nearest with ties to even."""
+        a = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.oracle_double_to_half_array(_ptr(a, ctypes.c_double), a.size,
+                                             _ptr(out, ctypes.c_uint16))
+        return out
+
+    def rope(self, x, positions, *, dims: int, base: float = 10000.0,
+             traditional: bool = False) -> np.ndarray:
+        """Rotary embedding of rows of fp16 values.
+
+        x [..., head_dim] (fp16 or uint16 bits); positions broadcast against
+        x's leading dimensions (one position per row).  Returns float64 of
+        x's shape, exact up to fp64 rounding.
+        """
+        xb = _bits(x)
+        D = xb.shape[-1]
+        lead = xb.shape[:-1]
+        pos = np.ascontiguousarray(np.broadcast_to(np.asarray(positions, dtype=np.int64), lead))
+        if pos.size and (pos.min() < 0 or pos.max() > 0xFFFFFFFF):
+            raise ValueError("positions must fit uint32")
+        pos = pos.astype(np.uint32).reshape(-1)
+        rows = int(np.prod(lead)) if lead else 1
+        out = np.empty(xb.shape, dtype=np.float64)
+        rc = self.lib.oracle_rope(_ptr(xb, ctypes.c_uint16), rows, D, int(dims), float(base),
+                                  1 if traditional else 0, _ptr(pos, ctypes.c_uint32),
+                                  _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError("oracle_rope rejected its arguments")
+        return out
+
+    def decode_step(self, q, k_new, v_new, k_cache, v_cache, current_pos: int, *, dims: int,
+                    base: float = 10000.0, traditional: bool = False, threads: int = 1):
+        """One decode step of one sequence: rotate, append, attend.
+
+        q, k_new, v_new [H, D] fp16 (q and k_new before rotation); k_cache and
+        v_cache [S, H, D] uint16 numpy arrays, whose row pos = min(current_pos,
+        S - 1) is OVERWRITTEN here with the rotated, fp16-rounded k_new and
+        with v_new (the append).  Rows before pos hold earlier tokens, already
+        rotated.  Then attention over positions 0..pos with the rotated,
+        fp16-rounded q.
+
+        Returns a dict: out [H, D] float64; q_rot and k_rot, the exact fp64
+        rotations; q16 and k16, their fp16 bits.
+        """
+        S = k_cache.shape[0]
+        if not (isinstance(k_cache, np.ndarray) and k_cache.dtype == np.uint16
+                and isinstance(v_cache, np.ndarray) and v_cache.dtype == np.uint16):
+            raise TypeError("k_cache and v_cache must be uint16 numpy arrays (updated in place)")
+        pos = min(int(current_pos), S - 1)
+        q_rot = self.rope(q, pos, dims=dims, base=base, traditional=traditional)
+        k_rot = self.rope(k_new, pos, dims=dims, base=base, traditional=traditional)
+        q16 = self.double_to_half(q_rot)
+        k16 = self.double_to_half(k_rot)
+        k_cache[pos] = k16
+        v_cache[pos] = _bits(v_new)
+        out, _, _ = self.decode(q16, k_cache, v_cache, pos, threads=threads)
+        return {"out": out, "q_rot": q_rot, "k_rot": k_rot, "q16": q16, "k16": k16, "pos": pos}
+
     def decode_batched(self, q, k, v, current_pos, *, want_scores=False, threads: int = 1):
         """Independent sequences: q [B, H, D], k/v [B, S, H, D], current_pos [B].
 
@@ -163,3 +233,15 @@ def decode_batched(q, k, v, current_pos, **kw):
 
 def pv_from_scores(scores, v, current_pos):
     return load().pv_from_scores(scores, v, current_pos)
+
+
+def double_to_half(x):
+    return load().double_to_half(x)
+
+
+def rope(x, positions, **kw):
+    return load().rope(x, positions, **kw)
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, **kw):
+    return load().decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, **kw)

@@ -18,6 +18,10 @@
  *       subtracted first (m = max s, z = sum exp(s - m), w = exp(s - m) / z),
  *       then out[h,d] = sum_p w[h,p] * v[p,h,d].
  *
+ * The decode step around it (the rotary embedding of the page "Tutorial 16:
+ * Writing Custom Metal Kernels", and the fp16 rounding of what is stored) is
+ * at the end of the file: oracle_rope and oracle_double_to_half.
+ *
  * Layouts (same section): Q and output [n_heads, head_dim]; K and V caches
  * [seq_len, n_heads, head_dim], element (p,h,i) at (p*n_heads + h)*head_dim + i;
  * scores [n_heads, seq_len].  Inputs are IEEE binary16 bit patterns.
@@ -186,4 +190,100 @@ int oracle_attn_pv_from_scores(const uint16_t *scores, const uint16_t *v, uint32
     }
     free(e);
     return rc;
+}
+
+/*
+ * IEEE 754 binary16 encoding of a binary64 value, rounded to nearest with
+ * ties to even (the rounding of an fp16 store).  Written from the format's
+ * definition: normal numbers are n * 2^(E-10) with 1024 <= n < 2048 and
+ * -14 <= E <= 15 (bits (E+15) << 10 | (n - 1024)); below 2^-14 the grid is
+ * n * 2^-24 with exponent field 0 (bits n, where n = 1024 is the smallest
+ * normal); magnitudes that round past 65504 become infinity; NaN stays NaN.
+ */
+static double oracle_round_half_even(double y)   /* y >= 0, y < 2^52 */
+{
+    const double f = floor(y);
+    const double r = y - f;   /* exact */
+    if (r > 0.5)
+        return f + 1.0;
+    if (r < 0.5)
+        return f;
+    return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+uint16_t oracle_double_to_half(double x)
+{
+    const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    const double a = fabs(x);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7e00u);
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7c00u);
+    if (a < ldexp(1.0, -14)) {
+        const double n = oracle_round_half_even(ldexp(a, 24));   /* 0 .. 1024 */
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int ex;
+    (void)frexp(a, &ex);   /* a = m * 2^ex, 0.5 <= m < 1, so 2^(ex-1) <= a < 2^ex */
+    int E = ex - 1;
+    if (E > 15)
+        return (uint16_t)(sign | 0x7c00u);
+    double n = oracle_round_half_even(ldexp(a, 10 - E));   /* 1024 .. 2048 */
+    if (n == 2048.0) {
+        n = 1024.0;
+        E += 1;
+        if (E > 15)
+            return (uint16_t)(sign | 0x7c00u);
+    }
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+void oracle_double_to_half_array(const double *x, size_t n, uint16_t *out)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = oracle_double_to_half(x[i]);
+}
+
+/*
+ * Rotary position embedding, as the page "Tutorial 16: Writing Custom Metal
+ * Kernels" (section "5. Example: Fused RoPE Kernel") describes its FastRoPE
+ * (dims, base = 10000, traditional = False, one offset per batch entry): the
+ * first `dims` values of a vector are split into pairs and each pair is
+ * turned through a 2D rotation whose angle grows with the position.
+ * Readings where the page leaves a step open:
+ *  - pair i (0 <= i < dims/2) turns by the angle pos * theta_i with
+ *    theta_i = base^(-2i/dims), the usual rotary frequencies;
+ *  - traditional = 0 pairs element i with element i + dims/2, traditional != 0
+ *    pairs elements 2i and 2i+1;
+ *  - a pair (a, b) becomes (a cos t - b sin t, a sin t + b cos t);
+ *  - elements at index >= dims are passed through unchanged.
+ * x: n_rows rows of head_dim binary16 values; pos[r] is row r's position;
+ * out: fp64 [n_rows, head_dim], exact up to fp64 rounding.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_rope(const uint16_t *x, uint32_t n_rows, uint32_t head_dim, uint32_t dims, double base,
+                int traditional, const uint32_t *pos, double *out)
+{
+    if (!x || !pos || !out || head_dim == 0 || dims > head_dim || (dims & 1u) || !(base > 0.0))
+        return -1;
+    const size_t D = head_dim;
+    const uint32_t half = dims / 2;
+    for (size_t r = 0; r < n_rows; ++r) {
+        const uint16_t *row = x + r * D;
+        double *o = out + r * D;
+        for (size_t d = 0; d < D; ++d)
+            o[d] = oracle_half_to_double(row[d]);
+        for (uint32_t i = 0; i < half; ++i) {
+            const size_t ia = traditional ? 2 * (size_t)i : i;
+            const size_t ib = traditional ? 2 * (size_t)i + 1 : (size_t)i + half;
+            const double theta = pow(base, -(2.0 * i) / (double)dims);
+            const double t = (double)pos[r] * theta;
+            const double c = cos(t), s = sin(t);
+            const double a = oracle_half_to_double(row[ia]);
+            const double b = oracle_half_to_double(row[ib]);
+            o[ia] = a * c - b * s;
+            o[ib] = a * s + b * c;
+        }
+    }
+    return 0;
 }

@@ -392,6 +392,266 @@ def pin_pv_direct_formula(orc):
         assert np.allclose(out, ref, rtol=1e-12, atol=1e-13), (S, H, D)
 
 
+# ------------------------------------------------------- fp16 rounding
+
+
+def pin_double_to_half_matches_numpy(orc):
+    """fp64 -> fp16 rounding agrees with numpy's own conversion everywhere
+    that matters: every fp16 value, every midpoint between neighbours (the
+    ties), one fp64 step either side of each midpoint, and a log-uniform
+    sweep from below the subnormals to past the overflow threshold."""
+    bits = np.arange(0x7C01, dtype=np.uint32).astype(np.uint16)   # +0 .. +inf
+    vals = bits.view(np.float16).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2.0                             # exact in fp64
+    rng = _rng(30)
+    sweep = np.exp2(rng.uniform(-30.0, 17.5, 200000))
+    xs = np.concatenate([vals, mids, np.nextafter(mids, 0.0), np.nextafter(mids, np.inf), sweep,
+                         [65504.0, 65519.99, 65520.0, 1e300, 2.0 ** -25, 2.0 ** -26]])
+    xs = np.concatenate([xs, -xs])
+    got = orc.double_to_half(xs)
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, "fp16 rounding differs at %r" % xs[bad[:5]]
+    nan = orc.double_to_half(np.array([np.nan]))[0]
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0, "NaN must stay NaN"
+
+
+def pin_double_to_half_hand_cases(orc):
+    """Values fixed by the binary16 format itself."""
+    cases = {
+        1.0: 0x3C00, -2.0: 0xC000, 65504.0: 0x7BFF, 65520.0: 0x7C00,   # tie at the top: to inf
+        2.0 ** -14: 0x0400, 2.0 ** -24: 0x0001, 2.0 ** -25: 0x0000,     # tie to even (0)
+        3 * 2.0 ** -25: 0x0002, 1.0 + 2.0 ** -11: 0x3C00,               # ties to even
+        1.0 + 3 * 2.0 ** -11: 0x3C02, -0.0: 0x8000, float("inf"): 0x7C00,
+    }
+    for x, want in cases.items():
+        got = int(orc.double_to_half(np.array([x]))[0])
+        assert got == want, (x, hex(got), hex(want))
+
+
+# ----------------------------------------------------------- rotary embedding
+# Page "Tutorial 16: Writing Custom Metal Kernels", section "5. Example: Fused
+# RoPE Kernel"; test names from the page "Developing Apple Metal Kernels in
+# Rust - A Deep Dive Through Attention", section "Testing".
+
+
+def _dec_pi(prec):
+    """pi to `prec` digits by Machin's formula, 16 atan(1/5) - 4 atan(1/239)."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = prec + 10
+        eps = Decimal(10) ** -(prec + 8)
+
+        def atan_inv(n):
+            x = Decimal(1) / n
+            x2, term, total, k = x * x, x, x, 1
+            while True:
+                term = -term * x2
+                k += 2
+                t = term / k
+                if abs(t) < eps:
+                    return total
+                total += t
+
+        return +(16 * atan_inv(5) - 4 * atan_inv(239))
+
+
+def _dec_angle_cos_sin(pos, i, dims, base, prec=50):
+    """cos and sin of pos * base^(-2i/dims), in decimal arithmetic (reduction
+    modulo 2 pi and Taylor series), independent of the C math library."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = prec + 20
+        theta = Decimal(base) ** (Decimal(-2 * i) / Decimal(dims))
+        t = Decimal(pos) * theta
+        two_pi = 2 * _dec_pi(prec + 20)
+        r = t - (t / two_pi).to_integral_value() * two_pi
+        eps = Decimal(10) ** -(prec + 5)
+        c, s = Decimal(0), Decimal(0)
+        term, n = Decimal(1), 0   # r^n / n!
+        while True:
+            if n % 4 == 0:
+                c += term
+            elif n % 4 == 1:
+                s += term
+            elif n % 4 == 2:
+                c -= term
+            else:
+                s -= term
+            n += 1
+            term = term * r / n
+            if abs(term) < eps and n > 4:
+                break
+        return float(c), float(s), float(t)
+
+
+def _unit(D, j):
+    x = np.zeros(D, dtype=np.float16)
+    x[j] = 1.0
+    return x
+
+
+def pin_rope_position_zero_is_identity(orc):
+    """Position 0 turns every pair by angle 0 (page test
+    test_rope_position_zero_is_identity)."""
+    rng = _rng(31)
+    for D, dims, trad in [(64, 64, False), (128, 128, True), (96, 32, False), (10, 6, True)]:
+        x = _randn_f16(rng, (5, D))
+        out = orc.rope(x, 0, dims=dims, traditional=trad)
+        assert np.array_equal(out, x.astype(np.float64)), (D, dims, trad)
+
+
+def pin_rope_positions_differ(orc):
+    """Different positions give different vectors (page test
+    test_rope_different_positions_differ), with the tail past dims untouched."""
+    rng = _rng(32)
+    x = _randn_f16(rng, (1, 80))
+    a = orc.rope(x, 5, dims=64)
+    b = orc.rope(x, 6, dims=64)
+    assert np.abs(a[:, :64] - b[:, :64]).max() > 1e-3
+    assert np.array_equal(a[:, 64:], x[:, 64:].astype(np.float64))
+    assert np.array_equal(b[:, 64:], x[:, 64:].astype(np.float64))
+
+
+def pin_rope_single_pair_closed_form(orc):
+    """dims = 2: one pair with frequency 1, so e_0 -> (cos p, sin p) and
+    e_1 -> (-sin p, cos p), for small and very large positions (decimal
+    reference, so the large angles check the fp64 reduction too)."""
+    for pos in [1, 2, 3, 1000, 20000, 131071]:
+        c, s, t = _dec_angle_cos_sin(pos, 0, 2, 10000)
+        tol = 1e-13 + 4e-16 * t
+        for trad in (False, True):
+            o0 = orc.rope(_unit(2, 0)[None], pos, dims=2, traditional=trad)[0]
+            o1 = orc.rope(_unit(2, 1)[None], pos, dims=2, traditional=trad)[0]
+            assert abs(o0[0] - c) < tol and abs(o0[1] - s) < tol, (pos, o0, c, s)
+            assert abs(o1[0] + s) < tol and abs(o1[1] - c) < tol, (pos, o1, c, s)
+
+
+def pin_rope_frequencies_and_pairing(orc):
+    """head_dim 6, dims 4: pair i turns by pos * base^(-2i/dims).  Half-split
+    pairs are (0, 2) and (1, 3); traditional pairs are (0, 1) and (2, 3);
+    elements 4 and 5 pass through.  Unit vectors show every entry."""
+    D, dims = 6, 4
+    for base, pos in [(10000.0, 100), (100.0, 10), (500000.0, 777)]:
+        for trad in (False, True):
+            pairs = [(0, 1), (2, 3)] if trad else [(0, 2), (1, 3)]
+            for i, (ia, ib) in enumerate(pairs):
+                c, s, t = _dec_angle_cos_sin(pos, i, dims, base)
+                tol = 1e-13 + 4e-16 * t
+                oa = orc.rope(_unit(D, ia)[None], pos, dims=dims, base=base, traditional=trad)[0]
+                ob = orc.rope(_unit(D, ib)[None], pos, dims=dims, base=base, traditional=trad)[0]
+                want_a = np.zeros(D)
+                want_a[ia], want_a[ib] = c, s
+                want_b = np.zeros(D)
+                want_b[ia], want_b[ib] = -s, c
+                assert np.abs(oa - want_a).max() < tol, (base, pos, trad, i, oa, want_a)
+                assert np.abs(ob - want_b).max() < tol, (base, pos, trad, i, ob, want_b)
+            for j in (4, 5):
+                o = orc.rope(_unit(D, j)[None], pos, dims=dims, base=base, traditional=trad)[0]
+                assert np.array_equal(o, _unit(D, j).astype(np.float64))
+
+
+def pin_rope_preserves_pair_norms(orc):
+    """A rotation keeps the length of every pair."""
+    rng = _rng(33)
+    D, dims = 128, 96
+    x = _randn_f16(rng, (64, D), 3.0)
+    pos = rng.integers(0, 200000, 64)
+    for trad in (False, True):
+        out = orc.rope(x, pos, dims=dims, traditional=trad)
+        xd = x.astype(np.float64)
+        if trad:
+            n_in = xd[:, 0:dims:2] ** 2 + xd[:, 1:dims:2] ** 2
+            n_out = out[:, 0:dims:2] ** 2 + out[:, 1:dims:2] ** 2
+        else:
+            h = dims // 2
+            n_in = xd[:, :h] ** 2 + xd[:, h:dims] ** 2
+            n_out = out[:, :h] ** 2 + out[:, h:dims] ** 2
+        assert np.allclose(n_out, n_in, rtol=1e-12, atol=1e-12)
+
+
+def pin_rope_scores_depend_on_relative_position(orc):
+    """<R(m) q, R(n) k> = <R(m - n) q, k>: the rotated dot product depends
+    only on the distance between the two positions."""
+    rng = _rng(34)
+    for D, dims, trad in [(128, 128, False), (64, 32, True)]:
+        q = _randn_f16(rng, (1, D))
+        k = _randn_f16(rng, (1, D))
+        scale = np.linalg.norm(q.astype(np.float64)) * np.linalg.norm(k.astype(np.float64))
+        for m, n in [(5, 0), (100, 37), (4096, 4000), (131071, 131000), (70000, 12)]:
+            lhs = float(orc.rope(q, m, dims=dims, traditional=trad)[0]
+                        @ orc.rope(k, n, dims=dims, traditional=trad)[0])
+            rhs = float(orc.rope(q, m - n, dims=dims, traditional=trad)[0] @ k[0].astype(np.float64))
+            assert abs(lhs - rhs) < 1e-10 * scale * (1 + m / 1000.0), (D, m, n, lhs, rhs)
+
+
+def pin_rope_traditional_is_interleaved_half_split(orc):
+    """Traditional pairing is the half-split pairing applied to the vector
+    with its even elements moved to the front and its odd ones after them."""
+    rng = _rng(35)
+    D, dims = 64, 48
+    x = _randn_f16(rng, (8, D))
+    pos = rng.integers(0, 50000, 8)
+    perm = np.concatenate([np.arange(0, dims, 2), np.arange(1, dims, 2), np.arange(dims, D)])
+    trad = orc.rope(x, pos, dims=dims, traditional=True)
+    split = orc.rope(np.ascontiguousarray(x[:, perm]), pos, dims=dims, traditional=False)
+    assert np.array_equal(trad[:, perm], split)
+
+
+def pin_decode_step_first_position(orc):
+    """A step at position 0 attends to its own row only: the output is v_new
+    exactly, and the appended key is k_new (angle 0)."""
+    rng = _rng(36)
+    S, H, D = 8, 3, 32
+    kc = _randn_f16(rng, (S, H, D)).view(np.uint16).copy()
+    vc = _randn_f16(rng, (S, H, D)).view(np.uint16).copy()
+    q, kn, vn = (_randn_f16(rng, (H, D)) for _ in range(3))
+    r = orc.decode_step(q, kn, vn, kc, vc, 0, dims=D)
+    assert np.array_equal(r["out"], vn.astype(np.float64))
+    assert np.array_equal(kc[0], kn.view(np.uint16)) and np.array_equal(vc[0], vn.view(np.uint16))
+
+
+def pin_decode_step_against_torch(orc):
+    """The step is rotate (at pos), round to fp16, write row pos, attend over
+    0..pos: rebuilt here with torch float64 for the rotation and torch's
+    scaled-dot-product attention, rows after pos filled with garbage."""
+    rng = _rng(37)
+    for S, H, D, dims, cp, trad in [(40, 4, 64, 64, 17, False), (33, 2, 128, 96, 32, True),
+                                    (16, 3, 32, 32, 99, False)]:
+        kc = _randn_f16(rng, (S, H, D)).view(np.uint16).copy()
+        vc = _randn_f16(rng, (S, H, D)).view(np.uint16).copy()
+        q, kn, vn = (_randn_f16(rng, (H, D)) for _ in range(3))
+        kc0, vc0 = kc.copy(), vc.copy()
+        r = orc.decode_step(q, kn, vn, kc, vc, cp, dims=dims, traditional=trad)
+        pos = min(cp, S - 1)
+
+        def t_rope(x):
+            x = torch.from_numpy(x.astype(np.float64))
+            i = torch.arange(dims // 2, dtype=torch.float64)
+            ang = pos * torch.pow(torch.tensor(10000.0, dtype=torch.float64), -2.0 * i / dims)
+            c, s = torch.cos(ang), torch.sin(ang)
+            y = x.clone()
+            ia = torch.arange(0, dims, 2) if trad else torch.arange(dims // 2)
+            ib = ia + 1 if trad else ia + dims // 2
+            a, b = x[:, ia], x[:, ib]
+            y[:, ia] = a * c - b * s
+            y[:, ib] = a * s + b * c
+            return y.numpy().astype(np.float16)
+
+        q16, k16 = t_rope(q), t_rope(kn)
+        assert np.array_equal(r["q16"], q16.view(np.uint16))
+        assert np.array_equal(r["k16"], k16.view(np.uint16))
+        want_k, want_v = kc0.copy(), vc0.copy()
+        want_k[pos], want_v[pos] = k16.view(np.uint16), vn.view(np.uint16)
+        assert np.array_equal(kc, want_k) and np.array_equal(vc, want_v)
+        kt = torch.from_numpy(want_k[: pos + 1].view(np.float16).astype(np.float64)).transpose(0, 1)
+        vt = torch.from_numpy(want_v[: pos + 1].view(np.float16).astype(np.float64)).transpose(0, 1)
+        qt = torch.from_numpy(q16.astype(np.float64))[:, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous())
+        assert np.allclose(r["out"], ref[:, 0, :].numpy(), rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_half_decoder_all_patterns,
     pin_one_hot_query_scores,
@@ -414,4 +674,15 @@ ALL_PINS = [
     pin_pv_two_positions_closed_form,
     pin_pv_neg_inf_scores_have_zero_weight,
     pin_pv_direct_formula,
+    pin_double_to_half_matches_numpy,
+    pin_double_to_half_hand_cases,
+    pin_rope_position_zero_is_identity,
+    pin_rope_positions_differ,
+    pin_rope_single_pair_closed_form,
+    pin_rope_frequencies_and_pairing,
+    pin_rope_preserves_pair_norms,
+    pin_rope_scores_depend_on_relative_position,
+    pin_rope_traditional_is_interleaved_half_split,
+    pin_decode_step_first_position,
+    pin_decode_step_against_torch,
 ]

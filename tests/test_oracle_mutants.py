@@ -32,6 +32,16 @@ MUTANTS = {
     "pv_scores_transposed": ("oracle_half_to_double(scores[h * S + p])", "oracle_half_to_double(scores[p * H + h])"),
     "pv_max_is_min": ("            if (s > m)\n", "            if (s < m || m == -INFINITY)\n"),
     "pv_neg_inf_not_skipped": ("                if (e[p] != 0.0)\n", ""),
+    "half_ties_always_up": ("return fmod(f, 2.0) == 0.0 ? f : f + 1.0;", "return f + 1.0;"),
+    "half_subnormal_scale": ("ldexp(a, 24)", "ldexp(a, 23)"),
+    "half_overflow_missed": ("int E = ex - 1;\n    if (E > 15)", "int E = ex - 1;\n    if (E > 99)"),
+    "half_sign_dropped": ("signbit(x) ? 0x8000u : 0u", "0u"),
+    "rope_sin_sign_flipped": ("o[ia] = a * c - b * s;", "o[ia] = a * c + b * s;"),
+    "rope_frequency_exponent": ("-(2.0 * i) / (double)dims", "-(1.0 * i) / (double)dims"),
+    "rope_pairing_swapped": ("traditional ? ", "!traditional ? "),
+    "rope_position_off_by_one": ("(double)pos[r] * theta", "(double)(pos[r] + 1) * theta"),
+    "rope_tail_zeroed": ("o[d] = oracle_half_to_double(row[d]);", "o[d] = 0.0;"),
+    "rope_partner_wrong": ("(size_t)i + half;", "(size_t)i + half - (i > 0);"),
 }
 
 
