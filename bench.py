@@ -59,9 +59,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
-    p.add_argument("--path", choices=["fused", "two_dispatch"], default="fused",
+    p.add_argument("--path", choices=["fused", "two_dispatch", "step"], default="fused",
                    help="two_dispatch: fp16 score row written then read back "
-                        "(attn_qk_f16 + attn_pv_f16), single-sequence workloads only")
+                        "(attn_qk_f16 + attn_pv_f16), single-sequence workloads only; "
+                        "step: rotate q and a new key, append the new K/V row at "
+                        "current_pos, attend (attn_decode_step_f16*), dense caches only")
     return p.parse_args()
 
 
@@ -220,6 +222,27 @@ def main():
             rc = lib.attn_qk_f16(*qk_args[r])
             return rc if rc else lib.attn_pv_f16(*pv_args[r])
         step_fns = [lambda r=r: two_dispatch(r) for r in range(copies)]
+    elif args.path == "step":
+        if w.paged:
+            raise SystemExit("--path step needs a dense cache")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed + 1000)
+        k_new = torch.randn(w.q_shape, generator=gen, device=dev).half()
+        v_new = torch.randn(w.q_shape, generator=gen, device=dev).half()
+        rot = (D, ctypes.c_double(10000.0), 0)
+        if w.batched:
+            step_args = [(vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
+                          vp(ks[r].data_ptr()), vp(vs[r].data_ptr()), vp(out.data_ptr()),
+                          vp(cp_dev.data_ptr()), B, H, D, S) + rot
+                         + (vp(ws.data_ptr()), ws_bytes, sh) for r in range(copies)]
+            fn = lib.attn_decode_step_f16_batched
+        else:
+            step_args = [(vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
+                          vp(ks[r].data_ptr()), vp(vs[r].data_ptr()), vp(out.data_ptr()),
+                          H, D, S, min(cp_host, S - 1)) + rot
+                         + (vp(ws.data_ptr()), ws_bytes, sh) for r in range(copies)]
+            fn = lib.attn_decode_step_f16
+        step_fns = [lambda sa=sa: fn(*sa) for sa in step_args]
     else:
         step_fns = [lambda fa=fa: full(*fa) for fa in full_args]
     split = lib.attn_decode_f16_paged_split if w.paged else lib.attn_decode_f16_split
@@ -294,6 +317,8 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "path": args.path,
     }
+    if args.path == "step":
+        config["kv_bytes_counted"] = "rows 0..pos-1 of K and V read, row pos of K and V written"
     line = {
         "metric": METRIC,
         "value": round(value, 2),

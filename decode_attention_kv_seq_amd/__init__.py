@@ -69,6 +69,16 @@ def load_library(path: str = LIB_PATH):
     lib.attn_qk_f16.restype = ctypes.c_int
     lib.attn_pv_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, vp, sz, vp]
     lib.attn_pv_f16.restype = ctypes.c_int
+    f64 = ctypes.c_double
+    i32 = ctypes.c_int
+    lib.attn_decode_step_f16.argtypes = [vp, vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, f64, i32,
+                                         vp, sz, vp]
+    lib.attn_decode_step_f16.restype = ctypes.c_int
+    lib.attn_decode_step_f16_batched.argtypes = [vp, vp, vp, vp, vp, vp, vp, u32, u32, u32, u32,
+                                                 u32, f64, i32, vp, sz, vp]
+    lib.attn_decode_step_f16_batched.restype = ctypes.c_int
+    lib.attn_rope_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, f64, i32, vp]
+    lib.attn_rope_f16.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -316,4 +326,85 @@ def pv(scores, v, current_pos: int, *, out=None, workspace=None, stream=None):
     _check(lib.attn_pv_f16(_ptr(scores), _ptr(v), _ptr(out), H, D, S, int(current_pos),
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                            _stream_handle(stream)))
+    return out
+
+
+def _rope_params(rope_dims, head_dim, base):
+    dims = head_dim if rope_dims is None else int(rope_dims)
+    if not 0 <= dims <= 0xFFFFFFFF:
+        raise ValueError("rope_dims out of range")
+    return dims, float(base)
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, *, rope_dims=None,
+                rope_base: float = 10000.0, traditional: bool = False, out=None, workspace=None,
+                stream=None):
+    """One decode step: rotate q and k_new at the new token's position, append
+    the rotated k_new and v_new at slot current_pos of the caches (written in
+    place), and attend over positions 0..current_pos.
+
+    Single sequence: q, k_new, v_new [H, D]; caches [S, H, D]; current_pos an
+    int < S.  Batch: q, k_new, v_new [B, H, D]; caches [B, S, H, D];
+    current_pos an int32 GPU tensor [B] (values >= S use slot S - 1).
+    ``rope_dims`` defaults to head_dim.  Returns out, shaped like q."""
+    lib = load_library()
+    _req(k_cache, "k_cache", torch.float16)
+    dev = k_cache.device
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (v_cache, "v_cache")):
+        _req(t, n, torch.float16, dev)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must have the same shape")
+    batched = k_cache.dim() == 4
+    if k_cache.dim() not in (3, 4):
+        raise ValueError("caches must be [S, H, D] or [B, S, H, D]")
+    S, H, D = k_cache.shape[-3:]
+    B = k_cache.shape[0] if batched else 1
+    row_shape = (B, H, D) if batched else (H, D)
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        if tuple(t.shape) != row_shape:
+            raise ValueError("%s must be %s" % (n, list(row_shape)))
+    if out is None:
+        out = torch.empty(row_shape, dtype=torch.float16, device=dev)
+    _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != row_shape:
+        raise ValueError("out must be %s" % list(row_shape))
+    dims, base = _rope_params(rope_dims, D, rope_base)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, D, S, dev)
+    ws_n = workspace.numel() * workspace.element_size()
+    if batched:
+        cp = _cp_tensor(current_pos, B, dev)
+        _check(lib.attn_decode_step_f16_batched(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cp),
+            B, H, D, S, dims, base, 1 if traditional else 0, _ptr(workspace), ws_n,
+            _stream_handle(stream)))
+    else:
+        if not 0 <= int(current_pos) <= 0xFFFFFFFF:
+            raise ValueError("current_pos must fit in uint32")
+        _check(lib.attn_decode_step_f16(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out), H, D, S,
+            int(current_pos), dims, base, 1 if traditional else 0, _ptr(workspace), ws_n,
+            _stream_handle(stream)))
+    return out
+
+
+def rope(x, positions, *, rope_dims=None, rope_base: float = 10000.0, traditional: bool = False,
+         out=None, stream=None):
+    """Rotary embedding: x [B, H, D] fp16, positions int32/uint32 GPU tensor
+    [B] (row (b, h) turns at positions[b]) -> fp16 [B, H, D]."""
+    lib = load_library()
+    _req(x, "x", torch.float16)
+    dev = x.device
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, n_heads, head_dim]")
+    B, H, D = x.shape
+    pos = _cp_tensor(positions, B, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [batch, n_heads, head_dim]")
+    dims, base = _rope_params(rope_dims, D, rope_base)
+    _check(lib.attn_rope_f16(_ptr(x), _ptr(out), _ptr(pos), B, H, D, dims, base,
+                             1 if traditional else 0, _stream_handle(stream)))
     return out

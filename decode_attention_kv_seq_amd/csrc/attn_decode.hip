@@ -73,6 +73,20 @@ __device__ __forceinline__ Pack<VEC> zero_pack() {
 }
 
 template <int VEC>
+__device__ __forceinline__ Pack<VEC> make_pack(const uint16_t (&hv)[VEC]) {
+    Pack<VEC> r;
+    if constexpr (VEC == 1) {
+        r.w = hv[0];
+    } else if constexpr (VEC == 2) {
+        r.w = (uint32_t)hv[0] | (uint32_t)hv[1] << 16;
+    } else {
+#pragma unroll
+        for (int j = 0; j < VEC / 2; ++j) r.w[j] = (uint32_t)hv[2 * j] | (uint32_t)hv[2 * j + 1] << 16;
+    }
+    return r;
+}
+
+template <int VEC>
 __device__ __forceinline__ uint32_t pack_word(const Pack<VEC> &p, int j) {
     if constexpr (VEC == 8) return p.w[j];
     else if constexpr (VEC == 4) return p.w[j];
@@ -137,6 +151,80 @@ __device__ __forceinline__ uint16_t f2h_rne(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// ------------------------------------------------------- rotary embedding
+// The rotation of the page "Tutorial 16: Writing Custom Metal Kernels"
+// (section "5. Example: Fused RoPE Kernel"): pair i of the first `dims`
+// values turns by pos * base^(-2i/dims); pairs are (i, i + dims/2), or
+// (2i, 2i+1) when `traditional`; values past dims pass through.  The page
+// loads precomputed cos/sin; here the frequencies come precomputed (fp64,
+// from the host) and cos/sin of the angle are evaluated in the kernel: the
+// angle and its reduction to [-pi/4, pi/4] are fp64, so positions in the
+// billions keep a full fp32 cos/sin, and the rotation itself is fp32.
+
+constexpr uint32_t kRopeMaxPairs = ATTN_MAX_HEAD_DIM / 2;
+
+struct RopeArgs {
+    const uint16_t *k_new;   // [B, H, D] new key rows, before rotation
+    const uint16_t *v_new;   // [B, H, D] new value rows
+    uint16_t *k_cache;       // caches the new rows are written into
+    uint16_t *v_cache;
+    uint32_t dims;           // rotated leading values (even, <= D)
+    uint32_t traditional;
+    double theta[kRopeMaxPairs];   // base^(-2i/dims) for i < dims/2
+};
+
+// cos and sin of pos * theta_i.  The angle t is split as n pi/2 + x with n
+// the nearest integer to t 2/pi and x = t - n pi/2 taken with pi/2 in two
+// parts (Cody and Waite's reduction), |x| <= pi/4; sin x and cos x come from
+// their Taylor series (through x^9 and x^10: truncation below 2e-9), and the
+// quadrant n mod 4 picks signs and order.
+__device__ __forceinline__ void rope_cos_sin(uint32_t i, uint32_t pos, const RopeArgs &r, float *c,
+                                             float *s) {
+    constexpr double kPio2Hi = 1.5707963267948966;      // pi/2 rounded to fp64
+    constexpr double kPio2Lo = 6.123233995736766e-17;   // pi/2 - kPio2Hi
+    constexpr double kTwoOverPi = 0.6366197723675814;
+    const double t = (double)pos * r.theta[i];
+    const double n = rint(t * kTwoOverPi);
+    const float x = (float)fma(-n, kPio2Lo, fma(-n, kPio2Hi, t));
+    const float x2 = x * x;
+    const float sx = x * (1.f + x2 * (-1.f / 6.f + x2 * (1.f / 120.f + x2 * (-1.f / 5040.f +
+                                                                             x2 * (1.f / 362880.f)))));
+    const float cx = 1.f + x2 * (-0.5f + x2 * (1.f / 24.f + x2 * (-1.f / 720.f +
+                                                                x2 * (1.f / 40320.f +
+                                                                      x2 * (-1.f / 3628800.f)))));
+    const uint32_t quad = (uint32_t)((uint64_t)n & 3u);   // t >= 0, so n >= 0
+    const float cq = (quad & 1u) ? sx : cx;
+    const float sq = (quad & 1u) ? cx : sx;
+    *c = (quad == 1u || quad == 2u) ? -cq : cq;
+    *s = (quad >= 2u) ? -sq : sq;
+}
+
+// The element that element d is paired with (d itself past dims).
+__device__ __forceinline__ uint32_t rope_partner(uint32_t d, const RopeArgs &r) {
+    if (d >= r.dims) return d;
+    const uint32_t half = r.dims >> 1;
+    return r.traditional ? (d ^ 1u) : (d < half ? d + half : d - half);
+}
+
+// Element d of a rotated row, from its value x and its partner's value y.
+__device__ __forceinline__ float rope_apply(float x, float y, uint32_t d, const RopeArgs &r,
+                                            uint32_t pos) {
+#pragma clang fp contract(off)
+    if (d >= r.dims) return x;
+    const uint32_t half = r.dims >> 1;
+    const bool first = r.traditional ? (d & 1u) == 0 : d < half;
+    const uint32_t i = r.traditional ? d >> 1 : (first ? d : d - half);
+    float c, s;
+    rope_cos_sin(i, pos, r, &c, &s);
+    // pair (a, b) -> (a c - b s, a s + b c); x is a when first, b otherwise
+    return first ? fmaf(x, c, -(y * s)) : fmaf(y, s, x * c);
+}
+
+__device__ __forceinline__ float rope_elem(const uint16_t *row, uint32_t d, const RopeArgs &r,
+                                           uint32_t pos) {
+    return rope_apply(h2f(row[d]), h2f(row[rope_partner(d, r)]), d, r, pos);
+}
+
 // ------------------------------------------------------------ split kernel
 
 struct SplitArgs {
@@ -166,6 +254,7 @@ struct SplitArgs {
     uint32_t max_blocks;      // block-table row length
     uint32_t num_blocks;      // pages in the pool
     uint32_t page_shift;      // log2(positions per page)
+    RopeArgs rope;            // decode step: q is rotated, the new token's slot is skipped
 };
 
 // Workspace header written by the split launch and read by the combine.
@@ -198,7 +287,8 @@ struct PieceDst {
 // Stream positions [c0, c_end) of head block hb of sequence b through the
 // online softmax and leave one merged state per head at `dst`.  The caller
 // guarantees c0 < c_end.  LDS is free again when this returns.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC,
+          bool ROPE>
 __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint32_t hb,
                                             uint32_t c0, uint32_t c_end, const PieceDst &dst,
                                             float *sm_o, float *sm_m, float *sm_l) {
@@ -227,7 +317,31 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     }
 
     Pack<VEC> qp[NV];
-    if constexpr (!SC) {
+    if constexpr (ROPE) {
+        // Decode step: the head block's query rows, rotated at the new
+        // token's position and rounded to fp16 (the combine rotates them the
+        // same way), one element per thread into LDS, which is free here.
+        // Done before the first K/V loads: overlapping the two costs the main
+        // loop registers, which is worse.
+        uint16_t *sq = reinterpret_cast<uint16_t *>(sm_o);
+        const uint32_t pos = valid_len(a.cp_dev ? a.cp_dev[b] : a.cp_host, a.S) - 1u;
+        const uint16_t *qblk = a.q + ((size_t)b * a.H + (size_t)hb * a.hpb) * D;
+        const uint32_t n_q = a.hpb * a.D;
+#pragma unroll 1
+        for (uint32_t idx = tid; idx < n_q; idx += kThreads) {
+            const uint32_t ho = idx / a.D;
+            sq[idx] = f2h_rne(rope_elem(qblk + (size_t)ho * D, idx - ho * a.D, a.rope, pos));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            uint16_t hv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) hv[e] = eok[j] ? sq[hg * a.D + eoff[j] + e] : 0;
+            qp[j] = make_pack<VEC>(hv);
+        }
+        __syncthreads();   // LDS is written again by the merge below
+    } else if constexpr (!SC) {
         const uint16_t *qrow = a.q + ((size_t)b * a.H + h) * D;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
@@ -430,7 +544,8 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 // Chunked grid: workgroup (hb + n_hb*chunk, b) takes positions
 // [chunk*C, (chunk+1)*C) of head block hb.  Partials: o [B, H, nc_stride, D],
 // (m, l) [B, H, nc_stride, 2].
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC,
+          bool ROPE>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     write_header(a, 0);
@@ -438,7 +553,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     const uint32_t hb = blockIdx.x % a.n_hb;
     const uint32_t chunk = blockIdx.x / a.n_hb;
     const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
-    const uint32_t L = valid_len(cp, a.S);
+    // a decode step streams the positions before the new token's slot
+    const uint32_t L = valid_len(cp, a.S) - (ROPE ? 1u : 0u);
     const uint32_t c0 = chunk * a.chunk;
     if (c0 >= L) return;                     // whole workgroup: nothing to read
     const uint32_t c_end = min(c0 + a.chunk, L);
@@ -449,21 +565,23 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     dst.pml = a.part_ml + (bh0 * a.nc_stride + chunk) * 2;
     dst.pml_hs = (size_t)a.nc_stride * 2;
     dst.out = a.direct ? a.out + bh0 * a.D : nullptr;
-    split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+    split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC, ROPE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
+                                                                 sm_l);
 }
 
-// Inclusive prefix of the valid lengths: pref[0] = 0, pref[b+1] = sum of
-// L_0..L_b, for batch <= kBalancedMaxBatch.  Hillis-Steele scan in LDS over
+// Inclusive prefix of the streamed lengths (valid length minus `excl`):
+// pref[0] = 0, pref[b+1] = sum of L_0..L_b, for batch <= kBalancedMaxBatch.  Hillis-Steele scan in LDS over
 // per-thread sums of consecutive sequences.  Every thread must call it.
 template <int NT>
 __device__ __forceinline__ void length_prefix(const uint32_t *cp, uint32_t cp_host, uint32_t S,
-                                              uint32_t batch, uint64_t *pref, uint64_t *tmp) {
+                                              uint32_t excl, uint32_t batch, uint64_t *pref,
+                                              uint64_t *tmp) {
     const uint32_t tid = threadIdx.x;
     const uint32_t per = (batch + NT - 1) / NT;   // <= kBalancedMaxBatch / NT
     const uint32_t b0 = tid * per;
     uint64_t sum = 0;
     for (uint32_t i = 0; i < per; ++i)
-        if (b0 + i < batch) sum += valid_len(cp ? cp[b0 + i] : cp_host, S);
+        if (b0 + i < batch) sum += valid_len(cp ? cp[b0 + i] : cp_host, S) - excl;
     tmp[tid] = sum;
     __syncthreads();
     for (uint32_t off = 1; off < NT; off <<= 1) {
@@ -476,14 +594,14 @@ __device__ __forceinline__ void length_prefix(const uint32_t *cp, uint32_t cp_ho
     if (tid == 0) pref[0] = 0;
     for (uint32_t i = 0; i < per; ++i)
         if (b0 + i < batch) {
-            run += valid_len(cp ? cp[b0 + i] : cp_host, S);
+            run += valid_len(cp ? cp[b0 + i] : cp_host, S) - excl;
             pref[b0 + i + 1] = run;
         }
     __syncthreads();
 }
 
-// Sequence b with pref[b] <= key < pref[b+1] (pref strictly increases: every
-// sequence has at least one position).
+// Sequence b with pref[b] <= key < pref[b+1], for key < pref[batch]; such a
+// sequence has at least one position (empty ones are never returned).
 __device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t batch, uint64_t key) {
     uint32_t lo = 0, hi = batch;   // pref[lo] <= key < pref[hi]
     while (hi - lo > 1) {
@@ -499,13 +617,14 @@ __device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t
 // `grid` equal ranges, one per workgroup.  A workgroup writes one partial per
 // segment piece it covers, at slot w + s; o [slots, hpb, D], (m, l)
 // [slots, hpb, 2] with slots = grid + batch*n_hb.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC,
+          bool ROPE>
 __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     write_header(a, 1);
     __shared__ uint64_t sm_pref[kBalancedMaxBatch + 1];
     __shared__ uint64_t sm_tmp[kThreads];
-    length_prefix<kThreads>(a.cp_dev, a.cp_host, a.S, a.batch, sm_pref, sm_tmp);
+    length_prefix<kThreads>(a.cp_dev, a.cp_host, a.S, ROPE ? 1u : 0u, a.batch, sm_pref, sm_tmp);
     if (blockIdx.x == 0) {   // publish the prefix for the combine launch
         uint64_t *hp = reinterpret_cast<uint64_t *>(a.header + kHdrPrefixWord);
         for (uint32_t i = threadIdx.x; i <= a.batch; i += kThreads) hp[i] = sm_pref[i];
@@ -536,7 +655,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs
         dst.pml = a.part_ml + slot * a.hpb * 2;
         dst.pml_hs = 2;
         dst.out = nullptr;
-        split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC>(a, b, hb, c0, c_end, dst, sm_o, sm_m, sm_l);
+        split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC, ROPE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
+                                                                 sm_l);
         x = x_end;
     }
 }
@@ -618,6 +738,11 @@ struct CombineArgs {
     uint32_t H, D, S, batch;
     const uint32_t *header;   // written by the split launch
     uint16_t *out;
+    // decode step: the new token (rotated q and k_new, v_new) joins as one
+    // more partial, and its k and v rows are appended to the caches
+    const uint16_t *q;
+    float scale_log2;         // log2(e) / sqrt(D)
+    RopeArgs rope;
 };
 
 // One workgroup per (sequence, head); thread (cg, d) handles element d of
@@ -642,9 +767,23 @@ __device__ __forceinline__ float block_max(float x, float *sm_red) {
     return M;
 }
 
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, float *sm_red) {
+    constexpr int NW = NT / 64;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    if ((threadIdx.x & 63) == 0) sm_red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float t = sm_red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t += sm_red[w];
+    return t;
+}
+
 // NT threads per workgroup: 1024 when there are few (sequence, head) pairs,
 // 256 when there are enough workgroups to fill the chip in one dispatch round.
-template <int NT>
+// STEP: the second launch of a decode step (see CombineArgs).
+template <int NT, bool STEP>
 __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
     __shared__ float sm_w[NT];
     __shared__ float sm_lc[NT];
@@ -656,12 +795,50 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
     const uint32_t b = blockIdx.y;
     const size_t bh = (size_t)b * a.H + h;
     const uint32_t tid = threadIdx.x;
+    const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
+
+    // The new token (STEP): element tid < D of its q, k_new (each with its
+    // pair partner) and v_new rows, loaded before the partials so the two
+    // sets of loads overlap.
+    float qx = 0.f, qy = 0.f, kx = 0.f, ky = 0.f;
+    uint16_t v16 = 0;
+    if constexpr (STEP) {
+        if (tid < a.D) {
+            const uint32_t pd = rope_partner(tid, a.rope);
+            const uint16_t *qrow = a.q + bh * a.D;
+            const uint16_t *krow = a.rope.k_new + bh * a.D;
+            qx = h2f(qrow[tid]);
+            qy = h2f(qrow[pd]);
+            kx = h2f(krow[tid]);
+            ky = h2f(krow[pd]);
+            v16 = a.rope.v_new[bh * a.D + tid];
+        }
+    }
+    // Its score: the rotated q against the rotated k_new, both rounded to
+    // fp16 as the split kernel and the cache hold them (base-2 units), and
+    // the append of its rows at slot pos.  Every thread must call it.
+    __shared__ float sm_dot[NT / 64];
+    auto new_token_score = [&]() -> float {
+        const uint32_t pos = valid_len(cp, a.S) - 1u;
+        float prod = 0.f;
+        if (tid < a.D) {
+            const uint16_t q16 = f2h_rne(rope_apply(qx, qy, tid, a.rope, pos));
+            const uint16_t k16 = f2h_rne(rope_apply(kx, ky, tid, a.rope, pos));
+            prod = h2f(q16) * h2f(k16);   // exact: both factors are fp16
+            const size_t row = (((size_t)b * a.S + pos) * a.H + h) * a.D + tid;
+            a.rope.k_cache[row] = k16;
+            a.rope.v_cache[row] = v16;
+        }
+        return block_sum<NT>(prod, sm_dot) * a.scale_log2;
+    };
+    float t_new = -INFINITY;
+
     uint32_t nc;              // partials of this (sequence, head)
-    const float *ml, *po;     // first partial's (m, l) and o row
-    size_t ml_cs, po_cs;      // strides between consecutive partials
+    const float *ml = nullptr, *po = nullptr;   // first partial's (m, l) and o row
+    size_t ml_cs = 0, po_cs = 0;                // strides between consecutive partials
     if (!a.header[kHdrBalanced]) {
-        const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
-        const uint32_t L = valid_len(cp, a.S);
+        // a decode step's partials cover the positions before the new token
+        const uint32_t L = valid_len(cp, a.S) - (STEP ? 1u : 0u);
         const uint32_t chunk = a.header[kHdrChunk];
         const size_t nc_stride = a.header[kHdrNcStride];
         nc = (L + chunk - 1) / chunk;
@@ -679,22 +856,27 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
         const uint64_t G = a.header[kHdrGrid] < W ? a.header[kHdrGrid] : W;   // as the split did
         const uint32_t hb = h / hpb, ho = h % hpb;
         const uint64_t L = pref[b + 1] - pref[b];
-        const uint64_t first = n_hb * pref[b] + hb * L;
-        const uint64_t last = first + L - 1;
-        const uint64_t w_first = ((first + 1) * G - 1) / W;   // W * G < 2^63
-        const uint64_t w_last = ((last + 1) * G - 1) / W;
-        nc = (uint32_t)(w_last - w_first + 1);
-        const uint64_t slot0 = w_first + (uint64_t)b * n_hb + hb;
-        ml = a.part_ml + (slot0 * hpb + ho) * 2;
-        po = a.part_o + (slot0 * hpb + ho) * a.D;
-        ml_cs = (size_t)hpb * 2;
-        po_cs = (size_t)hpb * a.D;
+        if (L == 0) {   // a decode step at position 0: no earlier positions
+            nc = 0;
+        } else {
+            const uint64_t first = n_hb * pref[b] + hb * L;
+            const uint64_t last = first + L - 1;
+            const uint64_t w_first = ((first + 1) * G - 1) / W;   // W * G < 2^63
+            const uint64_t w_last = ((last + 1) * G - 1) / W;
+            nc = (uint32_t)(w_last - w_first + 1);
+            const uint64_t slot0 = w_first + (uint64_t)b * n_hb + hb;
+            ml = a.part_ml + (slot0 * hpb + ho) * 2;
+            po = a.part_o + (slot0 * hpb + ho) * a.D;
+            ml_cs = (size_t)hpb * 2;
+            po_cs = (size_t)hpb * a.D;
+        }
     }
     const uint32_t G = NT / a.D;   // chunk groups (D <= 256)
     const uint32_t cg = tid / a.D;
     const uint32_t d = tid % a.D;
     const bool active = cg < G;
     float o = 0.f, lsum = 0.f;
+    float M_all;   // the largest m over all partials (and the new token)
 
     if (nc <= G * kCombineRegs && nc <= (uint32_t)NT) {
         // one round of loads
@@ -706,7 +888,10 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
             const uint32_t c = cg + j * G;
             ov[j] = (active && c < nc) ? po[c * po_cs + d] : 0.f;
         }
-        const float M = block_max<NT>(mc, sm_red);
+        if constexpr (STEP) t_new = new_token_score();
+        float M = block_max<NT>(mc, sm_red);
+        if constexpr (STEP) M = fmaxf(M, t_new);
+        M_all = M;
         if (tid < nc) {
             sm_w[tid] = __builtin_amdgcn_exp2f(mc - M);
             sm_lc[tid] = lc;
@@ -724,7 +909,10 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
     } else {
         float mx = -INFINITY;
         for (uint32_t c = tid; c < nc; c += NT) mx = fmaxf(mx, ml[c * ml_cs]);
-        const float M = block_max<NT>(mx, sm_red);
+        if constexpr (STEP) t_new = new_token_score();
+        float M = block_max<NT>(mx, sm_red);
+        if constexpr (STEP) M = fmaxf(M, t_new);
+        M_all = M;
         for (uint32_t t0 = 0; t0 < nc; t0 += NT) {
             const uint32_t tn = min(nc - t0, (uint32_t)NT);
             __syncthreads();   // previous tile's weights are consumed
@@ -754,6 +942,17 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
             }
         }
     }
+    if constexpr (STEP) {
+        if (tid < a.D) {   // the new token, with weight 2^(t_new - M) and l term 1
+            const float w = __builtin_amdgcn_exp2f(t_new - M_all);
+            o = fmaf(h2f(v16), w, o);
+            lsum = fmaf(1.f, w, lsum);
+        }
+    } else {
+        (void)M_all;
+        (void)t_new;
+        (void)new_token_score;
+    }
     sm_o[tid] = o;
     sm_l[tid] = lsum;
     __syncthreads();
@@ -778,6 +977,20 @@ __global__ __launch_bounds__(256) void attn_dump_fill_kernel(float *dump, const 
         const uint32_t p = (uint32_t)(i - bh * S);
         const uint32_t cp = cp_dev ? cp_dev[bh / H] : cp_host;
         if (p >= valid_len(cp, S)) dump[i] = -INFINITY;
+    }
+}
+
+// ------------------------------------------------------ standalone rotation
+
+// x, y [rows, D]; row r is at position pos[r / rows_per_pos].
+__global__ __launch_bounds__(256) void attn_rope_kernel(const uint16_t *x, uint16_t *y,
+                                                        const uint32_t *pos, uint32_t rows_per_pos,
+                                                        uint32_t D, uint64_t total, RopeArgs r) {
+    for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * 256u) {
+        const uint64_t row = i / D;
+        const uint32_t d = (uint32_t)(i - row * D);
+        y[i] = f2h_rne(rope_elem(x + row * D, d, r, pos[row / rows_per_pos]));
     }
 }
 
@@ -1004,37 +1217,37 @@ attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
 
 using SplitFn = void (*)(SplitArgs);
 
-template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED>
+template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED, bool ROPE>
 SplitFn kernel_for(bool bal) {
-    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, false>
-               : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, false>;
+    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, false, ROPE>
+               : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, false, ROPE>;
 }
 
 // Dense caches honour the unroll/prefetch knobs on the fast layouts; paged
 // caches are double-buffered with U=2 or U=4.
-template <int V, int G, int N, bool F, bool DUMP, bool PAGED>
+template <int V, int G, int N, bool F, bool DUMP, bool PAGED, bool ROPE>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
     if constexpr (PAGED) {
-        return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED>(bal)
-                             : kernel_for<V, G, N, F, 2, true, DUMP, PAGED>(bal);
+        return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, ROPE>(bal)
+                             : kernel_for<V, G, N, F, 2, true, DUMP, PAGED, ROPE>(bal);
     } else {
-        if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP, PAGED>(bal)
-                                       : kernel_for<V, G, N, F, 2, false, DUMP, PAGED>(bal);
-        if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP, PAGED>(bal)
-                                       : kernel_for<V, G, N, F, 8, false, DUMP, PAGED>(bal);
-        return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED>(bal)
-                    : kernel_for<V, G, N, F, 4, false, DUMP, PAGED>(bal);
+        if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP, PAGED, ROPE>(bal)
+                                       : kernel_for<V, G, N, F, 2, false, DUMP, PAGED, ROPE>(bal);
+        if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP, PAGED, ROPE>(bal)
+                                       : kernel_for<V, G, N, F, 8, false, DUMP, PAGED, ROPE>(bal);
+        return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, ROPE>(bal)
+                    : kernel_for<V, G, N, F, 4, false, DUMP, PAGED, ROPE>(bal);
     }
 }
 
-template <bool DUMP, bool PAGED>
+template <bool DUMP, bool PAGED, bool ROPE>
 SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     // fast paths: head_dim 64 and 128 with 16-byte rows
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP, PAGED>(k, bal);
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP, PAGED>(k, bal);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP, PAGED, ROPE>(k, bal);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP, PAGED, ROPE>(k, bal);
 #define ATTN_CASE(V, G, N, F)                                                          \
     if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
-        return kernel_for<V, G, N, F, 4, true, DUMP, PAGED>(bal);
+        return kernel_for<V, G, N, F, 4, true, DUMP, PAGED, ROPE>(bal);
     ATTN_CASE(8, 32, 1, true)
     ATTN_CASE(8, 8, 1, false)
     ATTN_CASE(8, 16, 1, false)
@@ -1071,7 +1284,7 @@ SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
 SplitFn pick_scores_split(const Layout &ly) {
 #define ATTN_SC(V, G, N, F)                                                            \
     if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
-        return attn_split_kernel<V, G, N, F, 4, true, false, false, true>;
+        return attn_split_kernel<V, G, N, F, 4, true, false, false, true, false>;
     ATTN_ALL_LAYOUTS(ATTN_SC)
 #undef ATTN_SC
     return nullptr;
@@ -1130,7 +1343,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
                            const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
                            uint32_t D, uint32_t S, float *dump, void *ws, uint16_t *out,
                            const Paging *pg, hipStream_t stream, bool *wrote_out,
-                           const uint16_t *scores_in = nullptr) {
+                           const uint16_t *scores_in = nullptr, const RopeArgs *rope = nullptr) {
     const Layout ly = scores_in ? choose_layout(D, v, v, v) : choose_layout(D, q, k, v);
     const Kind kind = pg ? Kind::paged : cp_dev ? Kind::batched : Kind::single;
     const Knobs kn = knobs(D, kind);
@@ -1138,12 +1351,17 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores_in && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
-    const SplitFn fn = scores_in ? pick_scores_split(ly)
-                     : pg ? (dump ? pick_split<true, true>(ly, kn, bal) : pick_split<false, true>(ly, kn, bal))
-                          : (dump ? pick_split<true, false>(ly, kn, bal) : pick_split<false, false>(ly, kn, bal));
+    const SplitFn fn =
+        scores_in ? pick_scores_split(ly)
+        : rope    ? pick_split<false, false, true>(ly, kn, bal)
+        : pg ? (dump ? pick_split<true, true, false>(ly, kn, bal) : pick_split<false, true, false>(ly, kn, bal))
+             : (dump ? pick_split<true, false, false>(ly, kn, bal) : pick_split<false, false, false>(ly, kn, bal));
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
-    // host current_pos: plan the exact span; device array: plan the capacity
-    const uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1;
+    // host current_pos: plan the exact span (a decode step streams one
+    // position less; at least one chunk is launched, so the header is
+    // written); device array: plan the capacity
+    uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1 - (rope ? 1u : 0u);
+    if (span == 0) span = 1;
     const Plan plan = make_plan(batch, H, D, S, span, kind);
     const WsLayout wl = workspace_layout(batch, H, D, S);
 
@@ -1165,7 +1383,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.header = static_cast<uint32_t *>(ws);
     a.part_o = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.o_off);
     a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.ml_off);
-    a.direct = (!bal && out && plan.n_chunks == 1) ? 1 : 0;
+    a.direct = (!bal && !rope && out && plan.n_chunks == 1) ? 1 : 0;
     a.out = out;
     a.dump = dump;
     a.batch = batch;
@@ -1176,6 +1394,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.max_blocks = pg ? pg->max_blocks : 0;
     a.num_blocks = pg ? pg->num_blocks : 0;
     a.page_shift = pg ? pg->page_shift : 0;
+    a.rope = rope ? *rope : RopeArgs{};
     *wrote_out = a.direct != 0;
 
     if (dump) {
@@ -1193,7 +1412,8 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
 
 attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_host,
                              uint32_t batch, uint32_t H, uint32_t D, uint32_t S, const void *ws,
-                             hipStream_t stream) {
+                             hipStream_t stream, const RopeArgs *rope = nullptr,
+                             const uint16_t *q = nullptr) {
     const WsLayout wl = workspace_layout(batch, H, D, S);
     CombineArgs c;
     c.header = static_cast<const uint32_t *>(ws);
@@ -1206,11 +1426,62 @@ attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_
     c.S = S;
     c.batch = batch;
     c.out = out;
-    if ((uint64_t)batch * H < kCombineWide)
-        hipLaunchKernelGGL(attn_combine_kernel<1024>, dim3(H, batch), dim3(1024), 0, stream, c);
-    else
-        hipLaunchKernelGGL(attn_combine_kernel<256>, dim3(H, batch), dim3(256), 0, stream, c);
+    c.q = q;
+    c.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    c.rope = rope ? *rope : RopeArgs{};
+    const bool wide = (uint64_t)batch * H < kCombineWide;
+    const dim3 grid(H, batch);
+    if (rope) {
+        if (wide) hipLaunchKernelGGL((attn_combine_kernel<1024, true>), grid, dim3(1024), 0, stream, c);
+        else hipLaunchKernelGGL((attn_combine_kernel<256, true>), grid, dim3(256), 0, stream, c);
+    } else {
+        if (wide) hipLaunchKernelGGL((attn_combine_kernel<1024, false>), grid, dim3(1024), 0, stream, c);
+        else hipLaunchKernelGGL((attn_combine_kernel<256, false>), grid, dim3(256), 0, stream, c);
+    }
     return hip_check("combine kernel launch");
+}
+
+// Rotation parameters: the frequencies base^(-2i/dims) in fp64; no pointers.
+void fill_rope(RopeArgs *r, uint32_t dims, double base, int traditional) {
+    memset(r, 0, sizeof *r);
+    r->dims = dims;
+    r->traditional = traditional ? 1u : 0u;
+    for (uint32_t i = 0; i < dims / 2; ++i) r->theta[i] = pow(base, -(2.0 * i) / (double)dims);
+}
+
+// One decode step: rotate q and k_new at pos = min(current_pos, S - 1),
+// stream positions 0..pos-1 (split launch), then merge them with the new
+// token and append its k and v rows at slot pos (combine launch).
+attn_status_t decode_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                          uint16_t *k_cache, uint16_t *v_cache, uint16_t *out,
+                          const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
+                          uint32_t D, uint32_t S, uint32_t dims, double base, int traditional,
+                          void *ws, size_t ws_bytes, void *stream) {
+    attn_status_t s = check_split(q, k_cache, v_cache, cp_dev, batch, H, D, S, nullptr);
+    if (s != ATTN_OK) return s;
+    if (!k_new || !v_new || !out) return fail(ATTN_ERR_NULL, "k_new, v_new and out must be non-NULL");
+    if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(out, 2))
+        return fail(ATTN_ERR_ALIGN, "fp16 tensors must be 2-byte aligned");
+    if ((dims & 1u) || dims > D)
+        return fail(ATTN_ERR_DIM, "rope_dims=%u must be even and <= head_dim=%u", dims, D);
+    if (!(base > 0.0) || !isfinite(base))
+        return fail(ATTN_ERR_DIM, "rope_base must be positive and finite");
+    if (!cp_dev && cp_host >= S)
+        return fail(ATTN_ERR_DIM, "current_pos=%u must be < seq_len=%u (the new token's slot)", cp_host, S);
+    s = check_workspace(ws, ws_bytes, batch, H, D, S);
+    if (s != ATTN_OK) return s;
+    RopeArgs r;
+    fill_rope(&r, dims, base, traditional);
+    r.k_new = k_new;
+    r.v_new = v_new;
+    r.k_cache = k_cache;
+    r.v_cache = v_cache;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool wrote = false;
+    s = launch_split(q, k_cache, v_cache, cp_dev, cp_host, batch, H, D, S, nullptr, ws, nullptr,
+                     nullptr, st, &wrote, nullptr, &r);
+    if (s != ATTN_OK) return s;
+    return launch_combine(out, cp_dev, cp_host, batch, H, D, S, ws, st, &r, q);
 }
 
 attn_status_t decode_full(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
@@ -1406,6 +1677,53 @@ attn_status_t attn_pv_f16(const uint16_t *scores, const uint16_t *v_cache, uint1
                      seq_len, nullptr, workspace, out, nullptr, st, &wrote, scores);
     if (s != ATTN_OK || wrote) return s;
     return launch_combine(out, nullptr, current_pos, 1, n_heads, head_dim, seq_len, workspace, st);
+}
+
+attn_status_t attn_decode_step_f16(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                   uint16_t *k_cache, uint16_t *v_cache, uint16_t *out,
+                                   uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                                   uint32_t current_pos, uint32_t rope_dims, double rope_base,
+                                   int rope_traditional, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    return decode_step(q, k_new, v_new, k_cache, v_cache, out, nullptr, current_pos, 1, n_heads,
+                       head_dim, seq_len, rope_dims, rope_base, rope_traditional, workspace,
+                       workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_step_f16_batched(const uint16_t *q, const uint16_t *k_new,
+                                           const uint16_t *v_new, uint16_t *k_cache,
+                                           uint16_t *v_cache, uint16_t *out,
+                                           const uint32_t *current_pos, uint32_t batch,
+                                           uint32_t n_heads, uint32_t head_dim, uint32_t capacity,
+                                           uint32_t rope_dims, double rope_base,
+                                           int rope_traditional, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    if (!current_pos) return fail(ATTN_ERR_NULL, "current_pos must be non-NULL");
+    return decode_step(q, k_new, v_new, k_cache, v_cache, out, current_pos, 0, batch, n_heads,
+                       head_dim, capacity, rope_dims, rope_base, rope_traditional, workspace,
+                       workspace_bytes, stream);
+}
+
+attn_status_t attn_rope_f16(const uint16_t *x, uint16_t *out, const uint32_t *positions,
+                            uint32_t batch, uint32_t n_heads, uint32_t head_dim, uint32_t rope_dims,
+                            double rope_base, int rope_traditional, void *stream) {
+    if (!x || !out || !positions) return fail(ATTN_ERR_NULL, "x, out and positions must be non-NULL");
+    attn_status_t s = check_sizes(batch, n_heads, head_dim, 1);
+    if (s != ATTN_OK) return s;
+    if (!aligned(x, 2) || !aligned(out, 2)) return fail(ATTN_ERR_ALIGN, "fp16 tensors must be 2-byte aligned");
+    if (!aligned(positions, 4)) return fail(ATTN_ERR_ALIGN, "positions must be 4-byte aligned");
+    if ((rope_dims & 1u) || rope_dims > head_dim)
+        return fail(ATTN_ERR_DIM, "rope_dims=%u must be even and <= head_dim=%u", rope_dims, head_dim);
+    if (!(rope_base > 0.0) || !isfinite(rope_base))
+        return fail(ATTN_ERR_DIM, "rope_base must be positive and finite");
+    RopeArgs r;
+    fill_rope(&r, rope_dims, rope_base, rope_traditional);
+    const uint64_t total = (uint64_t)batch * n_heads * head_dim;
+    const uint64_t blocks = cdiv(total, 256) < 8192 ? cdiv(total, 256) : 8192;
+    hipLaunchKernelGGL(attn_rope_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), x, out, positions, n_heads, head_dim,
+                       total, r);
+    return hip_check("rope kernel launch");
 }
 
 const char *attn_status_string(attn_status_t status) {

@@ -209,6 +209,69 @@ attn_status_t attn_pv_f16(const uint16_t *scores, const uint16_t *v_cache, uint1
                           uint32_t current_pos, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/*
+ * One decode step: rotary embedding of the new token's query and key, the
+ * append of its key and value rows to the caches, and attention over the
+ * cache including the new row, in two launches.  The rotation is the one the
+ * page "Tutorial 16: Writing Custom Metal Kernels" describes (section "5.
+ * Example: Fused RoPE Kernel": FastRoPE(dims, base, traditional) applied at
+ * a per-sequence offset); the cache layout, current_pos and the attention
+ * are those of the page "Developing Apple Metal Kernels in Rust - A Deep
+ * Dive Through Attention" (section "The MSL, briefly").
+ *
+ * For each sequence, with pos = current_pos (single sequence) or
+ * min(current_pos[b], capacity - 1) (batch):
+ *   rot(x)[2 values of pair i] = 2D rotation by pos * rope_base^(-2i/rope_dims)
+ *       of pair i, i < rope_dims/2; pair i is (i, i + rope_dims/2), or
+ *       (2i, 2i+1) when rope_traditional != 0; values at index >= rope_dims
+ *       are unchanged.  The rotated q and k_new are rounded to fp16 (nearest
+ *       even), as a rotated tensor is stored.
+ *   k_cache[pos] = rot(k_new), v_cache[pos] = v_new          (the append)
+ *   out = attention of rot(q) over cache positions 0..pos, as attn_decode_f16
+ * Rows before pos must already hold rotated keys.  Positions after pos are
+ * neither read nor written.
+ *   q, k_new, v_new   [n_heads, head_dim] fp16 (batch: [batch, n_heads, head_dim])
+ *   k_cache, v_cache  [seq_len, n_heads, head_dim] fp16 (batch: [batch,
+ *                     capacity, n_heads, head_dim]); row pos is written
+ *   out               [n_heads, head_dim] fp16 (batch: [batch, n_heads, head_dim])
+ *   current_pos       single: host value, must be < seq_len (ATTN_ERR_DIM
+ *                     otherwise); batch: DEVICE [batch] uint32, values >=
+ *                     capacity use slot capacity - 1
+ *   rope_dims         even, <= head_dim; 0 rotates nothing (append + attend)
+ *   rope_base         > 0 and finite (10000 on the page)
+ *   workspace         >= attn_decode_workspace_bytes(batch, n_heads, head_dim, seq_len)
+ * q, k_new, v_new and out must not overlap the caches or each other.
+ * Arithmetic: angle and its reduction modulo pi/2 in fp64, cos/sin and the
+ * rotation in fp32; the rest as attn_decode_f16.
+ */
+attn_status_t attn_decode_step_f16(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                                   uint16_t *k_cache, uint16_t *v_cache, uint16_t *out,
+                                   uint32_t n_heads, uint32_t head_dim, uint32_t seq_len,
+                                   uint32_t current_pos, uint32_t rope_dims, double rope_base,
+                                   int rope_traditional, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+attn_status_t attn_decode_step_f16_batched(const uint16_t *q, const uint16_t *k_new,
+                                           const uint16_t *v_new, uint16_t *k_cache,
+                                           uint16_t *v_cache, uint16_t *out,
+                                           const uint32_t *current_pos, uint32_t batch,
+                                           uint32_t n_heads, uint32_t head_dim, uint32_t capacity,
+                                           uint32_t rope_dims, double rope_base,
+                                           int rope_traditional, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
+/*
+ * The rotation alone (the page's FastRoPE with one offset per batch entry):
+ * row (b, h) of x turns at position positions[b], as rot() above, and is
+ * rounded to fp16.
+ *   x, out     [batch, n_heads, head_dim] fp16; out must not overlap x
+ *   positions  DEVICE [batch] uint32, any value
+ *   rope_dims, rope_base, rope_traditional  as for attn_decode_step_f16
+ */
+attn_status_t attn_rope_f16(const uint16_t *x, uint16_t *out, const uint32_t *positions,
+                            uint32_t batch, uint32_t n_heads, uint32_t head_dim, uint32_t rope_dims,
+                            double rope_base, int rope_traditional, void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(attn_status_t status);
 

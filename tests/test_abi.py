@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -161,3 +161,47 @@ def test_two_dispatch_rejects_bad_arguments(lib):
     assert lib.attn_pv_f16(FAKE, FAKE, None, 4, 64, 128, 5, FAKE, 1 << 30, None) == NULL
     assert lib.attn_pv_f16(FAKE, FAKE, FAKE, 4, 64, 128, 5, None, 1 << 30, None) == WS
     assert lib.attn_pv_f16(FAKE, FAKE + 1, FAKE, 4, 64, 128, 5, FAKE, 1 << 30, None) == ALIGN
+
+
+def test_decode_step_rejects_bad_arguments(lib):
+    f = lib.attn_decode_step_f16
+    ok = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, out=FAKE, H=4, D=64, S=128, cp=100,
+              dims=64, base=10000.0, trad=0, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["out"], a["H"], a["D"], a["S"],
+                 a["cp"], a["dims"], a["base"], a["trad"], a["ws"], a["wsb"], None)
+
+    for name in ("q", "kn", "vn", "kc", "vc", "out"):
+        assert call(**{name: None}) == NULL, name
+        assert call(**{name: FAKE + 1}) == ALIGN, name
+    assert call(dims=63) == DIM                     # odd
+    assert call(dims=66) == DIM                     # past head_dim
+    assert call(base=0.0) == DIM
+    assert call(base=-2.0) == DIM
+    assert call(base=float("nan")) == DIM
+    assert call(base=float("inf")) == DIM
+    assert call(cp=128) == DIM                      # the slot must exist
+    assert b"slot" in lib.attn_last_error()
+    assert call(D=0) == DIM
+    assert call(ws=None) == WS
+    assert call(wsb=16) == WS
+    g = lib.attn_decode_step_f16_batched
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 4, 64, 128, 64, 1e4, 0, FAKE, 1 << 30,
+             None) == NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 2, 4, 64, 128, 64, 1e4, 0, FAKE,
+             1 << 30, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 128, 65, 1e4, 0, FAKE, 1 << 30,
+             None) == DIM
+
+
+def test_rope_rejects_bad_arguments(lib):
+    f = lib.attn_rope_f16
+    assert f(None, FAKE, FAKE, 2, 4, 64, 64, 1e4, 0, None) == NULL
+    assert f(FAKE, FAKE, None, 2, 4, 64, 64, 1e4, 0, None) == NULL
+    assert f(FAKE, FAKE + 1, FAKE, 2, 4, 64, 64, 1e4, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE + 2, 2, 4, 64, 64, 1e4, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, 2, 4, 64, 3, 1e4, 0, None) == DIM
+    assert f(FAKE, FAKE, FAKE, 2, 4, 64, 64, 0.0, 0, None) == DIM
+    assert f(FAKE, FAKE, FAKE, 0, 4, 64, 64, 1e4, 0, None) == DIM
