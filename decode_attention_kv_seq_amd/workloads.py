@@ -119,6 +119,26 @@ def _normal_f16(seed: int, stream: int, index: torch.Tensor, sigma: float) -> to
     return (c * scale).to(torch.float16)
 
 
+def normal_f32(seed: int, stream: int, index: torch.Tensor, sigma: float) -> torch.Tensor:
+    """The same values as ``normal_f16`` before its final rounding: fp32."""
+    if index.device.type == "cpu" and index.numel() > _CPU_CHUNK:
+        flat = index.reshape(-1)
+        out = torch.empty(flat.shape, dtype=torch.float32)
+        for lo in range(0, flat.numel(), _CPU_CHUNK):
+            out[lo:lo + _CPU_CHUNK] = _normal_f32(seed, stream, flat[lo:lo + _CPU_CHUNK], sigma)
+        return out.view(index.shape)
+    return _normal_f32(seed, stream, index, sigma)
+
+
+def _normal_f32(seed: int, stream: int, index: torch.Tensor, sigma: float) -> torch.Tensor:
+    w = words(seed, stream, index)
+    total = torch.bitwise_and(w, 0xFFFF)
+    for shift in (16, 32, 48):
+        total = total + torch.bitwise_and(torch.bitwise_right_shift(w, shift), 0xFFFF)
+    c = (total - IRWIN_HALL_CENTRE).to(torch.float32)
+    return c * torch.tensor(sigma / IRWIN_HALL_SD, dtype=torch.float32, device=index.device)
+
+
 def uniform_u64(seed: int, stream: int, index: torch.Tensor) -> torch.Tensor:
     return words(seed, stream, index)
 
@@ -342,3 +362,82 @@ def page_pattern_f16(n: int) -> torch.Tensor:
     rounded to fp16 (the page converts an f32 value with f16::from_f32)."""
     i = torch.arange(n, dtype=torch.int64)
     return ((i % 10).to(torch.float32) * 0.1).to(torch.float16)
+
+
+# ------------------------------------------------------------ row softmax
+# The softmax step on its own (the Foundry notes' fm_softmax over a
+# [rows, cols] fp32 tensor) on the score matrices of the decode workloads:
+# row r is (sequence r // n_heads, head r % n_heads), column p a cache
+# position.  Values are seeded stand-ins for scaled scores: approximately
+# N(0, sigma^2), the decode workload's spike positions scaled the same way,
+# and -inf after each row's last valid position (the masked score of the
+# page's attention_qk_f16).
+
+STREAM_SCORES = 4
+
+
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    of: str          # the decode workload whose shape, lengths and spikes it takes
+    seed: int
+    sigma: float
+
+    @property
+    def decode(self) -> Workload:
+        return WORKLOADS[self.of]
+
+    @property
+    def rows(self) -> int:
+        return self.decode.batch * self.decode.n_heads
+
+    @property
+    def cols(self) -> int:
+        return self.decode.seq_len
+
+    def row_lengths(self) -> torch.Tensor:
+        """Valid (not -inf) columns of each row, int64 [rows] (host)."""
+        d = self.decode
+        lens = torch.clamp(d.positions(), max=d.seq_len - 1) + 1
+        return lens.repeat_interleave(d.n_heads)
+
+    def bytes_moved(self) -> int:
+        """Algorithmic bytes of one softmax: x read once, out written once."""
+        return self.rows * self.cols * 4 * 2
+
+
+def score_rows(w: SoftmaxWorkload, rows, device="cpu") -> torch.Tensor:
+    """fp32 [len(rows), cols]: the given rows of the workload's input."""
+    rows = torch.as_tensor(rows, dtype=torch.int64)
+    cols = w.cols
+    idx = rows.to(device)[:, None] * cols + torch.arange(cols, dtype=torch.int64, device=device)[None, :]
+    x = normal_f32(w.seed, STREAM_SCORES, idx, w.sigma)
+    d = w.decode
+    if d.spike_fraction > 0:
+        sp = d.spike_rows().to(device)
+        x[:, sp] = x[:, sp] * d.spike_scale
+    lens = w.row_lengths()[rows].to(device)
+    x[torch.arange(cols, device=device)[None, :] >= lens[:, None]] = -math.inf
+    return x
+
+
+def make_scores(w: SoftmaxWorkload, device="cpu", chunk_rows: int = 256) -> torch.Tensor:
+    """The whole input [rows, cols] fp32."""
+    x = torch.empty((w.rows, w.cols), dtype=torch.float32, device=device)
+    for lo in range(0, w.rows, chunk_rows):
+        hi = min(w.rows, lo + chunk_rows)
+        x[lo:hi] = score_rows(w, torch.arange(lo, hi), device)
+    return x
+
+
+SOFTMAX_WORKLOADS = {
+    sw.name: sw for sw in [
+        # the seq-32768 scores: q of sigma 2 gives scaled scores of sigma ~2
+        SoftmaxWorkload("sm_h32_s32768_masked", of="h32_d128_s32768_cp20000_garbage",
+                        seed=13, sigma=2.0),
+        SoftmaxWorkload("sm_b64_h32_cap8192_ragged", of="b64_h32_d128_cap8192_ragged",
+                        seed=14, sigma=1.0),
+        SoftmaxWorkload("sm_h64_s131072_spikes", of="h64_d64_s131072_spikes", seed=15,
+                        sigma=1.0),
+    ]
+}

@@ -11,7 +11,8 @@ Through Attention", section "The MSL, briefly" (kernels attention_qk_f16 and
 attention_pv_f16).  The decode step around it (rotary embedding of q and of
 the new key, the append of the new row, then attention) follows the page
 "Tutorial 16: Writing Custom Metal Kernels", section "5. Example: Fused RoPE
-Kernel", for the rotation.
+Kernel", for the rotation.  The row softmax on its own follows the Foundry
+notes' fm_softmax (section "API Reference").
 """
 from __future__ import annotations
 
@@ -64,6 +65,8 @@ class OracleLib:
         lib.oracle_rope.argtypes = [u16p, u32, u32, u32, ctypes.c_double, ctypes.c_int,
                                     ctypes.POINTER(ctypes.c_uint32), f64p]
         lib.oracle_rope.restype = ctypes.c_int
+        lib.oracle_softmax_rows.argtypes = [ctypes.POINTER(ctypes.c_float), u32, u32, f64p]
+        lib.oracle_softmax_rows.restype = ctypes.c_int
         self.path = path
         self.lib = lib
 
@@ -190,6 +193,34 @@ class OracleLib:
         out, _, _ = self.decode(q16, k_cache, v_cache, pos, threads=threads)
         return {"out": out, "q_rot": q_rot, "k_rot": k_rot, "q16": q16, "k16": k16, "pos": pos}
 
+    def softmax_rows(self, x, threads: int = 1) -> np.ndarray:
+        """Row softmax of an fp32 [rows, cols] array (numpy or torch) -> float64."""
+        if hasattr(x, "detach"):
+            x = x.detach().cpu().contiguous().numpy()
+        a = np.ascontiguousarray(x)
+        if a.dtype != np.float32 or a.ndim != 2:
+            raise TypeError("x must be a float32 [rows, cols] array")
+        rows, cols = a.shape
+        out = np.empty((rows, cols), dtype=np.float64)
+        fp = ctypes.POINTER(ctypes.c_float)
+
+        def run(lo_hi):
+            lo, hi = lo_hi
+            if hi > lo:
+                rc = self.lib.oracle_softmax_rows(a[lo:hi].ctypes.data_as(fp), hi - lo, cols,
+                                                  out[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+                if rc != 0:
+                    raise ValueError("oracle_softmax_rows rejected its arguments")
+
+        threads = max(1, min(int(threads), rows))
+        bounds = [(rows * i // threads, rows * (i + 1) // threads) for i in range(threads)]
+        if threads == 1:
+            run(bounds[0])
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(run, bounds))
+        return out
+
     def decode_batched(self, q, k, v, current_pos, *, want_scores=False, threads: int = 1):
         """Independent sequences: q [B, H, D], k/v [B, S, H, D], current_pos [B].
 
@@ -245,3 +276,7 @@ def rope(x, positions, **kw):
 
 def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, **kw):
     return load().decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, **kw)
+
+
+def softmax_rows(x, **kw):
+    return load().softmax_rows(x, **kw)

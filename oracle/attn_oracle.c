@@ -20,7 +20,8 @@
  *
  * The decode step around it (the rotary embedding of the page "Tutorial 16:
  * Writing Custom Metal Kernels", and the fp16 rounding of what is stored) is
- * at the end of the file: oracle_rope and oracle_double_to_half.
+ * at the end of the file: oracle_rope and oracle_double_to_half.  So is the
+ * softmax step on its own (oracle_softmax_rows, the Foundry notes' fm_softmax).
  *
  * Layouts (same section): Q and output [n_heads, head_dim]; K and V caches
  * [seq_len, n_heads, head_dim], element (p,h,i) at (p*n_heads + h)*head_dim + i;
@@ -284,6 +285,41 @@ int oracle_rope(const uint16_t *x, uint32_t n_rows, uint32_t head_dim, uint32_t 
             o[ia] = a * c - b * s;
             o[ib] = a * s + b * c;
         }
+    }
+    return 0;
+}
+
+/*
+ * Softmax over the last dimension of a [rows, cols] fp32 tensor, as the
+ * Foundry notes' fm_softmax (section "API Reference", custom compute kernels:
+ * x [rows, cols] -> out [rows, cols]) computes it, with the same max-shifted
+ * form as the page "Developing Apple Metal Kernels in Rust - A Deep Dive
+ * Through Attention" (section "The MSL, briefly", attention_pv_f16):
+ *   m = max_c x[r,c];  z = sum_c exp(x[r,c] - m);  out[r,c] = exp(x[r,c] - m) / z.
+ * Inputs are converted to fp64 exactly.  A -inf entry gets exactly 0.  The
+ * plain definition is kept where it breaks down: a row of -inf only gives NaN
+ * (m = -inf), and a NaN anywhere in a row makes the row NaN.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_softmax_rows(const float *x, uint32_t rows, uint32_t cols, double *out)
+{
+    if (!x || !out || cols == 0)
+        return -1;
+    const size_t C = cols;
+    for (size_t r = 0; r < rows; ++r) {
+        const float *row = x + r * C;
+        double *o = out + r * C;
+        double m = (double)row[0];
+        for (size_t c = 1; c < C; ++c)
+            if ((double)row[c] > m)
+                m = (double)row[c];
+        double z = 0.0;
+        for (size_t c = 0; c < C; ++c) {
+            o[c] = exp((double)row[c] - m);
+            z += o[c];
+        }
+        for (size_t c = 0; c < C; ++c)
+            o[c] = o[c] / z;
     }
     return 0;
 }

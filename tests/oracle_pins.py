@@ -652,6 +652,98 @@ def pin_decode_step_against_torch(orc):
         assert np.allclose(r["out"], ref[:, 0, :].numpy(), rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------- row softmax
+# The Foundry notes' fm_softmax (section "API Reference": x [rows, cols] ->
+# out [rows, cols]), in the max-shifted form of the page "Developing Apple
+# Metal Kernels in Rust - A Deep Dive Through Attention" ("The MSL, briefly").
+
+
+def pin_softmax_rows_sum_to_one_and_match_torch(orc):
+    """Rows sum to 1, and every value equals torch's own float64 softmax."""
+    rng = _rng(40)
+    for rows, cols, sigma in [(1, 1, 1.0), (3, 7, 1.0), (16, 1000, 3.0), (4, 5000, 8.0)]:
+        x = (rng.standard_normal((rows, cols)) * sigma).astype(np.float32)
+        out = orc.softmax_rows(x)
+        assert np.allclose(out.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+        ref = torch.softmax(torch.from_numpy(x.astype(np.float64)), dim=1).numpy()
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-300), (rows, cols)
+
+
+def pin_softmax_two_values_closed_form(orc):
+    """[a, b] -> [1/(1+e^(b-a)), 1/(1+e^(a-b))]; [x, x] -> [1/2, 1/2] exactly."""
+    for a, b in [(0.0, 0.0), (1.0, 3.0), (-20.0, 5.5), (100.0, 100.25)]:
+        out = orc.softmax_rows(np.array([[a, b]], np.float32))[0]
+        w0 = 1.0 / (1.0 + math.exp(b - a))
+        assert abs(out[0] - w0) < 1e-15 and abs(out[1] - (1.0 - w0)) < 1e-15, (a, b, out)
+    assert np.array_equal(orc.softmax_rows(np.full((1, 2), 7.5, np.float32))[0], [0.5, 0.5])
+
+
+def pin_softmax_uniform_row(orc):
+    """Equal values give exactly 1/cols for power-of-two lengths."""
+    for cols in (1, 2, 64, 4096):
+        out = orc.softmax_rows(np.full((2, cols), -3.25, np.float32))
+        assert np.all(out == 1.0 / cols), cols
+
+
+def pin_softmax_shift_invariant_exactly(orc):
+    """Adding the same integer to every entry of an integer-valued row leaves
+    x - max unchanged, so the output is bitwise unchanged."""
+    rng = _rng(41)
+    x = rng.integers(-40, 40, (5, 300)).astype(np.float32)
+    base = orc.softmax_rows(x)
+    for c in (1.0, -1000.0, 65536.0):
+        assert np.array_equal(orc.softmax_rows(x + np.float32(c)), base), c
+
+
+def pin_softmax_large_values_stay_finite(orc):
+    """Entries in the thousands: the max shift is there (exp(1000) overflows)."""
+    x = np.array([[1000.0, 999.0, 998.0], [3e4, 3e4, -3e4]], np.float32)
+    out = orc.softmax_rows(x)
+    assert np.all(np.isfinite(out))
+    e = np.exp([0.0, -1.0, -2.0])
+    assert np.allclose(out[0], e / e.sum(), rtol=1e-15, atol=0)
+    assert np.array_equal(out[1], [0.5, 0.5, 0.0])
+
+
+def pin_softmax_masked_entries(orc):
+    """-inf entries weigh exactly 0 and leave the rest as the shorter row;
+    a row of -inf only is NaN (the plain definition: m = -inf)."""
+    rng = _rng(42)
+    x = rng.standard_normal((3, 50)).astype(np.float32)
+    xm = x.copy()
+    xm[:, 30:] = -np.inf
+    out = orc.softmax_rows(xm)
+    assert np.all(out[:, 30:] == 0.0)
+    assert np.array_equal(out[:, :30], orc.softmax_rows(np.ascontiguousarray(x[:, :30])))
+    nan_row = orc.softmax_rows(np.full((1, 4), -np.inf, np.float32))
+    assert np.all(np.isnan(nan_row))
+
+
+def pin_softmax_rows_are_independent_and_row_major(orc):
+    """Row r of the output depends on row r of x only, laid out row-major."""
+    rng = _rng(43)
+    x = rng.standard_normal((6, 37)).astype(np.float32)
+    whole = orc.softmax_rows(x)
+    for r in range(6):
+        assert np.array_equal(whole[r], orc.softmax_rows(np.ascontiguousarray(x[r:r + 1]))[0])
+    col = orc.softmax_rows(np.ascontiguousarray(x[:, :1]))
+    assert np.all(col == 1.0)
+
+
+def pin_softmax_equals_decode_weights(orc):
+    """The decode oracle's softmax weights are the row softmax of its scores
+    (two separately written routines): scores rounded to fp32 first, so they
+    agree to the fp32 rounding of the scores (|ds| <= 2^-24 |s|)."""
+    rng = _rng(44)
+    S, H, D, cp = 200, 3, 64, 150
+    q, k, v = _randn_f16(rng, (H, D)), _randn_f16(rng, (S, H, D)), _randn_f16(rng, (S, H, D))
+    _, s, w = orc.decode(q, k, v, cp, want_scores=True, want_weights=True)
+    out = orc.softmax_rows(s.astype(np.float32))
+    bound = w * (2.0 ** -23) * (np.abs(s[:, : cp + 1]).max() + 1) * 4
+    assert np.all(out[:, cp + 1:] == 0.0)
+    assert np.all(np.abs(out[:, : cp + 1] - w[:, : cp + 1]) <= bound[:, : cp + 1] + 1e-300)
+
+
 ALL_PINS = [
     pin_half_decoder_all_patterns,
     pin_one_hot_query_scores,
@@ -685,4 +777,12 @@ ALL_PINS = [
     pin_rope_traditional_is_interleaved_half_split,
     pin_decode_step_first_position,
     pin_decode_step_against_torch,
+    pin_softmax_rows_sum_to_one_and_match_torch,
+    pin_softmax_two_values_closed_form,
+    pin_softmax_uniform_row,
+    pin_softmax_shift_invariant_exactly,
+    pin_softmax_large_values_stay_finite,
+    pin_softmax_masked_entries,
+    pin_softmax_rows_are_independent_and_row_major,
+    pin_softmax_equals_decode_weights,
 ]

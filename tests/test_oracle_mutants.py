@@ -42,6 +42,11 @@ MUTANTS = {
     "rope_position_off_by_one": ("(double)pos[r] * theta", "(double)(pos[r] + 1) * theta"),
     "rope_tail_zeroed": ("o[d] = oracle_half_to_double(row[d]);", "o[d] = 0.0;"),
     "rope_partner_wrong": ("(size_t)i + half;", "(size_t)i + half - (i > 0);"),
+    "softmax_min_for_max": ("            if ((double)row[c] > m)\n", "            if ((double)row[c] < m)\n"),
+    "softmax_no_shift": ("o[c] = exp((double)row[c] - m);", "o[c] = exp((double)row[c]);"),
+    "softmax_not_normalised": ("o[c] = o[c] / z;", "o[c] = o[c];"),
+    "softmax_column_major": ("const float *row = x + r * C;", "const float *row = x + r;"),
+    "softmax_last_column_dropped": ("        for (size_t c = 0; c < C; ++c) {\n            o[c] = exp(", "        for (size_t c = 0; c + 1 < C; ++c) {\n            o[c] = exp("),
 }
 
 

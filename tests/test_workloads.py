@@ -75,3 +75,23 @@ def test_batched_positions_and_bytes():
     w5 = wl.WORKLOADS["h64_d64_s131072_spikes"]
     assert w5.kv_bytes_read() == 2 * 131072 * 64 * 64 * 2
     assert len(w5.spike_rows()) == 1311
+
+
+def test_softmax_workloads_follow_their_decode_workloads():
+    """Score-matrix inputs: shape from the decode workload, -inf exactly after
+    each row's valid length, spike columns scaled, rows regenerated alike."""
+    from decode_attention_kv_seq_amd import workloads as wl
+    for name, w in wl.SOFTMAX_WORKLOADS.items():
+        d = w.decode
+        x = wl.make_scores(w)
+        assert tuple(x.shape) == (d.batch * d.n_heads, d.seq_len), name
+        lens = w.row_lengths()
+        cols = torch.arange(w.cols)[None, :]
+        assert torch.equal(torch.isinf(x), cols >= lens[:, None]), name
+        assert not torch.isnan(x).any()
+        some = torch.tensor([0, w.rows // 2, w.rows - 1])
+        assert torch.equal(wl.score_rows(w, some), x[some]), name
+        if d.spike_fraction > 0:
+            sp = d.spike_rows()
+            assert x[:, sp].abs().mean() > 4 * x.abs().mean() / 2
+    assert wl.SOFTMAX_WORKLOADS["sm_h32_s32768_masked"].row_lengths().unique().tolist() == [20001]
