@@ -52,7 +52,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default=None, help="workload name (default: the 131072-position cache)")
+    p.add_argument("--workload", default=None,
+                   help="workload name (default: the 131072-position cache); an sm_* name "
+                        "times the row softmax on that decode workload's score matrix")
     p.add_argument("--rotate", type=int, default=0,
                    help="K/V copies to cycle through (0: enough for >= 2 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -133,6 +135,99 @@ def load_traffic(workload: str):
     return int(fields["bytes_per_launch"])
 
 
+SOFTMAX_METRIC = "row-softmax HBM GB/s (fp32 x read + out written) and % of MI355X HBM peak"
+
+
+def run_softmax(args, name):
+    """The row softmax alone on a decode workload's score matrix: x read once
+    and out written once per call (8 bytes per element) over the call's time."""
+    import numpy as np
+    import torch
+    import decode_attention_kv_seq_amd as ad
+    from decode_attention_kv_seq_amd import workloads as wl
+    import oracle
+
+    w = wl.SOFTMAX_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = ad.load_library()
+    x0 = wl.make_scores(w, dev)
+    per_copy = 2 * x0.numel() * 4
+    copies = args.rotate or max(1, math.ceil((2 << 30) / per_copy))
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    outs = [torch.empty_like(x0) for _ in range(copies)]
+    ws = torch.empty(ad.softmax_workspace_bytes(w.rows, w.cols), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    vp = ctypes.c_void_p
+    call_args = [(vp(xs[r].data_ptr()), vp(outs[r].data_ptr()), w.rows, w.cols, vp(ws.data_ptr()),
+                  ws.numel(), sh) for r in range(copies)]
+    fn = lib.attn_softmax_f32
+
+    def check(rc):
+        if rc != 0:
+            raise ad.AttnError(rc, lib.attn_last_error().decode())
+
+    torch.cuda.synchronize()
+    log("inputs: %s [%d, %d] fp32, %d cop%s of %.1f MiB (x + out)" % (
+        name, w.rows, w.cols, copies, "y" if copies == 1 else "ies", per_copy / 2 ** 20))
+    for i in range(args.warmup):
+        check(fn(*call_args[i % copies]))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        check(fn(*call_args[i % copies]))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = w.bytes_moved()
+    value = nbytes / (ms * 1e-3) / 1e9
+    log("softmax %.2f us -> %.1f GB/s (%.1f%% of 8 TB/s)" % (ms * 1e3, value, 100 * value / HBM_PEAK_GBS))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        orc = oracle.load()
+        cores = min(os.cpu_count() or 1, 16)
+        xh = x0.cpu().numpy()
+        t0 = time.perf_counter()
+        orc.softmax_rows(xh[: max(1, w.rows // 8)])
+        est = (time.perf_counter() - t0) * 8
+        reps = max(1, int(args.cpu_seconds * cores / max(est, 1e-6) / cores))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            orc.softmax_rows(xh, threads=cores)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+               "kind": "oracle",
+               "sample": "the whole [%d, %d] input, %d time%s, %.2f s on %d threads (fp64 C oracle)"
+                         % (w.rows, w.cols, reps, "" if reps == 1 else "s", dt, cores)}
+        log("cpu baseline: %s" % json.dumps(cpu))
+
+    line = {
+        "metric": SOFTMAX_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "rows": w.rows, "cols": w.cols, "of": w.of,
+                   "bytes_per_call": nbytes, "copies_rotated": copies,
+                   "us_per_call": round(ms * 1e3, 3),
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -145,6 +240,8 @@ def main():
     from decode_attention_kv_seq_amd import workloads as wl
 
     name = args.workload or wl.BENCH_WORKLOAD
+    if name in wl.SOFTMAX_WORKLOADS:
+        return run_softmax(args, name)
     w = wl.WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -79,6 +79,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_step_f16_batched.restype = ctypes.c_int
     lib.attn_rope_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, f64, i32, vp]
     lib.attn_rope_f16.restype = ctypes.c_int
+    lib.attn_softmax_workspace_bytes.argtypes = [u32, u32]
+    lib.attn_softmax_workspace_bytes.restype = sz
+    lib.attn_softmax_f32.argtypes = [vp, vp, u32, u32, vp, sz, vp]
+    lib.attn_softmax_f32.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -407,4 +411,32 @@ def rope(x, positions, *, rope_dims=None, rope_base: float = 10000.0, traditiona
     dims, base = _rope_params(rope_dims, D, rope_base)
     _check(lib.attn_rope_f16(_ptr(x), _ptr(out), _ptr(pos), B, H, D, dims, base,
                              1 if traditional else 0, _stream_handle(stream)))
+    return out
+
+
+def softmax_workspace_bytes(rows: int, cols: int) -> int:
+    return int(load_library().attn_softmax_workspace_bytes(rows, cols))
+
+
+def softmax(x, *, out=None, workspace=None, stream=None):
+    """Row softmax of an fp32 GPU tensor [rows, cols] (last dimension).
+    ``out`` may be ``x`` itself."""
+    lib = load_library()
+    _req(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", torch.float32, x.device)
+    if tuple(out.shape) != (rows, cols):
+        raise ValueError("out must be [rows, cols]")
+    if workspace is None:
+        n = softmax_workspace_bytes(rows, cols)
+        if n == 0:
+            raise ValueError("invalid sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _check(lib.attn_softmax_f32(_ptr(x), _ptr(out), rows, cols, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(),
+                                _stream_handle(stream)))
     return out

@@ -272,6 +272,29 @@ attn_status_t attn_rope_f16(const uint16_t *x, uint16_t *out, const uint32_t *po
                             uint32_t batch, uint32_t n_heads, uint32_t head_dim, uint32_t rope_dims,
                             double rope_base, int rope_traditional, void *stream);
 
+/*
+ * Softmax over the last dimension of an fp32 [rows, cols] tensor, the softmax
+ * step on its own: the Foundry notes' fm_softmax (section "API Reference":
+ * x [rows, cols] -> out [rows, cols]), computed max-shifted as the page
+ * "Developing Apple Metal Kernels in Rust - A Deep Dive Through Attention"
+ * does inside attention_pv_f16 (section "The MSL, briefly"):
+ *   out[r,c] = exp(x[r,c] - m_r) / sum_c' exp(x[r,c'] - m_r),  m_r = max_c x[r,c]
+ * A -inf entry gets exactly 0.  A row of -inf only, or a row holding a NaN,
+ * gives NaN throughout, as the definition does.
+ *   x, out     DEVICE [rows, cols] fp32, row-major, 4-byte aligned (16-byte
+ *              aligned with cols % 4 == 0 takes 16-byte loads); out may be x
+ *              itself (in place), otherwise they must not overlap
+ *   workspace  >= attn_softmax_workspace_bytes(rows, cols) bytes, 16-byte
+ *              aligned (per-chunk statistics for long rows; no initialisation)
+ * Arithmetic: fp32; exp(t) as the hardware 2^(t log2 e); fixed reduction
+ * order, so results are bitwise reproducible.  Returns ATTN_ERR_DIM for a
+ * zero size or when rows * ceil(cols / 4096) exceeds 2^31 - 1.
+ */
+size_t attn_softmax_workspace_bytes(uint32_t rows, uint32_t cols);
+
+attn_status_t attn_softmax_f32(const float *x, float *out, uint32_t rows, uint32_t cols,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(attn_status_t status);
 

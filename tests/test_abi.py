@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -205,3 +205,20 @@ def test_rope_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, FAKE, 2, 4, 64, 3, 1e4, 0, None) == DIM
     assert f(FAKE, FAKE, FAKE, 2, 4, 64, 64, 0.0, 0, None) == DIM
     assert f(FAKE, FAKE, FAKE, 0, 4, 64, 64, 1e4, 0, None) == DIM
+
+
+def test_softmax_rejects_bad_arguments(lib):
+    f = lib.attn_softmax_f32
+    need = ad.softmax_workspace_bytes(8, 5000)
+    assert need >= 8 * 2 * 8 and need % 256 == 0
+    assert ad.softmax_workspace_bytes(0, 5) == 0 and ad.softmax_workspace_bytes(5, 0) == 0
+    assert f(None, FAKE, 8, 5000, FAKE, need, None) == NULL
+    assert f(FAKE, None, 8, 5000, FAKE, need, None) == NULL
+    assert f(FAKE, FAKE, 0, 5000, FAKE, need, None) == DIM
+    assert f(FAKE, FAKE, 8, 0, FAKE, need, None) == DIM
+    assert f(FAKE + 2, FAKE, 8, 5000, FAKE, need, None) == ALIGN
+    assert f(FAKE, FAKE + 2, 8, 5000, FAKE, need, None) == ALIGN
+    assert f(FAKE, FAKE, 8, 5000, FAKE + 8, need, None) == ALIGN
+    assert f(FAKE, FAKE, 8, 5000, None, need, None) == WS
+    assert f(FAKE, FAKE, 8, 5000, FAKE, need - 1, None) == WS
+    assert f(FAKE, FAKE, 1 << 20, 1 << 31, FAKE, 1 << 40, None) == DIM
