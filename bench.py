@@ -67,7 +67,7 @@ def parse():
                    help="two_dispatch: fp16 score row written then read back "
                         "(attn_qk_f16 + attn_pv_f16), single-sequence workloads only; "
                         "step: rotate q and a new key, append the new K/V row at "
-                        "current_pos, attend (attn_decode_step_f16*), dense caches only")
+                        "current_pos, attend (attn_decode_step_f16*)")
     return p.parse_args()
 
 
@@ -340,14 +340,19 @@ def main():
             return rc if rc else lib.attn_pv_f16(*pv_args[r])
         step_fns = [lambda r=r: two_dispatch(r) for r in range(copies)]
     elif args.path == "step":
-        if w.paged:
-            raise SystemExit("--path step needs a dense cache")
         gen = torch.Generator(device=dev)
         gen.manual_seed(w.seed + 1000)
         k_new = torch.randn(w.q_shape, generator=gen, device=dev).half()
         v_new = torch.randn(w.q_shape, generator=gen, device=dev).half()
         rot = (D, ctypes.c_double(10000.0), 0)
-        if w.batched:
+        if w.paged:
+            step_args = [(vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
+                          vp(ks[r].data_ptr()), vp(vs[r].data_ptr()), vp(out.data_ptr()),
+                          vp(bt.data_ptr()), vp(cp_dev.data_ptr()), B, H, D, w.page_size,
+                          w.max_blocks, w.num_blocks) + rot
+                         + (vp(ws.data_ptr()), ws_bytes, sh) for r in range(copies)]
+            fn = lib.attn_decode_step_f16_paged
+        elif w.batched:
             step_args = [(vp(q.data_ptr()), vp(k_new.data_ptr()), vp(v_new.data_ptr()),
                           vp(ks[r].data_ptr()), vp(vs[r].data_ptr()), vp(out.data_ptr()),
                           vp(cp_dev.data_ptr()), B, H, D, S) + rot

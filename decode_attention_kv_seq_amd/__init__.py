@@ -77,6 +77,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_step_f16_batched.argtypes = [vp, vp, vp, vp, vp, vp, vp, u32, u32, u32, u32,
                                                  u32, f64, i32, vp, sz, vp]
     lib.attn_decode_step_f16_batched.restype = ctypes.c_int
+    lib.attn_decode_step_f16_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u32, u32, u32, u32,
+                                               u32, u32, u32, f64, i32, vp, sz, vp]
+    lib.attn_decode_step_f16_paged.restype = ctypes.c_int
     lib.attn_rope_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, f64, i32, vp]
     lib.attn_rope_f16.restype = ctypes.c_int
     lib.attn_softmax_workspace_bytes.argtypes = [u32, u32]
@@ -389,6 +392,32 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, *, rope_dims=Non
             _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out), H, D, S,
             int(current_pos), dims, base, 1 if traditional else 0, _ptr(workspace), ws_n,
             _stream_handle(stream)))
+    return out
+
+
+def decode_step_paged(q, k_new, v_new, k_pool, v_pool, block_table, current_pos, *,
+                      rope_dims=None, rope_base: float = 10000.0, traditional: bool = False,
+                      out=None, workspace=None, stream=None):
+    """The decode step on a paged cache: q, k_new, v_new [B, H, D]; pools
+    [num_blocks, page_size, H, D] (slot current_pos written in place);
+    block_table int32 [B, max_blocks] and current_pos int32 [B] on the GPU."""
+    lib = load_library()
+    B, H, D, P, MB, NB, cp = _paged_args(q, k_pool, v_pool, block_table, current_pos)
+    dev = k_pool.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _req(t, n, torch.float16, dev)
+        if tuple(t.shape) != (B, H, D):
+            raise ValueError("%s must be [batch, n_heads, head_dim]" % n)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float16, device=dev)
+    _req(out, "out", torch.float16, dev)
+    dims, base = _rope_params(rope_dims, D, rope_base)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, D, P * MB, dev)
+    _check(lib.attn_decode_step_f16_paged(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+        _ptr(block_table), _ptr(cp), B, H, D, P, MB, NB, dims, base, 1 if traditional else 0,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return out
 
 

@@ -743,6 +743,10 @@ struct CombineArgs {
     const uint16_t *q;
     float scale_log2;         // log2(e) / sqrt(D)
     RopeArgs rope;
+    // paged caches: the appended rows go to the page the block table names
+    // for slot pos (nothing is written for an entry >= num_blocks)
+    const uint32_t *block_table;
+    uint32_t max_blocks, num_blocks, page_shift;
 };
 
 // One workgroup per (sequence, head); thread (cg, d) handles element d of
@@ -825,9 +829,18 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
             const uint16_t q16 = f2h_rne(rope_apply(qx, qy, tid, a.rope, pos));
             const uint16_t k16 = f2h_rne(rope_apply(kx, ky, tid, a.rope, pos));
             prod = h2f(q16) * h2f(k16);   // exact: both factors are fp16
-            const size_t row = (((size_t)b * a.S + pos) * a.H + h) * a.D + tid;
-            a.rope.k_cache[row] = k16;
-            a.rope.v_cache[row] = v16;
+            size_t slot = (size_t)b * a.S + pos;
+            bool write = true;
+            if (a.block_table) {
+                const uint32_t page = a.block_table[(size_t)b * a.max_blocks + (pos >> a.page_shift)];
+                write = page < a.num_blocks;
+                slot = (size_t)page << a.page_shift | (pos & ((1u << a.page_shift) - 1u));
+            }
+            if (write) {
+                const size_t row = (slot * a.H + h) * a.D + tid;
+                a.rope.k_cache[row] = k16;
+                a.rope.v_cache[row] = v16;
+            }
         }
         return block_sum<NT>(prod, sm_dot) * a.scale_log2;
     };
@@ -1508,7 +1521,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
     const SplitFn fn =
         scores_in ? pick_scores_split(ly)
-        : rope    ? pick_split<false, false, true>(ly, kn, bal)
+        : rope    ? (pg ? pick_split<false, true, true>(ly, kn, bal) : pick_split<false, false, true>(ly, kn, bal))
         : pg ? (dump ? pick_split<true, true, false>(ly, kn, bal) : pick_split<false, true, false>(ly, kn, bal))
              : (dump ? pick_split<true, false, false>(ly, kn, bal) : pick_split<false, false, false>(ly, kn, bal));
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
@@ -1568,7 +1581,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
 attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_host,
                              uint32_t batch, uint32_t H, uint32_t D, uint32_t S, const void *ws,
                              hipStream_t stream, const RopeArgs *rope = nullptr,
-                             const uint16_t *q = nullptr) {
+                             const uint16_t *q = nullptr, const Paging *pg = nullptr) {
     const WsLayout wl = workspace_layout(batch, H, D, S);
     CombineArgs c;
     c.header = static_cast<const uint32_t *>(ws);
@@ -1584,6 +1597,10 @@ attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_
     c.q = q;
     c.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     c.rope = rope ? *rope : RopeArgs{};
+    c.block_table = pg ? pg->block_table : nullptr;
+    c.max_blocks = pg ? pg->max_blocks : 0;
+    c.num_blocks = pg ? pg->num_blocks : 0;
+    c.page_shift = pg ? pg->page_shift : 0;
     const bool wide = (uint64_t)batch * H < kCombineWide;
     const dim3 grid(H, batch);
     if (rope) {
@@ -1611,7 +1628,7 @@ attn_status_t decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
                           uint16_t *k_cache, uint16_t *v_cache, uint16_t *out,
                           const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
                           uint32_t D, uint32_t S, uint32_t dims, double base, int traditional,
-                          void *ws, size_t ws_bytes, void *stream) {
+                          void *ws, size_t ws_bytes, void *stream, const Paging *pg = nullptr) {
     attn_status_t s = check_split(q, k_cache, v_cache, cp_dev, batch, H, D, S, nullptr);
     if (s != ATTN_OK) return s;
     if (!k_new || !v_new || !out) return fail(ATTN_ERR_NULL, "k_new, v_new and out must be non-NULL");
@@ -1634,9 +1651,9 @@ attn_status_t decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool wrote = false;
     s = launch_split(q, k_cache, v_cache, cp_dev, cp_host, batch, H, D, S, nullptr, ws, nullptr,
-                     nullptr, st, &wrote, nullptr, &r);
+                     pg, st, &wrote, nullptr, &r);
     if (s != ATTN_OK) return s;
-    return launch_combine(out, cp_dev, cp_host, batch, H, D, S, ws, st, &r, q);
+    return launch_combine(out, cp_dev, cp_host, batch, H, D, S, ws, st, &r, q, pg);
 }
 
 attn_status_t decode_full(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
@@ -1913,6 +1930,26 @@ attn_status_t attn_decode_step_f16_batched(const uint16_t *q, const uint16_t *k_
     return decode_step(q, k_new, v_new, k_cache, v_cache, out, current_pos, 0, batch, n_heads,
                        head_dim, capacity, rope_dims, rope_base, rope_traditional, workspace,
                        workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_step_f16_paged(const uint16_t *q, const uint16_t *k_new,
+                                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool,
+                                         uint16_t *out, const uint32_t *block_table,
+                                         const uint32_t *current_pos, uint32_t batch,
+                                         uint32_t n_heads, uint32_t head_dim, uint32_t page_size,
+                                         uint32_t max_blocks, uint32_t num_blocks,
+                                         uint32_t rope_dims, double rope_base, int rope_traditional,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+    attn_status_t s = check_sizes(batch, n_heads, head_dim, 1);
+    if (s != ATTN_OK) return s;
+    Paging pg;
+    uint32_t cap = 0;
+    s = check_paging(block_table, current_pos, batch, n_heads, head_dim, page_size, max_blocks,
+                     num_blocks, &pg, &cap);
+    if (s != ATTN_OK) return s;
+    return decode_step(q, k_new, v_new, k_pool, v_pool, out, current_pos, 0, batch, n_heads,
+                       head_dim, cap, rope_dims, rope_base, rope_traditional, workspace,
+                       workspace_bytes, stream, &pg);
 }
 
 attn_status_t attn_rope_f16(const uint16_t *x, uint16_t *out, const uint32_t *positions,

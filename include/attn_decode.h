@@ -38,7 +38,9 @@
  *    refused; work enqueued before it on the same call may have run).
  *    attn_last_error() gives the calling thread's detail text for its last
  *    non-OK return.
- *  - Outputs (out, scores_dump, workspace) must not overlap any input.
+ *  - Outputs (out, scores_dump, workspace) must not overlap any input, except
+ *    where an entry point says otherwise (the decode step writes one row of
+ *    its caches; the row softmax may run in place).
  */
 #ifndef ATTN_DECODE_H
 #define ATTN_DECODE_H
@@ -259,6 +261,29 @@ attn_status_t attn_decode_step_f16_batched(const uint16_t *q, const uint16_t *k_
                                            uint32_t rope_dims, double rope_base,
                                            int rope_traditional, void *workspace,
                                            size_t workspace_bytes, void *stream);
+
+/*
+ * The decode step on a paged cache (pool and block table as for
+ * attn_decode_f16_paged): slot pos = min(current_pos[b], capacity - 1) of
+ * sequence b is row pos % page_size of page block_table[b][pos / page_size];
+ * the rotated key and the new value are written there, positions 0..pos-1
+ * are read through the table, and the output is that of
+ * attn_decode_step_f16_batched on the equivalent dense cache.  A table entry
+ * >= num_blocks for slot pos means the new rows are not written (and reads
+ * use the last page, as for attn_decode_f16_paged: the output is then
+ * meaningless but every access stays in bounds).
+ *   k_pool, v_pool  [num_blocks, page_size, n_heads, head_dim] fp16, written at slot pos
+ *   capacity        max_blocks * page_size; workspace as for the batched step
+ *                   with that capacity
+ */
+attn_status_t attn_decode_step_f16_paged(const uint16_t *q, const uint16_t *k_new,
+                                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool,
+                                         uint16_t *out, const uint32_t *block_table,
+                                         const uint32_t *current_pos, uint32_t batch,
+                                         uint32_t n_heads, uint32_t head_dim, uint32_t page_size,
+                                         uint32_t max_blocks, uint32_t num_blocks,
+                                         uint32_t rope_dims, double rope_base, int rope_traditional,
+                                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The rotation alone (the page's FastRoPE with one offset per batch entry):

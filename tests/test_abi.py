@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -222,3 +222,24 @@ def test_softmax_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, 8, 5000, None, need, None) == WS
     assert f(FAKE, FAKE, 8, 5000, FAKE, need - 1, None) == WS
     assert f(FAKE, FAKE, 1 << 20, 1 << 31, FAKE, 1 << 40, None) == DIM
+
+
+def test_paged_step_rejects_bad_arguments(lib):
+    f = lib.attn_decode_step_f16_paged
+
+    def call(**kw):
+        a = dict(q=FAKE, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, out=FAKE, bt=FAKE, cp=FAKE, B=2, H=4,
+                 D=64, P=16, MB=8, NB=16, dims=64, base=1e4, trad=0, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return f(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["out"], a["bt"], a["cp"], a["B"],
+                 a["H"], a["D"], a["P"], a["MB"], a["NB"], a["dims"], a["base"], a["trad"],
+                 a["ws"], a["wsb"], None)
+
+    assert call(bt=None) == NULL
+    assert call(cp=None) == NULL
+    assert call(kn=None) == NULL
+    assert call(P=12) == DIM
+    assert call(dims=65) == DIM
+    assert call(base=-1.0) == DIM
+    assert call(out=FAKE + 1) == ALIGN
+    assert call(wsb=16) == WS

@@ -330,3 +330,72 @@ def test_step_long_context_sampled():
 def test_step_masked_garbage_sampled():
     w = wl.WORKLOADS["h32_d128_s32768_cp20000_garbage"]
     sampled_heads_step(w, [0, 31], w.cur_pos, trad=True)
+
+
+# ------------------------------------------------------ paged decode step
+
+
+def scatter_pages(kc, vc, page_size, rng, extra=3):
+    """Dense [B, S, H, D] caches -> shuffled page pools and a block table."""
+    B, S, H, D = kc.shape
+    mb = S // page_size
+    nb = B * mb + extra
+    perm = rng.permutation(nb)[: B * mb].reshape(B, mb)
+    kp = np.zeros((nb, page_size, H, D), np.float16)
+    vp = np.zeros((nb, page_size, H, D), np.float16)
+    for b in range(B):
+        for j in range(mb):
+            kp[perm[b, j]] = kc[b, j * page_size:(j + 1) * page_size]
+            vp[perm[b, j]] = vc[b, j * page_size:(j + 1) * page_size]
+    return kp, vp, perm.astype(np.int32)
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 256])
+def test_paged_step_equals_dense_step(page_size):
+    """The same caches dense or in shuffled pages: the paged step gives the
+    dense step's output bits, writes the same rows into the right pages,
+    leaves every other pool row alone, and matches the oracle."""
+    rng = np.random.default_rng(300 + page_size)
+    B, S, H, D = 6, 1024, 8, 128
+    cps = [1023, 0, 500, 15, 16, 2000]      # 2000: past the capacity, slot 1023
+    q, kn, vn, kc, vc, cps = batched_inputs(rng, B, S, H, D, cps)
+    print("paged step, page %d" % page_size, flush=True)
+    dense_out, dense_k, dense_v = run_step_batched(q, kn, vn, kc, vc, cps, D, True)
+    kp, vp, bt = scatter_pages(kc, vc, page_size, rng)
+    kp_d, vp_d = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    cp = torch.from_numpy(cps.astype(np.int32)).to(DEV)
+    out = ad.decode_step_paged(torch.from_numpy(q).to(DEV), torch.from_numpy(kn).to(DEV),
+                               torch.from_numpy(vn).to(DEV), kp_d, vp_d,
+                               torch.from_numpy(bt).to(DEV), cp, traditional=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), dense_out)
+    kp_g, vp_g = kp_d.cpu().numpy(), vp_d.cpu().numpy()
+    want_k, want_v = kp.copy(), vp.copy()
+    for b in range(B):
+        pos = min(int(cps[b]), S - 1)
+        page, r = bt[b, pos // page_size], pos % page_size
+        want_k[page, r] = dense_k[b, pos]
+        want_v[page, r] = dense_v[b, pos]
+    assert np.array_equal(kp_g.view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(vp_g.view(np.uint16), want_v.view(np.uint16))
+    for b in (0, 2, 5):
+        check_step(out[b], dense_k[b], dense_v[b], kc[b], vc[b], q[b], kn[b], vn[b],
+                   int(cps[b]), D, True, what="paged sequence %d" % b)
+
+
+def test_paged_step_out_of_range_entry_writes_nothing():
+    """A block-table entry past the pool for the new slot: no row is written
+    (the output is unspecified but the call stays in bounds)."""
+    rng = np.random.default_rng(77)
+    B, S, H, D, P = 2, 64, 2, 64, 16
+    q, kn, vn, kc, vc, cps = batched_inputs(rng, B, S, H, D, [40, 63])
+    kp, vp, bt = scatter_pages(kc, vc, P, rng)
+    bt[1, 63 // P] = kp.shape[0] + 5
+    kp_d, vp_d = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    ad.decode_step_paged(torch.from_numpy(q).to(DEV), torch.from_numpy(kn).to(DEV),
+                         torch.from_numpy(vn).to(DEV), kp_d, vp_d, torch.from_numpy(bt).to(DEV),
+                         torch.from_numpy(cps.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    kp_g = kp_d.cpu().numpy().view(np.uint16)
+    changed = np.argwhere(np.any(kp_g != kp.view(np.uint16), axis=(2, 3)))
+    assert changed.tolist() == [[bt[0, 40 // P], 40 % P]]

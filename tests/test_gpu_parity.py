@@ -638,3 +638,19 @@ def test_two_dispatches_against_fp16_score_reading():
     torch.cuda.synchronize()
     assert_close(out, ref, "two dispatches")
     print("two dispatches vs one pass: max |diff| %.3g" % float((out.float() - fused.float()).abs().max()))
+
+
+def test_batch_at_the_size_limit():
+    """batch = 65535 (the largest the header allows), ragged lengths including
+    the capacity bound; 40 sampled sequences against the oracle."""
+    rng = np.random.default_rng(65535)
+    B, S, H, D = 65535, 4, 1, 8
+    q = randn16(rng, (B, H, D))
+    k = randn16(rng, (B, S, H, D))
+    v = randn16(rng, (B, S, H, D))
+    cp = rng.integers(0, S + 2, B)
+    out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), to_dev(cp.astype(np.int32)))
+    torch.cuda.synchronize()
+    pick = np.concatenate([[0, B - 1], rng.choice(B, 38, replace=False)])
+    ref, _ = oracle.decode_batched(q[pick], k[pick], v[pick], cp[pick])
+    assert_close(out[torch.from_numpy(pick)], ref, "batch 65535")

@@ -160,3 +160,14 @@ def test_softmax_of_decode_scores():
         assert np.allclose(g[:L], ref_w[0, :L], rtol=1e-3, atol=1e-12), h
     del k_d, v_d
     torch.cuda.empty_cache()
+
+
+def test_softmax_million_short_rows():
+    """2^20 rows of 24 columns (the wave-per-row path at scale), sampled rows."""
+    rng = np.random.default_rng(20)
+    rows, cols = 1 << 20, 24
+    x = (rng.standard_normal((rows, cols)) * 4).astype(np.float32)
+    got = ad.softmax(torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    pick = np.concatenate([[0, rows - 1], rng.choice(rows, 2000, replace=False)])
+    check(got[torch.from_numpy(pick).to(DEV)], np.ascontiguousarray(x[pick]), "2^20 rows")
