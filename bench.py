@@ -71,8 +71,20 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(w, seconds: float):
-    """Time the oracle (as it is) on whole (sequence, head) units of the workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(w, seconds: float, path: str = "fused"):
+    """Time the oracle (as it is) on whole (sequence, head) units of the
+    workload: its decode, or for the decode step its rotate-append-attend."""
     import numpy as np
     from decode_attention_kv_seq_amd import workloads as wl
     import oracle
@@ -91,10 +103,25 @@ def cpu_baseline(w, seconds: float):
         q, k, v = wl.head_slice_paged(w, b, h, bt) if w.paged else wl.head_slice(w, b, h)
         return q[0], k, v, int(pos[b]), k.shape[0] * w.head_dim * 2 * 2
 
+    step_rng = np.random.default_rng(1)
+    D = w.head_dim
+
+    def run(s):
+        q, k, v, cp = s[0], s[1], s[2], s[3]
+        if path != "step":
+            return orc.decode(q, k, v, cp)
+        # the step oracle on this head: rotate q and a new key at cp, write row cp, attend
+        kn = (step_rng.standard_normal((1, D))).astype(np.float16)
+        vn = (step_rng.standard_normal((1, D))).astype(np.float16)
+        kc = k.numpy().view(np.uint16).copy()
+        vc = v.numpy().view(np.uint16).copy()
+        return orc.decode_step(q.numpy(), kn, vn, kc, vc, cp, dims=D)
+
     # estimate the rate on one unit, then size a sample of ~`seconds`
-    q, k, v, cp, nbytes = one(*units[0])
+    first = one(*units[0])
+    nbytes = first[4]
     t0 = time.perf_counter()
-    orc.decode(q, k, v, cp)
+    run(first)
     t1 = time.perf_counter() - t0
     n_units = max(cores, int(seconds * cores / max(t1, 1e-6)))
     n_units = min(n_units, len(units))
@@ -104,15 +131,17 @@ def cpu_baseline(w, seconds: float):
     from concurrent.futures import ThreadPoolExecutor
     t0 = time.perf_counter()
     with ThreadPoolExecutor(cores) as ex:
-        list(ex.map(lambda s: orc.decode(s[0], s[1], s[2], s[3]), sample))
+        list(ex.map(run, sample))
     dt = time.perf_counter() - t0
     return {
         "value": round(total_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "%d of %d (sequence, head) units, %.1f MB of K+V, %.2f s on %d threads "
-                  "(fp64 scalar C oracle)" % (n_units, len(units), total_bytes / 1e6, dt, cores),
+        "sample": "%d of %d (sequence, head) units, %.1f MB of K+V, %.2f s on %d threads of "
+                  "%s (fp64 scalar C oracle%s)" % (
+                      n_units, len(units), total_bytes / 1e6, dt, cores, cpu_model(),
+                      ": rotate, append, attend" if path == "step" else ""),
     }
 
 
@@ -219,8 +248,9 @@ def run_softmax(args, name):
         dt = time.perf_counter() - t0
         cpu = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
-               "sample": "the whole [%d, %d] input, %d time%s, %.2f s on %d threads (fp64 C oracle)"
-                         % (w.rows, w.cols, reps, "" if reps == 1 else "s", dt, cores)}
+               "sample": "the whole [%d, %d] input, %d time%s, %.2f s on %d threads of %s "
+                         "(fp64 C oracle)" % (w.rows, w.cols, reps, "" if reps == 1 else "s", dt,
+                                              cores, cpu_model())}
         log("cpu baseline: %s" % json.dumps(cpu))
 
     line = {
@@ -425,7 +455,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds, args.path)
         log("cpu baseline: %s" % json.dumps(cpu))
 
     config = {
