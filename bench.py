@@ -129,18 +129,24 @@ def cpu_baseline(w, seconds: float, path: str = "fused"):
     total_bytes = sum(s[4] for s in sample)
 
     from concurrent.futures import ThreadPoolExecutor
+    # small workloads: repeat the whole sample until it is long enough to time
+    reps, dt = 0, 0.0
     t0 = time.perf_counter()
     with ThreadPoolExecutor(cores) as ex:
-        list(ex.map(run, sample))
-    dt = time.perf_counter() - t0
+        while reps == 0 or (dt < 0.5 * seconds / cores and reps < 10000):
+            list(ex.map(run, sample))
+            reps += 1
+            dt = time.perf_counter() - t0
+    total_bytes *= reps
     return {
         "value": round(total_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "%d of %d (sequence, head) units, %.1f MB of K+V, %.2f s on %d threads of "
+        "sample": "%d of %d (sequence, head) units%s, %.1f MB of K+V, %.2f s on %d threads of "
                   "%s (fp64 scalar C oracle%s)" % (
-                      n_units, len(units), total_bytes / 1e6, dt, cores, cpu_model(),
+                      n_units, len(units), "" if reps == 1 else " x %d passes" % reps,
+                      total_bytes / 1e6, dt, cores, cpu_model(),
                       ": rotate, append, attend" if path == "step" else ""),
     }
 
