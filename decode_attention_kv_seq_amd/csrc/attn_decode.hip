@@ -286,17 +286,26 @@ struct PieceDst {
     uint16_t *out;
 };
 
+// What a split launch computes: the one-pass decode; softmax.V from stored
+// fp16 scores (the page's second dispatch); the decode step (q rotated, the
+// new token's slot left to the combine); or only the scores, written as fp16
+// (the page's first dispatch).
+enum : int { kModeDecode = 0, kModePv = 1, kModeStep = 2, kModeQk = 3 };
+
 // Stream positions [c0, c_end) of head block hb of sequence b through the
-// online softmax and leave one merged state per head at `dst`.  The caller
+// online softmax and leave one merged state per head at `dst` (kModeQk: write
+// the scores of those positions instead).  The caller
 // guarantees c0 < c_end.  LDS is free again when this returns.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC,
-          bool ROPE>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
 __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint32_t hb,
                                             uint32_t c0, uint32_t c_end, const PieceDst &dst,
                                             float *sm_o, float *sm_m, float *sm_l) {
     constexpr int RG = 64 / GL;              // row groups per wave
     constexpr int NG = kWaves * RG;          // row groups per workgroup
     constexpr int DPAD = VEC * GL * NV;      // padded row length in LDS
+    constexpr bool SC = MODE == kModePv;
+    constexpr bool ROPE = MODE == kModeStep;
+    constexpr bool QK = MODE == kModeQk;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -406,11 +415,25 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
             for (int j = 0; j < NV; ++j) {
                 if constexpr (!SC)
                     blk.k[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
-                blk.v[u][j] = eok[j] ? load_pack<VEC>(vbase + row + eoff[j]) : zero_pack<VEC>();
+                if constexpr (!QK)
+                    blk.v[u][j] = eok[j] ? load_pack<VEC>(vbase + row + eoff[j]) : zero_pack<VEC>();
             }
         }
     };
+    uint16_t *qk_row = QK ? a.scores_out + ((size_t)b * a.H + h) * a.S : nullptr;
     auto consume = [&](const Block &blk, uint32_t base) {
+        if constexpr (QK) {   // first dispatch: the fp16 score of each position
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t p = base + u * pps + pg;
+                float dot = 0.f;
+#pragma unroll
+                for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], blk.k[u][j], dot);
+                dot = group_sum<GL>(dot);
+                if (gl == 0 && p < c_end) qk_row[p] = f2h_rne(dot * a.scale);
+            }
+            return;
+        }
         float t[U];
         float tmax = -INFINITY;
 #pragma unroll
@@ -496,6 +519,8 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         }
     }
 
+    if constexpr (QK) return;   // no softmax state to merge
+
     // ---- merge the row groups that share a head
 #pragma unroll
     for (int j = 0; j < NV; ++j)
@@ -546,11 +571,29 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 // Chunked grid: workgroup (hb + n_hb*chunk, b) takes positions
 // [chunk*C, (chunk+1)*C) of head block hb.  Partials: o [B, H, nc_stride, D],
 // (m, l) [B, H, nc_stride, 2].
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC,
-          bool ROPE>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
-    write_header(a, 0);
+    constexpr bool ROPE = MODE == kModeStep;
+    if constexpr (MODE == kModeQk) {
+        // workgroups past the reading grid write -inf over the masked
+        // positions [L, S) of every head (their rows are never read)
+        if (blockIdx.x >= a.grid) {
+            constexpr uint16_t kNegInfHalf = 0xFC00;
+            const uint32_t L = valid_len(a.cp_host, a.S);
+            const uint64_t span = a.S - L;
+            const uint64_t total = (uint64_t)a.H * span;
+            const uint64_t n_fill = gridDim.x - a.grid;
+            for (uint64_t i = (uint64_t)(blockIdx.x - a.grid) * kThreads + threadIdx.x; i < total;
+                 i += n_fill * kThreads) {
+                const uint64_t h = i / span;
+                a.scores_out[h * a.S + L + (i - h * span)] = kNegInfHalf;
+            }
+            return;
+        }
+    } else {
+        write_header(a, 0);
+    }
     const uint32_t b = blockIdx.y;
     const uint32_t hb = blockIdx.x % a.n_hb;
     const uint32_t chunk = blockIdx.x / a.n_hb;
@@ -567,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     dst.pml = a.part_ml + (bh0 * a.nc_stride + chunk) * 2;
     dst.pml_hs = (size_t)a.nc_stride * 2;
     dst.out = a.direct ? a.out + bh0 * a.D : nullptr;
-    split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC, ROPE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
+    split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, MODE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
                                                                  sm_l);
 }
 
@@ -619,10 +662,10 @@ __device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t
 // `grid` equal ranges, one per workgroup.  A workgroup writes one partial per
 // segment piece it covers, at slot w + s; o [slots, hpb, D], (m, l)
 // [slots, hpb, 2] with slots = grid + batch*n_hb.
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, bool SC,
-          bool ROPE>
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
+    constexpr bool ROPE = MODE == kModeStep;
     write_header(a, 1);
     __shared__ uint64_t sm_pref[kBalancedMaxBatch + 1];
     __shared__ uint64_t sm_tmp[kThreads];
@@ -657,76 +700,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs
         dst.pml = a.part_ml + slot * a.hpb * 2;
         dst.pml_hs = 2;
         dst.out = nullptr;
-        split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, SC, ROPE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
+        split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, MODE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
                                                                  sm_l);
         x = x_end;
-    }
-}
-
-// ------------------------------------------------ first dispatch (scores)
-// The page's attention_qk_f16 as its own launch: the scaled score of every
-// position, rounded to fp16, -inf after current_pos (positions there are not
-// read).  Same lane layout as the split kernel; workgroup (hb + n_hb*chunk)
-// covers chunk*C .. (chunk+1)*C-1 of head block hb, over the whole cache.
-template <int VEC, int GL, int NV, bool FULL>
-__global__ __launch_bounds__(kThreads) void attn_qk_kernel(SplitArgs a) {
-    constexpr int RG = 64 / GL;
-    constexpr int NG = kWaves * RG;
-    constexpr int U = 4;
-    const uint32_t hb = blockIdx.x % a.n_hb;
-    const uint32_t chunk = blockIdx.x / a.n_hb;
-    const uint32_t L = valid_len(a.cp_host, a.S);
-    const uint32_t c0 = chunk * a.chunk;
-    const uint32_t c_end = min(c0 + a.chunk, a.S);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int g = (tid >> 6) * RG + lane / GL;
-    const int gl = lane % GL;
-    const uint32_t hg = (uint32_t)g % a.hpb;
-    const uint32_t pg = (uint32_t)g / a.hpb;
-    const uint32_t pps = NG / a.hpb;
-    const uint32_t h = hb * a.hpb + hg;
-    const size_t D = a.D;
-    const size_t HD = (size_t)a.H * D;
-    uint16_t *srow = a.scores_out + (size_t)h * a.S;
-    constexpr uint16_t kNegInfHalf = 0xFC00;
-    if (c0 >= L) {   // every position of this chunk is masked
-        for (uint32_t p = c0 + pg; p < c_end; p += pps)
-            if (gl == 0) srow[p] = kNegInfHalf;
-        return;
-    }
-    int eoff[NV];
-    bool eok[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        eoff[j] = (gl + GL * j) * VEC;
-        eok[j] = FULL || eoff[j] < (int)a.D;
-    }
-    Pack<VEC> qp[NV];
-    const uint16_t *qrow = a.q + (size_t)h * D;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        qp[j] = eok[j] ? load_pack<VEC>(qrow + eoff[j]) : zero_pack<VEC>();
-    const uint16_t *kbase = a.k + (size_t)h * D;
-    for (uint32_t base = c0; base < c_end; base += pps * U) {
-        Pack<VEC> kr[U][NV];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t p = base + u * pps + pg;
-            const size_t row = (size_t)(p < L ? p : L - 1) * HD;   // masked slots reread a valid row
-#pragma unroll
-            for (int j = 0; j < NV; ++j)
-                kr[u][j] = eok[j] ? load_pack<VEC>(kbase + row + eoff[j]) : zero_pack<VEC>();
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t p = base + u * pps + pg;
-            float dot = 0.f;
-#pragma unroll
-            for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], kr[u][j], dot);
-            dot = group_sum<GL>(dot);
-            if (gl == 0 && p < c_end) srow[p] = p < L ? f2h_rne(dot * a.scale) : kNegInfHalf;
-        }
     }
 }
 
@@ -1027,12 +1003,16 @@ const Knobs &env_knobs() {
 }
 
 // Defaults by row size (head_dim) and by call kind: one sequence (host
-// current_pos), a batch with per-sequence lengths, or a paged batch.
-enum class Kind { single, batched, paged };
+// current_pos), a batch with per-sequence lengths, a paged batch, or one
+// sequence streaming a single tensor per position (the page's two
+// dispatches: K alone for the scores, V alone for softmax.V), which needs
+// double buffering and wider head blocks to keep as many bytes in flight.
+enum class Kind { single, batched, paged, stream };
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
-    if (kind != Kind::single) k = Knobs{256, 8192, 8, 4, 1, 1};        // batches, dense or paged
+    if (kind == Kind::batched || kind == Kind::paged) k = Knobs{256, 8192, 8, 4, 1, 1};
+    else if (kind == Kind::stream) k = D <= 64 ? Knobs{1024, 8192, 8, 2, 1, 0} : Knobs{1024, 8192, 2, 2, 1, 0};
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
     else k = Knobs{512, 8192, 2, 2, 1, 0};                             // 256-byte rows and wider
     const Knobs &e = env_knobs();
@@ -1106,7 +1086,7 @@ uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S)
 // depends on sizes only.
 uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     uint32_t m = 0;
-    for (Kind kd : {Kind::single, Kind::batched, Kind::paged}) {
+    for (Kind kd : {Kind::single, Kind::batched, Kind::paged, Kind::stream}) {
         const uint32_t c = chunk_bound_for(knobs(D, kd), batch, H, S);
         if (c > m) m = c;
     }
@@ -1143,7 +1123,7 @@ size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
     if (batch > kBalancedMaxBatch) return 0;
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     size_t m = 0;
-    for (Kind kd : {Kind::single, Kind::batched, Kind::paged}) {
+    for (Kind kd : {Kind::single, Kind::batched, Kind::paged, Kind::stream}) {
         const Knobs k = knobs(D, kd);
         const size_t n = (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
         if (n > m) m = n;
@@ -1184,37 +1164,40 @@ attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
 
 using SplitFn = void (*)(SplitArgs);
 
-template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED, bool ROPE>
+template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED, int MODE>
 SplitFn kernel_for(bool bal) {
-    return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, false, ROPE>
-               : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, false, ROPE>;
+    if constexpr (MODE == kModeQk || MODE == kModePv)   // single sequence: chunked grid
+        return attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>;
+    else
+        return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>
+                   : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>;
 }
 
 // Dense caches honour the unroll/prefetch knobs on the fast layouts; paged
 // caches are double-buffered with U=2 or U=4.
-template <int V, int G, int N, bool F, bool DUMP, bool PAGED, bool ROPE>
+template <int V, int G, int N, bool F, bool DUMP, bool PAGED, int MODE>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
     if constexpr (PAGED) {
-        return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, ROPE>(bal)
-                             : kernel_for<V, G, N, F, 2, true, DUMP, PAGED, ROPE>(bal);
+        return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal)
+                             : kernel_for<V, G, N, F, 2, true, DUMP, PAGED, MODE>(bal);
     } else {
-        if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP, PAGED, ROPE>(bal)
-                                       : kernel_for<V, G, N, F, 2, false, DUMP, PAGED, ROPE>(bal);
-        if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP, PAGED, ROPE>(bal)
-                                       : kernel_for<V, G, N, F, 8, false, DUMP, PAGED, ROPE>(bal);
-        return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, ROPE>(bal)
-                    : kernel_for<V, G, N, F, 4, false, DUMP, PAGED, ROPE>(bal);
+        if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP, PAGED, MODE>(bal)
+                                       : kernel_for<V, G, N, F, 2, false, DUMP, PAGED, MODE>(bal);
+        if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP, PAGED, MODE>(bal)
+                                       : kernel_for<V, G, N, F, 8, false, DUMP, PAGED, MODE>(bal);
+        return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal)
+                    : kernel_for<V, G, N, F, 4, false, DUMP, PAGED, MODE>(bal);
     }
 }
 
-template <bool DUMP, bool PAGED, bool ROPE>
+template <bool DUMP, bool PAGED, int MODE>
 SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     // fast paths: head_dim 64 and 128 with 16-byte rows
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP, PAGED, ROPE>(k, bal);
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP, PAGED, ROPE>(k, bal);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8) return pick_unroll<8, 8, 1, true, DUMP, PAGED, MODE>(k, bal);
+    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16) return pick_unroll<8, 16, 1, true, DUMP, PAGED, MODE>(k, bal);
 #define ATTN_CASE(V, G, N, F)                                                          \
     if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
-        return kernel_for<V, G, N, F, 4, true, DUMP, PAGED, ROPE>(bal);
+        return kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal);
     ATTN_CASE(8, 32, 1, true)
     ATTN_CASE(8, 8, 1, false)
     ATTN_CASE(8, 16, 1, false)
@@ -1236,33 +1219,6 @@ SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     ATTN_CASE(1, 64, 3, false)
     ATTN_CASE(1, 64, 4, false)
 #undef ATTN_CASE
-    return nullptr;
-}
-
-#define ATTN_ALL_LAYOUTS(X)                                                              \
-    X(8, 8, 1, true) X(8, 16, 1, true) X(8, 32, 1, true) X(8, 8, 1, false) X(8, 16, 1, false) \
-    X(8, 32, 1, false) X(4, 8, 1, false) X(4, 16, 1, false) X(4, 32, 1, false)            \
-    X(4, 64, 1, false) X(2, 8, 1, false) X(2, 16, 1, false) X(2, 32, 1, false)            \
-    X(2, 64, 1, false) X(2, 64, 2, false) X(1, 8, 1, false) X(1, 16, 1, false)            \
-    X(1, 32, 1, false) X(1, 64, 1, false) X(1, 64, 2, false) X(1, 64, 3, false)           \
-    X(1, 64, 4, false)
-
-// Second dispatch (softmax.V from stored scores): chunked grid, U=4, double-buffered.
-SplitFn pick_scores_split(const Layout &ly) {
-#define ATTN_SC(V, G, N, F)                                                            \
-    if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F)                       \
-        return attn_split_kernel<V, G, N, F, 4, true, false, false, true, false>;
-    ATTN_ALL_LAYOUTS(ATTN_SC)
-#undef ATTN_SC
-    return nullptr;
-}
-
-using QkFn = void (*)(SplitArgs);
-QkFn pick_qk(const Layout &ly) {
-#define ATTN_QK(V, G, N, F)                                                            \
-    if (ly.vec == V && ly.gl == G && ly.nv == N && ly.full == F) return attn_qk_kernel<V, G, N, F>;
-    ATTN_ALL_LAYOUTS(ATTN_QK)
-#undef ATTN_QK
     return nullptr;
 }
 
@@ -1305,17 +1261,20 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
                            const Paging *pg, hipStream_t stream, bool *wrote_out,
                            const uint16_t *scores_in = nullptr, const RopeArgs *rope = nullptr) {
     const Layout ly = scores_in ? choose_layout(D, v, v, v) : choose_layout(D, q, k, v);
-    const Kind kind = pg ? Kind::paged : cp_dev ? Kind::batched : Kind::single;
+    const Kind kind = scores_in ? Kind::stream : pg ? Kind::paged : cp_dev ? Kind::batched : Kind::single;
     const Knobs kn = knobs(D, kind);
     const uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores_in && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
     const SplitFn fn =
-        scores_in ? pick_scores_split(ly)
-        : rope    ? (pg ? pick_split<false, true, true>(ly, kn, bal) : pick_split<false, false, true>(ly, kn, bal))
-        : pg ? (dump ? pick_split<true, true, false>(ly, kn, bal) : pick_split<false, true, false>(ly, kn, bal))
-             : (dump ? pick_split<true, false, false>(ly, kn, bal) : pick_split<false, false, false>(ly, kn, bal));
+        scores_in ? pick_split<false, false, kModePv>(ly, kn, false)
+        : rope    ? (pg ? pick_split<false, true, kModeStep>(ly, kn, bal)
+                        : pick_split<false, false, kModeStep>(ly, kn, bal))
+        : pg ? (dump ? pick_split<true, true, kModeDecode>(ly, kn, bal)
+                     : pick_split<false, true, kModeDecode>(ly, kn, bal))
+             : (dump ? pick_split<true, false, kModeDecode>(ly, kn, bal)
+                     : pick_split<false, false, kModeDecode>(ly, kn, bal));
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
     // host current_pos: plan the exact span (a decode step streams one
     // position less; at least one chunk is launched, so the header is
@@ -1601,11 +1560,14 @@ attn_status_t attn_qk_f16(const uint16_t *q, const uint16_t *k_cache, uint16_t *
     if (!aligned(q, 2) || !aligned(k_cache, 2) || !aligned(scores, 2))
         return fail(ATTN_ERR_ALIGN, "fp16 tensors must be 2-byte aligned");
     const Layout ly = choose_layout(head_dim, q, k_cache, k_cache);
-    const QkFn fn = pick_qk(ly);
+    const Knobs kn = knobs(head_dim, Kind::stream);
+    const SplitFn fn = pick_split<false, false, kModeQk>(ly, kn, false);
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", head_dim);
-    const Knobs kn = knobs(head_dim, Kind::single);
     const uint32_t hpb = heads_per_wg(n_heads, ly, kn.hpb);
-    const Plan plan = make_plan(1, n_heads, head_dim, seq_len, seq_len, Kind::single);
+    // the reading grid covers positions 0..current_pos; a few more
+    // workgroups write -inf over the rest
+    const uint32_t L = (current_pos < seq_len - 1 ? current_pos : seq_len - 1) + 1;
+    const Plan plan = make_plan(1, n_heads, head_dim, seq_len, L, Kind::stream);
     SplitArgs a = {};
     a.q = q;
     a.k = k_cache;
@@ -1618,7 +1580,12 @@ attn_status_t attn_qk_f16(const uint16_t *q, const uint16_t *k_cache, uint16_t *
     a.hpb = hpb;
     a.scale = (float)(1.0 / sqrt((double)head_dim));
     a.scores_out = scores;
-    hipLaunchKernelGGL(fn, dim3(a.n_hb * plan.n_chunks), dim3(kThreads), 0,
+    a.batch = 1;
+    a.grid = a.n_hb * plan.n_chunks;
+    const uint64_t masked = (uint64_t)(seq_len - L) * n_heads;
+    const uint64_t fill = masked ? cdiv(masked, (uint64_t)kThreads * 16) : 0;
+    const uint32_t n_fill = (uint32_t)(fill < 1024 ? fill : 1024);
+    hipLaunchKernelGGL(fn, dim3(a.grid + n_fill), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), a);
     return hip_check("score kernel launch");
 }
