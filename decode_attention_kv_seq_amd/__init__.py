@@ -3,7 +3,8 @@
 A thin Python binding over ``libattn_decode.so`` (declared in
 ``include/attn_decode.h``).  This module only checks and marshals
 arguments: every step of the computation runs in the library's HIP kernels.
-PyTorch provides device memory and the stream; calls enqueue on
+PyTorch provides device memory and the stream; each call runs with its
+tensors' device current and enqueues on that device's
 ``torch.cuda.current_stream()`` unless a stream is given.
 
 The operation (page "Developing Apple Metal Kernels in Rust - A Deep Dive
@@ -168,9 +169,10 @@ def decode(q, k, v, current_pos: int, *, out=None, dump: bool = False, workspace
     sc = torch.empty((H, S), dtype=torch.float32, device=dev) if dump else None
     if workspace is None:
         workspace = alloc_workspace(1, H, D, S, dev)
-    _check(lib.attn_decode_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, D, S, int(current_pos),
-                               _ptr(sc), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream_handle(stream)))
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_decode_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, D, S, int(current_pos),
+                                   _ptr(sc), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream_handle(stream)))
     return (out, sc) if dump else out
 
 
@@ -197,10 +199,11 @@ def decode_batched(q, k, v, current_pos, *, out=None, dump: bool = False, worksp
     sc = torch.empty((B, H, S), dtype=torch.float32, device=dev) if dump else None
     if workspace is None:
         workspace = alloc_workspace(B, H, D, S, dev)
-    _check(lib.attn_decode_f16_batched(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cp), B, H, D, S,
-                                       _ptr(sc), _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(),
-                                       _stream_handle(stream)))
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_decode_f16_batched(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cp), B, H, D, S,
+                                           _ptr(sc), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream_handle(stream)))
     return (out, sc) if dump else out
 
 
@@ -224,10 +227,11 @@ def split(q, k, v, current_pos, workspace, *, dump=None, stream=None):
         raise ValueError("shape mismatch")
     cp_dev, cp_host = (None, int(current_pos)) if not isinstance(current_pos, torch.Tensor) \
         else (_cp_tensor(current_pos, B, k.device), 0)
-    _check(lib.attn_decode_f16_split(_ptr(q3), _ptr(k4), _ptr(v4), _ptr(cp_dev), cp_host, B, H, D, S,
-                                     _ptr(dump), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(),
-                                     _stream_handle(stream)))
+    with torch.cuda.device(k.device):   # launch on the tensors' device
+        _check(lib.attn_decode_f16_split(_ptr(q3), _ptr(k4), _ptr(v4), _ptr(cp_dev), cp_host, B, H, D, S,
+                                         _ptr(dump), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream)))
 
 
 def combine(out, current_pos, batch, n_heads, head_dim, seq_len, workspace, *, stream=None):
@@ -236,10 +240,11 @@ def combine(out, current_pos, batch, n_heads, head_dim, seq_len, workspace, *, s
     _req(out, "out", torch.float16)
     cp_dev, cp_host = (None, int(current_pos)) if not isinstance(current_pos, torch.Tensor) \
         else (_cp_tensor(current_pos, batch, out.device), 0)
-    _check(lib.attn_decode_f16_combine(_ptr(out), _ptr(cp_dev), cp_host, batch, n_heads, head_dim,
-                                       seq_len, _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(),
-                                       _stream_handle(stream)))
+    with torch.cuda.device(out.device):   # launch on the tensors' device
+        _check(lib.attn_decode_f16_combine(_ptr(out), _ptr(cp_dev), cp_host, batch, n_heads, head_dim,
+                                           seq_len, _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream_handle(stream)))
     return out
 
 
@@ -277,10 +282,11 @@ def decode_paged(q, k_pool, v_pool, block_table, current_pos, *, out=None, dump=
     sc = torch.empty((B, H, cap), dtype=torch.float32, device=dev) if dump else None
     if workspace is None:
         workspace = alloc_workspace(B, H, D, cap, dev)
-    _check(lib.attn_decode_f16_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
-                                     _ptr(block_table), _ptr(cp), B, H, D, P, MB, NB, _ptr(sc),
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _stream_handle(stream)))
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_decode_f16_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+                                         _ptr(block_table), _ptr(cp), B, H, D, P, MB, NB, _ptr(sc),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream)))
     return (out, sc) if dump else out
 
 
@@ -289,11 +295,12 @@ def split_paged(q, k_pool, v_pool, block_table, current_pos, workspace, *, dump=
     max_blocks * page_size, workspace)` is the second."""
     lib = load_library()
     B, H, D, P, MB, NB, cp = _paged_args(q, k_pool, v_pool, block_table, current_pos)
-    _check(lib.attn_decode_f16_paged_split(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-                                           _ptr(cp), B, H, D, P, MB, NB, _ptr(dump),
-                                           _ptr(workspace),
-                                           workspace.numel() * workspace.element_size(),
-                                           _stream_handle(stream)))
+    with torch.cuda.device(k_pool.device):   # launch on the tensors' device
+        _check(lib.attn_decode_f16_paged_split(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                               _ptr(cp), B, H, D, P, MB, NB, _ptr(dump),
+                                               _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(),
+                                               _stream_handle(stream)))
 
 
 def qk(q, k, current_pos: int, *, scores=None, stream=None):
@@ -311,8 +318,9 @@ def qk(q, k, current_pos: int, *, scores=None, stream=None):
     _req(scores, "scores", torch.float16, dev)
     if tuple(scores.shape) != (H, S):
         raise ValueError("scores must be [n_heads, seq_len]")
-    _check(lib.attn_qk_f16(_ptr(q), _ptr(k), _ptr(scores), H, D, S, int(current_pos),
-                           _stream_handle(stream)))
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_qk_f16(_ptr(q), _ptr(k), _ptr(scores), H, D, S, int(current_pos),
+                               _stream_handle(stream)))
     return scores
 
 
@@ -330,9 +338,10 @@ def pv(scores, v, current_pos: int, *, out=None, workspace=None, stream=None):
     _req(out, "out", torch.float16, dev)
     if workspace is None:
         workspace = alloc_workspace(1, H, D, S, dev)
-    _check(lib.attn_pv_f16(_ptr(scores), _ptr(v), _ptr(out), H, D, S, int(current_pos),
-                           _ptr(workspace), workspace.numel() * workspace.element_size(),
-                           _stream_handle(stream)))
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_pv_f16(_ptr(scores), _ptr(v), _ptr(out), H, D, S, int(current_pos),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream_handle(stream)))
     return out
 
 
@@ -381,17 +390,19 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, *, rope_dims=Non
     ws_n = workspace.numel() * workspace.element_size()
     if batched:
         cp = _cp_tensor(current_pos, B, dev)
-        _check(lib.attn_decode_step_f16_batched(
-            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cp),
-            B, H, D, S, dims, base, 1 if traditional else 0, _ptr(workspace), ws_n,
-            _stream_handle(stream)))
+        with torch.cuda.device(dev):   # launch on the tensors' device
+            _check(lib.attn_decode_step_f16_batched(
+                _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cp),
+                B, H, D, S, dims, base, 1 if traditional else 0, _ptr(workspace), ws_n,
+                _stream_handle(stream)))
     else:
         if not 0 <= int(current_pos) <= 0xFFFFFFFF:
             raise ValueError("current_pos must fit in uint32")
-        _check(lib.attn_decode_step_f16(
-            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out), H, D, S,
-            int(current_pos), dims, base, 1 if traditional else 0, _ptr(workspace), ws_n,
-            _stream_handle(stream)))
+        with torch.cuda.device(dev):   # launch on the tensors' device
+            _check(lib.attn_decode_step_f16(
+                _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out), H, D, S,
+                int(current_pos), dims, base, 1 if traditional else 0, _ptr(workspace), ws_n,
+                _stream_handle(stream)))
     return out
 
 
@@ -414,10 +425,11 @@ def decode_step_paged(q, k_new, v_new, k_pool, v_pool, block_table, current_pos,
     dims, base = _rope_params(rope_dims, D, rope_base)
     if workspace is None:
         workspace = alloc_workspace(B, H, D, P * MB, dev)
-    _check(lib.attn_decode_step_f16_paged(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out),
-        _ptr(block_table), _ptr(cp), B, H, D, P, MB, NB, dims, base, 1 if traditional else 0,
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_decode_step_f16_paged(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+            _ptr(block_table), _ptr(cp), B, H, D, P, MB, NB, dims, base, 1 if traditional else 0,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return out
 
 
@@ -438,8 +450,9 @@ def rope(x, positions, *, rope_dims=None, rope_base: float = 10000.0, traditiona
     if tuple(out.shape) != (B, H, D):
         raise ValueError("out must be [batch, n_heads, head_dim]")
     dims, base = _rope_params(rope_dims, D, rope_base)
-    _check(lib.attn_rope_f16(_ptr(x), _ptr(out), _ptr(pos), B, H, D, dims, base,
-                             1 if traditional else 0, _stream_handle(stream)))
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_rope_f16(_ptr(x), _ptr(out), _ptr(pos), B, H, D, dims, base,
+                                 1 if traditional else 0, _stream_handle(stream)))
     return out
 
 
@@ -465,7 +478,8 @@ def softmax(x, *, out=None, workspace=None, stream=None):
         if n == 0:
             raise ValueError("invalid sizes")
         workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
-    _check(lib.attn_softmax_f32(_ptr(x), _ptr(out), rows, cols, _ptr(workspace),
-                                workspace.numel() * workspace.element_size(),
-                                _stream_handle(stream)))
+    with torch.cuda.device(x.device):   # launch on the tensors' device
+        _check(lib.attn_softmax_f32(_ptr(x), _ptr(out), rows, cols, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream_handle(stream)))
     return out
