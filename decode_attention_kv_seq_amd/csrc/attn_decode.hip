@@ -21,6 +21,15 @@
 //
 // Positions after current_pos are never loaded.  MFMA is not used: one query
 // row per head makes this a matrix-vector product bound by HBM bandwidth.
+//
+// The same split kernel, in other modes, also serves the page's own two
+// dispatches (scores written as fp16, then softmax.V from a stored score
+// row), a paged cache read through a block table, and the decode step of the
+// page "Tutorial 16: Writing Custom Metal Kernels" (q rotated at the new
+// token's position; the combine folds in the new token and appends its K/V
+// rows).  File layout: device helpers (packs, lane-group sums, rotation),
+// split kernels, combine kernel, dump fill, standalone rotation; then the
+// host planner, kernel selection, launchers and the C ABI.
 
 #include <hip/hip_runtime.h>
 

@@ -399,3 +399,56 @@ def test_paged_step_out_of_range_entry_writes_nothing():
     kp_g = kp_d.cpu().numpy().view(np.uint16)
     changed = np.argwhere(np.any(kp_g != kp.view(np.uint16), axis=(2, 3)))
     assert changed.tolist() == [[bt[0, 40 // P], 40 % P]]
+
+
+def _full_batch_step_sampled(name, pairs):
+    """The decode step on a whole 64-sequence workload (the bench's --path
+    step launch), (sequence, head) pairs against the oracle on host copies
+    regenerated from the seeded generator."""
+    w = wl.WORKLOADS[name]
+    rng = np.random.default_rng(w.seed + 300)
+    q = wl.make_q(w, DEV)
+    kn = torch.from_numpy(randn16(rng, w.q_shape)).to(DEV)
+    vn = torch.from_numpy(randn16(rng, w.q_shape)).to(DEV)
+    cp = w.positions().to(torch.int32).to(DEV)
+    if w.paged:
+        kp, vp = wl.make_kv_paged(w, DEV)
+        bt = w.block_table()
+        out = ad.decode_step_paged(q, kn, vn, kp, vp, bt.to(torch.int32).to(DEV), cp)
+    else:
+        kc, vc = wl.make_kv(w, DEV)
+        out = ad.decode_step(q, kn, vn, kc, vc, cp)
+    torch.cuda.synchronize()
+    pos_all = w.positions()
+    for b, h in pairs:
+        pos = min(int(pos_all[b]), w.seq_len - 1)
+        if w.paged:
+            qh, kh, vh = wl.head_slice_paged(w, b, h, bt)
+            new_k = kp[bt[b, pos // w.page_size], pos % w.page_size, h].cpu().numpy()
+        else:
+            qh, kh, vh = wl.head_slice(w, b, h)
+            new_k = kc[b, pos, h].cpu().numpy()
+        kh = kh.numpy().view(np.uint16).copy()   # rows 0..pos; the oracle rewrites row pos
+        vh = vh.numpy().view(np.uint16).copy()
+        knh = kn[b, h:h + 1].cpu().numpy()
+        vnh = vn[b, h:h + 1].cpu().numpy()
+        r = oracle.decode_step(qh[0].numpy(), knh, vnh, kh, vh, pos, dims=w.head_dim)
+        assert_close(out[b, h:h + 1], r["out"], "%s b=%d h=%d" % (name, b, h))
+        assert_rotation(new_k.view(np.uint16)[None], knh, r["k_rot"], r["k16"], w.head_dim, False,
+                        "%s b=%d h=%d k row" % (name, b, h))
+
+
+def test_step_full_ragged_batch_sampled():
+    w = wl.WORKLOADS["b64_h32_d128_cap8192_ragged"]
+    lens = w.positions()
+    longest, shortest = int(torch.argmax(lens)), int(torch.argmin(lens))
+    _full_batch_step_sampled(w.name, [(0, 0), (longest, 31), (shortest, 5), (17, 12), (63, 30)])
+    torch.cuda.empty_cache()
+
+
+def test_step_full_paged_batch_sampled():
+    w = wl.WORKLOADS["b64_h32_d128_cap8192_ragged_paged16"]
+    lens = w.positions()
+    longest, shortest = int(torch.argmax(lens)), int(torch.argmin(lens))
+    _full_batch_step_sampled(w.name, [(1, 3), (longest, 0), (shortest, 31), (40, 17)])
+    torch.cuda.empty_cache()

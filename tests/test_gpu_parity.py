@@ -654,3 +654,27 @@ def test_batch_at_the_size_limit():
     pick = np.concatenate([[0, B - 1], rng.choice(B, 38, replace=False)])
     ref, _ = oracle.decode_batched(q[pick], k[pick], v[pick], cp[pick])
     assert_close(out[torch.from_numpy(pick)], ref, "batch 65535")
+
+
+def test_two_dispatches_full_size_sampled():
+    """The page's two dispatches on the 131072-position cache (the bench's
+    --path two_dispatch launch): every stored score of 4 sampled heads is an
+    fp16 neighbour of the oracle's score, and the output of those heads
+    matches softmax.V of the oracle's scores rounded to fp16."""
+    w = wl.WORKLOADS["h64_d64_s131072_spikes"]
+    q = wl.make_q(w, DEV)[0]
+    k, v = wl.make_kv(w, DEV)
+    sc = ad.qk(q, k[0], w.cur_pos)
+    out = ad.pv(sc, v[0], w.cur_pos)
+    torch.cuda.synchronize()
+    for h in (0, 21, 42, 63):
+        qh, kh, vh = wl.head_slice(w, 0, h)
+        _, s_ref, _ = oracle.decode(qh[0], kh, vh, w.cur_pos, want_scores=True)
+        got = sc[h].cpu().numpy().astype(np.float64)
+        err = np.abs(got - s_ref[0])
+        cond = np.abs(kh[:, 0].numpy().astype(np.float64)) @ np.abs(qh[0, 0].numpy().astype(np.float64)) / 8.0
+        assert np.all(err < f16_ulp(s_ref[0]) + 64 * 2.0 ** -24 * cond), h
+        ref = oracle.pv_from_scores(s_ref.astype(np.float16), vh, w.cur_pos)
+        assert_close(out[h:h + 1], ref, "two dispatches head %d" % h)
+    del k, v
+    torch.cuda.empty_cache()
