@@ -53,7 +53,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;            // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr uint32_t kBalancedMaxBatch = 1024;   // sequences the balanced grid handles
-constexpr uint32_t kCombineWide = 512;   // (sequence, head) pairs below which the combine uses 1024 threads
+constexpr uint32_t kCombineWide = 512;    // (sequence, head) pairs from which the combine uses 256 threads
+constexpr uint32_t kCombineWave = 2048;   // ... and from which it takes one wave per pair
 
 // ------------------------------------------------------------------ packs
 // A pack is VEC consecutive fp16 values of one row held by one lane.
@@ -745,9 +746,76 @@ struct CombineArgs {
 // exactly 1.
 constexpr int kCombineRegs = 8;   // chunk values per thread held in registers
 
+// Where the split launch left the partials of (sequence b, head h): nc of
+// them, the first at (ml, po), consecutive ones ml_cs and po_cs floats apart.
+// `excl` positions at the end of the sequence are not in the partials (a
+// decode step's new token).
+struct PartialSpan {
+    uint32_t nc;
+    const float *ml, *po;
+    size_t ml_cs, po_cs;
+};
+
+__device__ __forceinline__ PartialSpan locate_partials(const CombineArgs &a, uint32_t b, uint32_t h,
+                                                       uint32_t cp, uint32_t excl) {
+    PartialSpan r{0, nullptr, nullptr, 0, 0};
+    const size_t bh = (size_t)b * a.H + h;
+    if (!a.header[kHdrBalanced]) {
+        const uint32_t L = valid_len(cp, a.S) - excl;
+        const uint32_t chunk = a.header[kHdrChunk];
+        const size_t nc_stride = a.header[kHdrNcStride];
+        r.nc = (L + chunk - 1) / chunk;
+        r.ml = a.part_ml + bh * nc_stride * 2;
+        r.po = a.part_o + bh * nc_stride * a.D;
+        r.ml_cs = 2;
+        r.po_cs = a.D;
+    } else {
+        // the split grid's workgroups w_first..w_last covered segment
+        // s = b*n_hb + hb; workgroup w left its piece at slot w + s
+        const uint64_t *pref = reinterpret_cast<const uint64_t *>(a.header + kHdrPrefixWord);
+        const uint32_t hpb = a.header[kHdrHpb];
+        const uint64_t n_hb = a.header[kHdrNHb];
+        const uint64_t W = n_hb * pref[a.batch];
+        const uint64_t G = a.header[kHdrGrid] < W ? a.header[kHdrGrid] : W;   // as the split did
+        const uint32_t hb = h / hpb, ho = h % hpb;
+        const uint64_t L = pref[b + 1] - pref[b];
+        if (L > 0) {   // (a decode step at position 0 has no earlier positions)
+            const uint64_t first = n_hb * pref[b] + hb * L;
+            const uint64_t last = first + L - 1;
+            const uint64_t w_first = ((first + 1) * G - 1) / W;   // W * G < 2^63
+            const uint64_t w_last = ((last + 1) * G - 1) / W;
+            r.nc = (uint32_t)(w_last - w_first + 1);
+            const uint64_t slot0 = w_first + (uint64_t)b * n_hb + hb;
+            r.ml = a.part_ml + (slot0 * hpb + ho) * 2;
+            r.po = a.part_o + (slot0 * hpb + ho) * a.D;
+            r.ml_cs = (size_t)hpb * 2;
+            r.po_cs = (size_t)hpb * a.D;
+        }
+    }
+    return r;
+}
+
+// Decode step: element d of the new token's rotated key and value row into
+// slot pos of sequence b's caches (dense, or the page the block table names;
+// nothing for a table entry past the pool).
+__device__ __forceinline__ void append_elem(const CombineArgs &a, uint32_t b, uint32_t h,
+                                            uint32_t pos, uint32_t d, uint16_t k16, uint16_t v16) {
+    size_t slot = (size_t)b * a.S + pos;
+    if (a.block_table) {
+        const uint32_t page = a.block_table[(size_t)b * a.max_blocks + (pos >> a.page_shift)];
+        if (page >= a.num_blocks) return;
+        slot = (size_t)page << a.page_shift | (pos & ((1u << a.page_shift) - 1u));
+    }
+    const size_t row = (slot * a.H + h) * a.D + d;
+    a.rope.k_cache[row] = k16;
+    a.rope.v_cache[row] = v16;
+}
+
 // NT threads per workgroup: 1024 when there are few (sequence, head) pairs,
-// 256 when there are enough workgroups to fill the chip in one dispatch round.
-// STEP: the second launch of a decode step (see CombineArgs).
+// each of which may have many partials; 256 from kCombineWide pairs, so the
+// grid fills the chip in one round; larger batches take
+// attn_combine_wave_kernel below.  STEP: the second launch of a decode step
+// (see CombineArgs).
 template <int NT, bool STEP>
 __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
     __shared__ float sm_w[NT];
@@ -790,61 +858,16 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
             const uint16_t q16 = f2h_rne(rope_apply(qx, qy, tid, a.rope, pos));
             const uint16_t k16 = f2h_rne(rope_apply(kx, ky, tid, a.rope, pos));
             prod = h2f(q16) * h2f(k16);   // exact: both factors are fp16
-            size_t slot = (size_t)b * a.S + pos;
-            bool write = true;
-            if (a.block_table) {
-                const uint32_t page = a.block_table[(size_t)b * a.max_blocks + (pos >> a.page_shift)];
-                write = page < a.num_blocks;
-                slot = (size_t)page << a.page_shift | (pos & ((1u << a.page_shift) - 1u));
-            }
-            if (write) {
-                const size_t row = (slot * a.H + h) * a.D + tid;
-                a.rope.k_cache[row] = k16;
-                a.rope.v_cache[row] = v16;
-            }
+            append_elem(a, b, h, pos, tid, k16, v16);
         }
         return block_sum<NT>(prod, sm_dot) * a.scale_log2;
     };
     float t_new = -INFINITY;
 
-    uint32_t nc;              // partials of this (sequence, head)
-    const float *ml = nullptr, *po = nullptr;   // first partial's (m, l) and o row
-    size_t ml_cs = 0, po_cs = 0;                // strides between consecutive partials
-    if (!a.header[kHdrBalanced]) {
-        // a decode step's partials cover the positions before the new token
-        const uint32_t L = valid_len(cp, a.S) - (STEP ? 1u : 0u);
-        const uint32_t chunk = a.header[kHdrChunk];
-        const size_t nc_stride = a.header[kHdrNcStride];
-        nc = (L + chunk - 1) / chunk;
-        ml = a.part_ml + bh * nc_stride * 2;
-        po = a.part_o + bh * nc_stride * a.D;
-        ml_cs = 2;
-        po_cs = a.D;
-    } else {
-        // the split grid's workgroups w_first..w_last covered segment
-        // s = b*n_hb + hb; workgroup w left its piece at slot w + s
-        const uint64_t *pref = reinterpret_cast<const uint64_t *>(a.header + kHdrPrefixWord);
-        const uint32_t hpb = a.header[kHdrHpb];
-        const uint64_t n_hb = a.header[kHdrNHb];
-        const uint64_t W = n_hb * pref[a.batch];
-        const uint64_t G = a.header[kHdrGrid] < W ? a.header[kHdrGrid] : W;   // as the split did
-        const uint32_t hb = h / hpb, ho = h % hpb;
-        const uint64_t L = pref[b + 1] - pref[b];
-        if (L == 0) {   // a decode step at position 0: no earlier positions
-            nc = 0;
-        } else {
-            const uint64_t first = n_hb * pref[b] + hb * L;
-            const uint64_t last = first + L - 1;
-            const uint64_t w_first = ((first + 1) * G - 1) / W;   // W * G < 2^63
-            const uint64_t w_last = ((last + 1) * G - 1) / W;
-            nc = (uint32_t)(w_last - w_first + 1);
-            const uint64_t slot0 = w_first + (uint64_t)b * n_hb + hb;
-            ml = a.part_ml + (slot0 * hpb + ho) * 2;
-            po = a.part_o + (slot0 * hpb + ho) * a.D;
-            ml_cs = (size_t)hpb * 2;
-            po_cs = (size_t)hpb * a.D;
-        }
-    }
+    const PartialSpan ps = locate_partials(a, b, h, cp, STEP ? 1u : 0u);
+    const uint32_t nc = ps.nc;
+    const float *ml = ps.ml, *po = ps.po;
+    const size_t ml_cs = ps.ml_cs, po_cs = ps.po_cs;
     const uint32_t G = NT / a.D;   // chunk groups (D <= 256)
     const uint32_t cg = tid / a.D;
     const uint32_t d = tid % a.D;
@@ -937,6 +960,91 @@ __global__ __launch_bounds__(NT) void attn_combine_kernel(CombineArgs a) {
             ls += sm_l[r * a.D + tid];
         }
         a.out[bh * a.D + tid] = f2h_rne(os / ls);
+    }
+}
+
+// Many (sequence, head) pairs, each with a few partials (batches): one wave
+// per pair, four pairs per workgroup, so the launch is a quarter of the
+// workgroups and no barrier is needed.  Lane i holds output elements
+// i, i+64, ...; the partials are merged in chunk order (the max first, then
+// the weighted sums of o and l through the same operations, so all-equal V
+// rows still give exactly 1).  STEP as in attn_combine_kernel.
+template <bool STEP>
+__global__ __launch_bounds__(256) void attn_combine_wave_kernel(CombineArgs a) {
+    constexpr int EPL = ATTN_MAX_HEAD_DIM / 64;   // output elements per lane, at most
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t pair = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= (uint64_t)a.batch * a.H) return;   // the whole wave
+    const uint32_t b = (uint32_t)(pair / a.H), h = (uint32_t)(pair % a.H);
+    const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
+
+    float qx[EPL], qy[EPL], kx[EPL], ky[EPL];
+    uint16_t v16[EPL];
+    if constexpr (STEP) {   // the new token's rows, loaded before the partials
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const uint32_t d = lane + 64u * j;
+            qx[j] = qy[j] = kx[j] = ky[j] = 0.f;
+            v16[j] = 0;
+            if (d < a.D) {
+                const uint32_t pd = rope_partner(d, a.rope);
+                const uint16_t *qrow = a.q + pair * a.D;
+                const uint16_t *krow = a.rope.k_new + pair * a.D;
+                qx[j] = h2f(qrow[d]);
+                qy[j] = h2f(qrow[pd]);
+                kx[j] = h2f(krow[d]);
+                ky[j] = h2f(krow[pd]);
+                v16[j] = a.rope.v_new[pair * a.D + d];
+            }
+        }
+    }
+    const PartialSpan ps = locate_partials(a, b, h, cp, STEP ? 1u : 0u);
+    float M = -INFINITY;
+    for (uint32_t c = lane; c < ps.nc; c += 64) M = fmaxf(M, ps.ml[c * ps.ml_cs]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float t_new = -INFINITY;
+    if constexpr (STEP) {
+        const uint32_t pos = valid_len(cp, a.S) - 1u;
+        float prod = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const uint32_t d = lane + 64u * j;
+            if (d < a.D) {
+                const uint16_t q16 = f2h_rne(rope_apply(qx[j], qy[j], d, a.rope, pos));
+                const uint16_t k16 = f2h_rne(rope_apply(kx[j], ky[j], d, a.rope, pos));
+                prod += h2f(q16) * h2f(k16);   // exact products, fp32 sum
+                append_elem(a, b, h, pos, d, k16, v16[j]);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) prod += __shfl_xor(prod, off, 64);
+        t_new = prod * a.scale_log2;
+        M = fmaxf(M, t_new);
+    }
+    float o[EPL], l = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) o[j] = 0.f;
+#pragma unroll 4
+    for (uint32_t c = 0; c < ps.nc; ++c) {
+        const float w = __builtin_amdgcn_exp2f(ps.ml[c * ps.ml_cs] - M);
+        l = fmaf(ps.ml[c * ps.ml_cs + 1], w, l);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const uint32_t d = lane + 64u * j;
+            if (d < a.D) o[j] = fmaf(ps.po[c * ps.po_cs + d], w, o[j]);
+        }
+    }
+    if constexpr (STEP) {   // the new token, with weight 2^(t_new - M) and l term 1
+        const float w = __builtin_amdgcn_exp2f(t_new - M);
+        l = fmaf(1.f, w, l);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) o[j] = fmaf(h2f(v16[j]), w, o[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const uint32_t d = lane + 64u * j;
+        if (d < a.D) a.out[pair * a.D + d] = f2h_rne(o[j] / l);
     }
 }
 
@@ -1361,14 +1469,18 @@ attn_status_t launch_combine(uint16_t *out, const uint32_t *cp_dev, uint32_t cp_
     c.max_blocks = pg ? pg->max_blocks : 0;
     c.num_blocks = pg ? pg->num_blocks : 0;
     c.page_shift = pg ? pg->page_shift : 0;
-    const bool wide = (uint64_t)batch * H < kCombineWide;
+    const uint64_t pairs = (uint64_t)batch * H;
     const dim3 grid(H, batch);
-    if (rope) {
-        if (wide) hipLaunchKernelGGL((attn_combine_kernel<1024, true>), grid, dim3(1024), 0, stream, c);
-        else hipLaunchKernelGGL((attn_combine_kernel<256, true>), grid, dim3(256), 0, stream, c);
-    } else {
-        if (wide) hipLaunchKernelGGL((attn_combine_kernel<1024, false>), grid, dim3(1024), 0, stream, c);
+    const dim3 wave_grid((unsigned)cdiv(pairs, 4));
+    if (pairs < kCombineWide) {   // few pairs, possibly many partials each
+        if (rope) hipLaunchKernelGGL((attn_combine_kernel<1024, true>), grid, dim3(1024), 0, stream, c);
+        else hipLaunchKernelGGL((attn_combine_kernel<1024, false>), grid, dim3(1024), 0, stream, c);
+    } else if (pairs < kCombineWave) {
+        if (rope) hipLaunchKernelGGL((attn_combine_kernel<256, true>), grid, dim3(256), 0, stream, c);
         else hipLaunchKernelGGL((attn_combine_kernel<256, false>), grid, dim3(256), 0, stream, c);
+    } else {                      // many pairs, a few partials each
+        if (rope) hipLaunchKernelGGL((attn_combine_wave_kernel<true>), wave_grid, dim3(256), 0, stream, c);
+        else hipLaunchKernelGGL((attn_combine_wave_kernel<false>), wave_grid, dim3(256), 0, stream, c);
     }
     return hip_check("combine kernel launch");
 }

@@ -678,3 +678,20 @@ def test_two_dispatches_full_size_sampled():
         assert_close(out[h:h + 1], ref, "two dispatches head %d" % h)
     del k, v
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,H", [(40, 8), (100, 8), (300, 8)], ids=["pairs320", "pairs800", "pairs2400"])
+def test_combine_tiers(B, H):
+    """The combine takes 1024 threads per (sequence, head) below 512 pairs,
+    256 threads up to 2048, one wave per pair beyond: each tier against the
+    oracle on a ragged batch (some sequences shorter than one chunk)."""
+    rng = np.random.default_rng(B * H)
+    S, D = 1536, 64
+    q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, S, B)
+    pos[::5] = rng.integers(0, 8, len(pos[::5]))
+    out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), to_dev(pos.astype(np.int32)))
+    torch.cuda.synchronize()
+    pick = np.concatenate([[0, B - 1], rng.choice(B, 14, replace=False)])
+    ref, _ = oracle.decode_batched(q[pick], k[pick], v[pick], pos[pick])
+    assert_close(out[torch.from_numpy(pick)], ref, "B=%d H=%d" % (B, H))
