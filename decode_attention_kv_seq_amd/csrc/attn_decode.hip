@@ -55,6 +55,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr uint32_t kBalancedMaxBatch = 1024;   // sequences the balanced grid handles
 constexpr uint32_t kCombineWide = 512;    // (sequence, head) pairs from which the combine uses 256 threads
 constexpr uint32_t kCombineWave = 2048;   // ... and from which it takes one wave per pair
+constexpr uint32_t kScoreWindow = 8192;   // fp16 scores a scores-mode workgroup holds in LDS
 
 // ------------------------------------------------------------------ packs
 // A pack is VEC consecutive fp16 values of one row held by one lane.
@@ -103,6 +104,17 @@ __device__ __forceinline__ uint32_t pack_word(const Pack<VEC> &p, int j) {
     if constexpr (VEC == 8) return p.w[j];
     else if constexpr (VEC == 4) return p.w[j];
     else return p.w;
+}
+
+// Store N fp16 values to N consecutive elements in one write; dst must be
+// aligned to 2N bytes.
+template <int N>
+__device__ __forceinline__ void store_halves(uint16_t *dst, const uint16_t (&hv)[N]) {
+    const Pack<N> pk = make_pack<N>(hv);
+    if constexpr (N == 8) *reinterpret_cast<u32x4 *>(dst) = pk.w;
+    else if constexpr (N == 4) *reinterpret_cast<u32x2 *>(dst) = pk.w;
+    else if constexpr (N == 2) *reinterpret_cast<uint32_t *>(dst) = pk.w;
+    else *dst = pk.w;
 }
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
@@ -309,7 +321,8 @@ enum : int { kModeDecode = 0, kModePv = 1, kModeStep = 2, kModeQk = 3 };
 template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
 __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint32_t hb,
                                             uint32_t c0, uint32_t c_end, const PieceDst &dst,
-                                            float *sm_o, float *sm_m, float *sm_l) {
+                                            float *sm_o, float *sm_m, float *sm_l,
+                                            uint16_t *sm_sc = nullptr) {
     constexpr int RG = 64 / GL;              // row groups per wave
     constexpr int NG = kWaves * RG;          // row groups per workgroup
     constexpr int DPAD = VEC * GL * NV;      // padded row length in LDS
@@ -387,6 +400,15 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[j][e] = 0.f;
 
+    // Position of block slot u of this lane's row group.  Row groups
+    // interleave (slot u of every row group, then slot u + 1), except in
+    // scores mode, where a row group takes U adjacent positions so that its
+    // leader writes their scores with one packed store.  Each load
+    // instruction still reads whole head blocks of single positions.
+    auto pos_at = [&](uint32_t base, int u) -> uint32_t {
+        return QK ? base + pg * U + u : base + u * pps + pg;
+    };
+
     // One block = U positions per row group.  Slots past the chunk end load
     // the chunk's first row (always valid) and get weight 0.
     struct Block {
@@ -403,7 +425,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         if constexpr (PAGED) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t p = base + u * pps + pg;
+                const uint32_t p = pos_at(base, u);
                 pi.id[u] = bt[(p < c_end ? p : c0) >> a.page_shift];
             }
         }
@@ -411,7 +433,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     auto load_rows = [&](Block &blk, uint32_t base, const Pids &pi) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t p = base + u * pps + pg;
+            const uint32_t p = pos_at(base, u);
             const uint32_t pc = p < c_end ? p : c0;
             size_t row;
             if constexpr (PAGED) {
@@ -430,17 +452,46 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
             }
         }
     };
-    uint16_t *qk_row = QK ? a.scores_out + ((size_t)b * a.H + h) * a.S : nullptr;
+    // Scores mode: the scores of a window of qk_w positions per head collect
+    // in LDS (sm_sc, kScoreWindow values) and leave in 16-byte stores when
+    // the window is full or the piece ends.  Stores and loads share one
+    // completion counter, so a store per block would put a write
+    // acknowledgement into every block's wait.  qk_w is a power of two and
+    // a multiple of the block's positions, so blocks never straddle windows.
+    const uint32_t qk_w = QK ? kScoreWindow / a.hpb : 0;
+    auto flush_scores = [&](uint32_t w0, uint32_t wn) {
+        const uint32_t n8 = (wn + 7) / 8;
+        for (uint32_t idx = tid; idx < a.hpb * n8; idx += kThreads) {
+            const uint32_t ho = idx / n8;
+            const uint32_t j = idx - ho * n8;
+            const uint16_t *src = sm_sc + ho * qk_w + j * 8;
+            uint16_t *out = a.scores_out + ((size_t)b * a.H + (size_t)hb * a.hpb + ho) * a.S + w0 + j * 8;
+            const uint32_t cnt = min(8u, wn - j * 8);
+            if (cnt == 8 && ((uintptr_t)out & 15) == 0) {
+                *reinterpret_cast<u32x4 *>(out) = *reinterpret_cast<const u32x4 *>(src);
+            } else {
+                for (uint32_t e = 0; e < cnt; ++e) out[e] = src[e];
+            }
+        }
+    };
     auto consume = [&](const Block &blk, uint32_t base) {
         if constexpr (QK) {   // first dispatch: the fp16 score of each position
+            uint16_t s16[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t p = base + u * pps + pg;
                 float dot = 0.f;
 #pragma unroll
                 for (int j = 0; j < NV; ++j) dot = dot_pack<VEC>(qp[j], blk.k[u][j], dot);
-                dot = group_sum<GL>(dot);
-                if (gl == 0 && p < c_end) qk_row[p] = f2h_rne(dot * a.scale);
+                s16[u] = f2h_rne(group_sum<GL>(dot) * a.scale);
+            }
+            const uint32_t w0 = c0 + (base - c0) / qk_w * qk_w;
+            // slots past the piece's end land inside the window, unflushed
+            if (gl == 0) store_halves<U>(sm_sc + hg * qk_w + (pos_at(base, 0) - w0), s16);
+            const uint32_t next = base + pps * U;
+            if (next == w0 + qk_w || next >= c_end) {   // the same for every thread
+                __syncthreads();
+                flush_scores(w0, min(qk_w, c_end - w0));
+                __syncthreads();
             }
             return;
         }
@@ -448,7 +499,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         float tmax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t p = base + u * pps + pg;
+            const uint32_t p = pos_at(base, u);
             float dot = 0.f;
             if constexpr (SC) {
                 // natural-log score from the buffer, in base-2 units
@@ -620,8 +671,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     dst.pml = a.part_ml + (bh0 * a.nc_stride + chunk) * 2;
     dst.pml_hs = (size_t)a.nc_stride * 2;
     dst.out = a.direct ? a.out + bh0 * a.D : nullptr;
+    __shared__ __align__(16) uint16_t sm_sc[MODE == kModeQk ? kScoreWindow : 8];
     split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, MODE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
-                                                                 sm_l);
+                                                                 sm_l, sm_sc);
 }
 
 // Inclusive prefix of the streamed lengths (valid length minus `excl`):
@@ -1122,9 +1174,11 @@ const Knobs &env_knobs() {
 // Defaults by row size (head_dim) and by call kind: one sequence (host
 // current_pos), a batch with per-sequence lengths, a paged batch, or one
 // sequence streaming a single tensor per position (the page's two
-// dispatches: K alone for the scores, V alone for softmax.V), which needs
-// double buffering and wider head blocks to keep as many bytes in flight.
-enum class Kind { single, batched, paged, stream, batched_chunked };
+// dispatches: V alone for softmax.V, K alone for the scores), which needs
+// double buffering to keep as many bytes in flight.  The scores pass has its
+// own row: it writes as it reads, and its best head blocking and unroll
+// differ.
+enum class Kind { single, batched, paged, stream, batched_chunked, scores };
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
@@ -1134,6 +1188,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     // ragged lengths better (2048 x 512 positions: +10% ragged, +4% full)
     else if (kind == Kind::batched_chunked) k = Knobs{256, 8192, 4, 2, 1, 0};
     else if (kind == Kind::stream) k = D <= 64 ? Knobs{1024, 8192, 8, 2, 1, 0} : Knobs{1024, 8192, 2, 2, 1, 0};
+    else if (kind == Kind::scores) k = D <= 64 ? Knobs{1024, 8192, 4, 2, 1, 0} : Knobs{1024, 8192, 4, 8, 1, 0};
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
     else k = Knobs{512, 8192, 2, 2, 1, 0};                             // 256-byte rows and wider
     const Knobs &e = env_knobs();
@@ -1690,14 +1745,14 @@ attn_status_t attn_qk_f16(const uint16_t *q, const uint16_t *k_cache, uint16_t *
     if (!aligned(q, 2) || !aligned(k_cache, 2) || !aligned(scores, 2))
         return fail(ATTN_ERR_ALIGN, "fp16 tensors must be 2-byte aligned");
     const Layout ly = choose_layout(head_dim, q, k_cache, k_cache);
-    const Knobs kn = knobs(head_dim, Kind::stream);
+    const Knobs kn = knobs(head_dim, Kind::scores);
     const SplitFn fn = pick_split<false, false, kModeQk>(ly, kn, false);
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", head_dim);
     const uint32_t hpb = heads_per_wg(n_heads, ly, kn.hpb);
     // the reading grid covers positions 0..current_pos; a few more
     // workgroups write -inf over the rest
     const uint32_t L = (current_pos < seq_len - 1 ? current_pos : seq_len - 1) + 1;
-    const Plan plan = make_plan(1, n_heads, head_dim, seq_len, L, Kind::stream);
+    const Plan plan = make_plan(1, n_heads, head_dim, seq_len, L, Kind::scores);
     SplitArgs a = {};
     a.q = q;
     a.k = k_cache;
