@@ -123,6 +123,25 @@ def _req(t: torch.Tensor, name: str, dtype, device=None):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _req_buf(t: torch.Tensor, name: str, device):
+    """A caller's scratch buffer (any dtype): contiguous, on ``device``.  The
+    library takes raw device pointers, so a host tensor must never reach it."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _req_dump(dump, shape, device):
+    """An optional caller-provided fp32 score dump of the given shape."""
+    if dump is not None:
+        _req(dump, "dump", torch.float32, device)
+        if tuple(dump.shape) != tuple(shape):
+            raise ValueError("dump must be %s" % list(shape))
+
+
 def workspace_bytes(batch: int, n_heads: int, head_dim: int, seq_len: int) -> int:
     return int(load_library().attn_decode_workspace_bytes(batch, n_heads, head_dim, seq_len))
 
@@ -169,6 +188,7 @@ def decode(q, k, v, current_pos: int, *, out=None, dump: bool = False, workspace
     sc = torch.empty((H, S), dtype=torch.float32, device=dev) if dump else None
     if workspace is None:
         workspace = alloc_workspace(1, H, D, S, dev)
+    _req_buf(workspace, "workspace", dev)
     with torch.cuda.device(dev):   # launch on the tensors' device
         _check(lib.attn_decode_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, D, S, int(current_pos),
                                    _ptr(sc), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -199,6 +219,7 @@ def decode_batched(q, k, v, current_pos, *, out=None, dump: bool = False, worksp
     sc = torch.empty((B, H, S), dtype=torch.float32, device=dev) if dump else None
     if workspace is None:
         workspace = alloc_workspace(B, H, D, S, dev)
+    _req_buf(workspace, "workspace", dev)
     with torch.cuda.device(dev):   # launch on the tensors' device
         _check(lib.attn_decode_f16_batched(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cp), B, H, D, S,
                                            _ptr(sc), _ptr(workspace),
@@ -227,6 +248,8 @@ def split(q, k, v, current_pos, workspace, *, dump=None, stream=None):
         raise ValueError("shape mismatch")
     cp_dev, cp_host = (None, int(current_pos)) if not isinstance(current_pos, torch.Tensor) \
         else (_cp_tensor(current_pos, B, k.device), 0)
+    _req_dump(dump, (B, H, S), k.device)
+    _req_buf(workspace, "workspace", k.device)
     with torch.cuda.device(k.device):   # launch on the tensors' device
         _check(lib.attn_decode_f16_split(_ptr(q3), _ptr(k4), _ptr(v4), _ptr(cp_dev), cp_host, B, H, D, S,
                                          _ptr(dump), _ptr(workspace),
@@ -240,6 +263,7 @@ def combine(out, current_pos, batch, n_heads, head_dim, seq_len, workspace, *, s
     _req(out, "out", torch.float16)
     cp_dev, cp_host = (None, int(current_pos)) if not isinstance(current_pos, torch.Tensor) \
         else (_cp_tensor(current_pos, batch, out.device), 0)
+    _req_buf(workspace, "workspace", out.device)
     with torch.cuda.device(out.device):   # launch on the tensors' device
         _check(lib.attn_decode_f16_combine(_ptr(out), _ptr(cp_dev), cp_host, batch, n_heads, head_dim,
                                            seq_len, _ptr(workspace),
@@ -279,9 +303,12 @@ def decode_paged(q, k_pool, v_pool, block_table, current_pos, *, out=None, dump=
     if out is None:
         out = torch.empty((B, H, D), dtype=torch.float16, device=dev)
     _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [batch, n_heads, head_dim]")
     sc = torch.empty((B, H, cap), dtype=torch.float32, device=dev) if dump else None
     if workspace is None:
         workspace = alloc_workspace(B, H, D, cap, dev)
+    _req_buf(workspace, "workspace", dev)
     with torch.cuda.device(dev):   # launch on the tensors' device
         _check(lib.attn_decode_f16_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
                                          _ptr(block_table), _ptr(cp), B, H, D, P, MB, NB, _ptr(sc),
@@ -295,6 +322,8 @@ def split_paged(q, k_pool, v_pool, block_table, current_pos, workspace, *, dump=
     max_blocks * page_size, workspace)` is the second."""
     lib = load_library()
     B, H, D, P, MB, NB, cp = _paged_args(q, k_pool, v_pool, block_table, current_pos)
+    _req_dump(dump, (B, H, P * MB), k_pool.device)
+    _req_buf(workspace, "workspace", k_pool.device)
     with torch.cuda.device(k_pool.device):   # launch on the tensors' device
         _check(lib.attn_decode_f16_paged_split(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                                _ptr(cp), B, H, D, P, MB, NB, _ptr(dump),
@@ -310,6 +339,8 @@ def qk(q, k, current_pos: int, *, scores=None, stream=None):
     _req(k, "k", torch.float16)
     dev = k.device
     _req(q, "q", torch.float16, dev)
+    if k.dim() != 3:
+        raise ValueError("k must be [seq_len, n_heads, head_dim]")
     S, H, D = k.shape
     if tuple(q.shape) != (H, D):
         raise ValueError("q must be [n_heads, head_dim]")
@@ -330,14 +361,19 @@ def pv(scores, v, current_pos: int, *, out=None, workspace=None, stream=None):
     _req(v, "v", torch.float16)
     dev = v.device
     _req(scores, "scores", torch.float16, dev)
+    if v.dim() != 3:
+        raise ValueError("v must be [seq_len, n_heads, head_dim]")
     S, H, D = v.shape
     if tuple(scores.shape) != (H, S):
         raise ValueError("scores must be [n_heads, seq_len]")
     if out is None:
         out = torch.empty((H, D), dtype=torch.float16, device=dev)
     _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != (H, D):
+        raise ValueError("out must be [n_heads, head_dim]")
     if workspace is None:
         workspace = alloc_workspace(1, H, D, S, dev)
+    _req_buf(workspace, "workspace", dev)
     with torch.cuda.device(dev):   # launch on the tensors' device
         _check(lib.attn_pv_f16(_ptr(scores), _ptr(v), _ptr(out), H, D, S, int(current_pos),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -387,6 +423,7 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, *, rope_dims=Non
     dims, base = _rope_params(rope_dims, D, rope_base)
     if workspace is None:
         workspace = alloc_workspace(B, H, D, S, dev)
+    _req_buf(workspace, "workspace", dev)
     ws_n = workspace.numel() * workspace.element_size()
     if batched:
         cp = _cp_tensor(current_pos, B, dev)
@@ -422,9 +459,12 @@ def decode_step_paged(q, k_new, v_new, k_pool, v_pool, block_table, current_pos,
     if out is None:
         out = torch.empty((B, H, D), dtype=torch.float16, device=dev)
     _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [batch, n_heads, head_dim]")
     dims, base = _rope_params(rope_dims, D, rope_base)
     if workspace is None:
         workspace = alloc_workspace(B, H, D, P * MB, dev)
+    _req_buf(workspace, "workspace", dev)
     with torch.cuda.device(dev):   # launch on the tensors' device
         _check(lib.attn_decode_step_f16_paged(
             _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out),
@@ -478,6 +518,7 @@ def softmax(x, *, out=None, workspace=None, stream=None):
         if n == 0:
             raise ValueError("invalid sizes")
         workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _req_buf(workspace, "workspace", x.device)
     with torch.cuda.device(x.device):   # launch on the tensors' device
         _check(lib.attn_softmax_f32(_ptr(x), _ptr(out), rows, cols, _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),

@@ -413,6 +413,42 @@ def test_side_stream():
     assert torch.equal(out, ref)
 
 
+def test_binding_rejects_host_and_misshaped_buffers():
+    """The library takes raw device pointers, so the binding refuses, before
+    any launch, caller buffers that are on the host, of the wrong dtype or
+    shape, or tensors of the wrong rank."""
+    rng = np.random.default_rng(16)
+    S, H, D = 300, 4, 64
+    q, k, v = to_dev(randn16(rng, (H, D))), to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
+    n = ad.workspace_bytes(1, H, D, S)
+    host_ws = torch.empty(n, dtype=torch.uint8)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError, match="workspace"):
+        ad.decode(q, k, v, S - 1, workspace=host_ws)
+    with pytest.raises(ValueError, match="workspace"):
+        ad.split(q, k, v, S - 1, host_ws)
+    with pytest.raises(TypeError, match="dump"):
+        ad.split(q, k, v, S - 1, ws, dump=torch.empty((1, H, S), dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError, match="dump"):
+        ad.split(q, k, v, S - 1, ws, dump=torch.empty((1, H, S - 1), dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError, match="workspace"):
+        ad.combine(torch.empty((H, D), dtype=torch.float16, device=DEV), S - 1, 1, H, D, S, host_ws)
+    with pytest.raises(ValueError, match="v must be"):
+        ad.pv(torch.empty((H, S), dtype=torch.float16, device=DEV), v.unsqueeze(0), S - 1)
+    with pytest.raises(ValueError, match="k must be"):
+        ad.qk(q, k.unsqueeze(0), S - 1)
+    x = torch.zeros((3, 5), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="workspace"):
+        ad.softmax(x, workspace=torch.empty(ad.softmax_workspace_bytes(3, 5) + 1, dtype=torch.uint8))
+    bt = torch.zeros((1, 2), dtype=torch.int32, device=DEV)
+    cp = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pool = to_dev(randn16(rng, (2, 16, H, D)))
+    with pytest.raises(ValueError, match="out must be"):
+        ad.decode_paged(q.unsqueeze(0), pool, pool, bt, cp,
+                        out=torch.empty((1, H, D + 1), dtype=torch.float16, device=DEV))
+    torch.cuda.synchronize()
+
+
 def test_workspace_errors_on_gpu():
     rng = np.random.default_rng(15)
     S, H, D = 1000, 4, 64
