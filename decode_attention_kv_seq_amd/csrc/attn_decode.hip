@@ -403,7 +403,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     // Position of block slot u of this lane's row group.  Row groups
     // interleave (slot u of every row group, then slot u + 1), except in
     // scores mode, where a row group takes U adjacent positions so that its
-    // leader writes their scores with one packed store.  Each load
+    // leader writes their scores to LDS with one packed store.  Each load
     // instruction still reads whole head blocks of single positions.
     auto pos_at = [&](uint32_t base, int u) -> uint32_t {
         return QK ? base + pg * U + u : base + u * pps + pg;
@@ -599,11 +599,15 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         const uint32_t d = idx % a.D;
         float M = -INFINITY;
         for (uint32_t r = 0; r < pps; ++r) M = fmaxf(M, sm_m[r * a.hpb + ho]);
-        // position lane 0 always saw position c0, so M is finite
+        // Position lane 0 always saw position c0, so M is finite unless every
+        // score here is a stored -inf (softmax.V from a masked stretch of the
+        // row); such a head merges to (-inf, 0, 0), which the combine weighs
+        // exactly 0, rather than to the NaN that 2^(-inf - -inf) would give.
+        const float Mu = M == -INFINITY ? 0.f : M;
         float o = 0.f, lsum = 0.f;
         for (uint32_t r = 0; r < pps; ++r) {
             const int gg = r * a.hpb + ho;
-            const float w = __builtin_amdgcn_exp2f(sm_m[gg] - M);
+            const float w = __builtin_amdgcn_exp2f(sm_m[gg] - Mu);
             o = fmaf(sm_o[gg * DPAD + d], w, o);
             lsum = fmaf(sm_l[gg], w, lsum);
         }

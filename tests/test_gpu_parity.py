@@ -658,6 +658,24 @@ def test_pv_from_stored_scores(shape):
     assert_close(out, ref, str(shape))
 
 
+@pytest.mark.parametrize("S,H,D,lo,hi", [(20000, 4, 64, 0, 12000), (20001, 8, 128, 3000, 19000),
+                                         (5000, 3, 48, 0, 4990), (70000, 2, 64, 10, 65000)],
+                         ids=lambda x: str(x))
+def test_pv_with_long_masked_stretch(S, H, D, lo, hi):
+    """Second dispatch on score rows that are -inf over [lo, hi), a stretch
+    far longer than a chunk (a sliding-window mask, say), with NaN V there:
+    chunks made only of -inf scores must weigh nothing."""
+    rng = np.random.default_rng(S + lo + hi)
+    sc = randn16(rng, (H, S), 2.0)
+    sc[:, lo:hi] = -np.inf
+    v = randn16(rng, (S, H, D))
+    v[lo:hi] = np.nan
+    ref = oracle.pv_from_scores(sc, v, S - 1)
+    out = ad.pv(to_dev(sc), to_dev(v), S - 1)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "masked [%d, %d) of %d" % (lo, hi, S))
+
+
 def test_two_dispatches_against_fp16_score_reading():
     """QK then PV on the GPU equals softmax.V of the oracle's scores rounded to
     fp16 (the page's two-dispatch design stores fp16 scores), within the bar."""
