@@ -1,6 +1,7 @@
 """Seeded random configurations through every entry point, against the
 oracle: head_dim 1..256 (every lane layout), odd head counts, ragged and
-out-of-range lengths, page sizes, rotation settings, unaligned tensors.
+out-of-range lengths, page sizes, rotation settings, unaligned tensors,
+stored score rows with -inf stretches.
 Each case prints its parameters before it runs.  Bars as in the other GPU
 tests: |gpu - oracle| <= 2e-3 + 4e-3 |oracle| for fp16 outputs; the rotation
 and softmax bars of test_gpu_decode_step.py and test_gpu_softmax.py."""
@@ -146,6 +147,36 @@ def test_random_two_dispatch(case):
     out = ad.pv(torch.from_numpy(s16).to(DEV), torch.from_numpy(v).to(DEV), cp)
     torch.cuda.synchronize()
     close(out, ref, "two dispatches case %d" % case)
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_masked_score_rows(case):
+    """Second dispatch on fp16 score rows with random -inf stretches (some far
+    longer than a chunk) and holes, NaN V under them; at least one finite
+    score per head."""
+    rng = np.random.default_rng(6000 + case)
+    D, H, _ = shape_draw(rng)
+    S = int(rng.choice([50, 1000, 5000, 20000, 40001]))
+    cp = int(rng.integers(0, S + 2))
+    L = min(cp, S - 1) + 1
+    print("case", case, dict(S=S, H=H, D=D, cp=cp), flush=True)
+    sc = randn16(rng, (H, S), float(rng.choice([1.0, 3.0])))
+    v = randn16(rng, (S, H, D))
+    masked = np.zeros((H, S), dtype=bool)
+    for _ in range(int(rng.integers(1, 4))):
+        lo = int(rng.integers(0, L))
+        hi = int(rng.integers(lo, L + 1))
+        masked[:, lo:hi] = True
+    masked[:, rng.integers(0, L, size=int(rng.integers(0, 6)))] = True
+    for h in range(H):                        # keep one finite score per head
+        if masked[h, :L].all():
+            masked[h, int(rng.integers(0, L))] = False
+    sc[masked] = -np.inf
+    v[masked.T] = np.nan                      # V of (position, head) pairs never weighed
+    ref = oracle.pv_from_scores(sc, v, cp)
+    out = ad.pv(torch.from_numpy(sc).to(DEV), torch.from_numpy(v).to(DEV), cp)
+    torch.cuda.synchronize()
+    close(out, ref, "masked score rows case %d" % case)
 
 
 @pytest.mark.parametrize("case", range(N_CASES))
