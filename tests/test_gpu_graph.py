@@ -97,3 +97,72 @@ def test_graph_decode_step_and_softmax():
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(kc, e_k) and torch.equal(vc, e_v)
+
+
+def test_graph_paged_and_two_dispatches():
+    rng = np.random.default_rng(3)
+    B, P, MB, H, D = 3, 16, 8, 8, 64
+    NB = B * MB + 5
+    q = torch.from_numpy(rng.standard_normal((B, H, D)).astype(np.float16)).to(DEV)
+    kp = torch.from_numpy(rng.standard_normal((NB, P, H, D)).astype(np.float16)).to(DEV)
+    vp = torch.from_numpy(rng.standard_normal((NB, P, H, D)).astype(np.float16)).to(DEV)
+    bt = torch.from_numpy(rng.permutation(NB)[: B * MB].reshape(B, MB).astype(np.int32)).to(DEV)
+    cp = torch.tensor([5, P * MB - 1, 77], dtype=torch.int32, device=DEV)
+    wsp = ad.alloc_workspace(B, H, D, P * MB, DEV)
+    S, cp1 = 4000, 3210
+    q1 = torch.from_numpy(rng.standard_normal((H, D)).astype(np.float16)).to(DEV)
+    k1 = torch.from_numpy(rng.standard_normal((S, H, D)).astype(np.float16)).to(DEV)
+    v1 = torch.from_numpy(rng.standard_normal((S, H, D)).astype(np.float16)).to(DEV)
+    ws1 = ad.alloc_workspace(1, H, D, S, DEV)
+    e_p = ad.decode_paged(q, kp, vp, bt, cp, workspace=wsp).clone()
+    e_sc = ad.qk(q1, k1, cp1).clone()
+    e_o = ad.pv(e_sc, v1, cp1, workspace=ws1).clone()
+    out_p = torch.empty((B, H, D), dtype=torch.float16, device=DEV)
+    sc = torch.empty((H, S), dtype=torch.float16, device=DEV)
+    out1 = torch.empty((H, D), dtype=torch.float16, device=DEV)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ad.decode_paged(q, kp, vp, bt, cp, out=out_p, workspace=wsp)
+        ad.qk(q1, k1, cp1, scores=sc)
+        ad.pv(sc, v1, cp1, out=out1, workspace=ws1)
+
+    def disturb():
+        ad.decode_paged(q, kp, vp, bt, torch.zeros_like(cp), workspace=wsp)
+        ad.pv(torch.zeros_like(e_sc), v1, 10, workspace=ws1)
+
+    replay_and_check(g, [out_p, sc, out1], [e_p, e_sc, e_o], disturb)
+
+
+def test_two_streams_at_once():
+    """Calls enqueued on two streams at once, each stream with its own
+    workspace, give the bits of the same calls run one after another: the
+    library keeps no state across calls."""
+    rng = np.random.default_rng(4)
+    S, H, D, cp = 20000, 8, 128, 19000
+    q = torch.from_numpy(rng.standard_normal((H, D)).astype(np.float16)).to(DEV)
+    k = torch.from_numpy(rng.standard_normal((S, H, D)).astype(np.float16)).to(DEV)
+    v = torch.from_numpy(rng.standard_normal((S, H, D)).astype(np.float16)).to(DEV)
+    B, Sb, Hb, Db = 6, 3000, 4, 64
+    qb = torch.from_numpy(rng.standard_normal((B, Hb, Db)).astype(np.float16)).to(DEV)
+    kb = torch.from_numpy(rng.standard_normal((B, Sb, Hb, Db)).astype(np.float16)).to(DEV)
+    vb = torch.from_numpy(rng.standard_normal((B, Sb, Hb, Db)).astype(np.float16)).to(DEV)
+    cpb = torch.from_numpy(rng.integers(0, Sb, B).astype(np.int32)).to(DEV)
+    ws1 = ad.alloc_workspace(1, H, D, S, DEV)
+    ws2 = ad.alloc_workspace(B, Hb, Db, Sb, DEV)
+    e1 = ad.decode(q, k, v, cp, workspace=ws1).clone()
+    e2 = ad.decode_batched(qb, kb, vb, cpb, workspace=ws2).clone()
+    n = 12
+    outs1 = [torch.empty((H, D), dtype=torch.float16, device=DEV) for _ in range(n)]
+    outs2 = [torch.empty((B, Hb, Db), dtype=torch.float16, device=DEV) for _ in range(n)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for i in range(n):
+        with torch.cuda.stream(s1):
+            ad.decode(q, k, v, cp, out=outs1[i], workspace=ws1)
+        with torch.cuda.stream(s2):
+            ad.decode_batched(qb, kb, vb, cpb, out=outs2[i], workspace=ws2)
+    torch.cuda.synchronize()
+    for i in range(n):
+        assert torch.equal(outs1[i], e1), "stream 1 call %d" % i
+        assert torch.equal(outs2[i], e2), "stream 2 call %d" % i
