@@ -63,6 +63,8 @@ SHAPES = [  # rows, cols: the plan takes a wave per row up to 1024 columns, a
     (1, 1), (1, 2), (3, 7), (5, 64), (7, 1000), (4, 1024), (4, 1025), (300, 4096), (2, 8192),
     (3, 8193), (2, 16385), (2, 32768), (300, 1030), (2, 32769), (64, 40000), (100, 30000),
     (1, 300001), (3, 4097), (260, 20000),
+    # long rows, 64-100 of them (split path; odd widths take scalar loads)
+    (64, 262143), (64, 262144), (64, 131072), (70, 65536), (100, 32769), (64, 40001),
 ]
 
 
@@ -77,11 +79,11 @@ def test_softmax_shapes(shape):
     check(got, x, str(shape))
 
 
-@pytest.mark.parametrize("offset,cols", [(1, 64), (1, 5000), (2, 1024), (3, 40000)])
-def test_softmax_unaligned(offset, cols):
+@pytest.mark.parametrize("offset,cols,rows", [(1, 64, 5), (1, 5000, 5), (2, 1024, 5), (3, 40000, 5),
+                                              (1, 70000, 64)])
+def test_softmax_unaligned(offset, cols, rows):
     """Rows not 16-byte aligned (scalar loads): a view offset by whole floats."""
     rng = np.random.default_rng(offset + cols)
-    rows = 5
     base = torch.from_numpy(rng.standard_normal(rows * cols + offset).astype(np.float32)).to(DEV)
     x = base[offset:].view(rows, cols)
     out_base = torch.empty(rows * cols + offset, dtype=torch.float32, device=DEV)
@@ -91,12 +93,12 @@ def test_softmax_unaligned(offset, cols):
     check(out, x.cpu().numpy(), "offset %d" % offset)
 
 
+@pytest.mark.parametrize("rows", [8, 64])
 @pytest.mark.parametrize("cols", [100, 5000, 40000, 100000])
-def test_softmax_masked_rows(cols):
-    """-inf tails (whole -inf chunks on the split path), a row of -inf only,
-    a row with a NaN, a row with +inf, a single finite entry."""
-    rng = np.random.default_rng(cols)
-    rows = 8
+def test_softmax_masked_rows(cols, rows):
+    """-inf tails (whole -inf chunks on the split path), a row of -inf only, a
+    row with a NaN, a row with +inf, a single finite entry; 8 or 64 rows."""
+    rng = np.random.default_rng(cols + rows)
     x = rng.standard_normal((rows, cols)).astype(np.float32)
     x[0, cols // 3:] = -np.inf
     x[1, :] = -np.inf
@@ -110,7 +112,7 @@ def test_softmax_masked_rows(cols):
     assert np.all(np.isnan(g[1])) and np.all(np.isnan(g[2])) and np.all(np.isnan(g[4]))
     assert g[3, 0] == 1.0 and np.all(g[3, 1:] == 0.0)
     assert g[5, -1] == 1.0 and np.all(g[5, :-1] == 0.0)
-    keep = [0, 3, 5, 6, 7]
+    keep = [0, 3, 5] + list(range(6, rows))
     check(got[keep], np.ascontiguousarray(x[keep]), "masked cols=%d" % cols)
 
 
@@ -128,7 +130,7 @@ def test_softmax_workloads_full(name):
 
 def test_softmax_in_place_and_repeatable():
     rng = np.random.default_rng(11)
-    for shape in [(300, 4096), (4, 100000), (50, 700)]:
+    for shape in [(300, 4096), (4, 100000), (50, 700), (64, 100000)]:
         x_h = (rng.standard_normal(shape) * 2).astype(np.float32)
         x = torch.from_numpy(x_h).to(DEV)
         a = ad.softmax(x)
