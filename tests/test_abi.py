@@ -4,6 +4,7 @@ host before any HIP call (no kernel is launched by these tests)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -243,3 +244,18 @@ def test_paged_step_rejects_bad_arguments(lib):
     assert call(base=-1.0) == DIM
     assert call(out=FAKE + 1) == ALIGN
     assert call(wsb=16) == WS
+
+
+def test_header_and_library_from_c(tmp_path):
+    """tests/c/abi_from_c.c, a strict C99 program (gcc -std=c99 -pedantic
+    -Werror) that includes the header, links the library and checks its
+    host-side answers; none of its calls reaches the GPU."""
+    lib_dir = os.path.dirname(ad.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c", "abi_from_c.c"),
+           "-o", exe, "-L", lib_dir, "-lattn_decode", "-Wl,-rpath," + lib_dir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
