@@ -259,3 +259,26 @@ def test_header_and_library_from_c(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+def test_missing_library_is_an_error():
+    """No fallback: without the built library the binding raises ImportError."""
+    saved = ad._lib
+    ad._lib = None
+    try:
+        with pytest.raises(ImportError, match="not built"):
+            ad.load_library(os.path.join(ROOT, "no_such_dir", "libattn_decode.so"))
+    finally:
+        ad._lib = saved
+
+
+def test_host_tensors_are_refused():
+    """Every call needs GPU tensors; host tensors are an error, never
+    computed some other way."""
+    import torch
+    q = torch.zeros((4, 64), dtype=torch.float16)
+    k = torch.zeros((128, 4, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ad.decode(q, k, k, 100)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ad.softmax(torch.zeros((2, 8), dtype=torch.float32))
