@@ -1182,7 +1182,12 @@ const Knobs &env_knobs() {
 // double buffering to keep as many bytes in flight.  The scores pass has its
 // own row: it writes as it reads, and its best head blocking and unroll
 // differ.
-enum class Kind { single, batched, paged, stream, batched_chunked, scores };
+// A single sequence of head_dim > 64 that streams at most kShortSpan
+// positions takes one head per workgroup: with so few positions per chunk
+// the narrower head block wins (4096 positions: 16.5 against 18.6 us; 8192:
+// 27.2 against 27.9; from 16384 on it loses).
+enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short };
+constexpr uint32_t kShortSpan = 8192;
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
@@ -1193,6 +1198,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     else if (kind == Kind::batched_chunked) k = Knobs{256, 8192, 4, 2, 1, 0};
     else if (kind == Kind::stream) k = D <= 64 ? Knobs{1024, 8192, 8, 2, 1, 0} : Knobs{1024, 8192, 2, 2, 1, 0};
     else if (kind == Kind::scores) k = D <= 64 ? Knobs{1024, 8192, 4, 2, 1, 0} : Knobs{1024, 8192, 4, 8, 1, 0};
+    else if (kind == Kind::single_short && D > 64) k = Knobs{512, 8192, 1, 2, 0, 0};
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
     else k = Knobs{512, 8192, 2, 2, 1, 0};                             // 256-byte rows and wider
     const Knobs &e = env_knobs();
@@ -1266,7 +1272,8 @@ uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S)
 // depends on sizes only.
 uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     uint32_t m = 0;
-    for (Kind kd : {Kind::single, Kind::batched, Kind::paged, Kind::stream, Kind::batched_chunked}) {
+    for (Kind kd : {Kind::single, Kind::single_short, Kind::batched, Kind::paged, Kind::stream,
+                    Kind::batched_chunked}) {
         const uint32_t c = chunk_bound_for(knobs(D, kd), batch, H, S);
         if (c > m) m = c;
     }
@@ -1303,7 +1310,8 @@ size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
     if (batch > kBalancedMaxBatch) return 0;
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     size_t m = 0;
-    for (Kind kd : {Kind::single, Kind::batched, Kind::paged, Kind::stream, Kind::batched_chunked}) {
+    for (Kind kd : {Kind::single, Kind::single_short, Kind::batched, Kind::paged, Kind::stream,
+                    Kind::batched_chunked}) {
         const Knobs k = knobs(D, kd);
         const size_t n = (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
         if (n > m) m = n;
@@ -1441,7 +1449,13 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
                            const Paging *pg, hipStream_t stream, bool *wrote_out,
                            const uint16_t *scores_in = nullptr, const RopeArgs *rope = nullptr) {
     const Layout ly = scores_in ? choose_layout(D, v, v, v) : choose_layout(D, q, k, v);
-    Kind kind = scores_in ? Kind::stream : pg ? Kind::paged : cp_dev ? Kind::batched : Kind::single;
+    // host current_pos: plan the exact span (a decode step streams one
+    // position less; at least one chunk is launched, so the header is
+    // written); device array: plan the capacity
+    uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1 - (rope ? 1u : 0u);
+    if (span == 0) span = 1;
+    Kind kind = scores_in ? Kind::stream : pg ? Kind::paged : cp_dev ? Kind::batched
+              : (D > 64 && span <= kShortSpan) ? Kind::single_short : Kind::single;
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
@@ -1461,11 +1475,6 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
              : (dump ? pick_split<true, false, kModeDecode>(ly, kn, bal)
                      : pick_split<false, false, kModeDecode>(ly, kn, bal));
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
-    // host current_pos: plan the exact span (a decode step streams one
-    // position less; at least one chunk is launched, so the header is
-    // written); device array: plan the capacity
-    uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1 - (rope ? 1u : 0u);
-    if (span == 0) span = 1;
     const Plan plan = make_plan(batch, H, D, S, span, kind);
     const WsLayout wl = workspace_layout(batch, H, D, S);
 
