@@ -1186,7 +1186,11 @@ const Knobs &env_knobs() {
 // positions takes one head per workgroup: with so few positions per chunk
 // the narrower head block wins (4096 positions: 16.5 against 18.6 us; 8192:
 // 27.2 against 27.9; from 16384 on it loses).
-enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short };
+// A decode step of such a sequence over more positions than that wants
+// fewer workgroups than the plain decode, one per CU (32 heads x 32768
+// positions: 83.4 against 87.5 us; 64 x 16384: 88.9 against 94.9; head_dim
+// 256: 89.8 against 95.5).
+enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short, single_step };
 constexpr uint32_t kShortSpan = 8192;
 
 Knobs knobs(uint32_t D, Kind kind) {
@@ -1199,6 +1203,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     else if (kind == Kind::stream) k = D <= 64 ? Knobs{1024, 8192, 8, 2, 1, 0} : Knobs{1024, 8192, 2, 2, 1, 0};
     else if (kind == Kind::scores) k = D <= 64 ? Knobs{1024, 8192, 4, 2, 1, 0} : Knobs{1024, 8192, 4, 8, 1, 0};
     else if (kind == Kind::single_short && D > 64) k = Knobs{512, 8192, 1, 2, 0, 0};
+    else if (kind == Kind::single_step && D > 64) k = Knobs{256, 8192, 2, 2, 1, 0};
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
     else k = Knobs{512, 8192, 2, 2, 1, 0};                             // 256-byte rows and wider
     const Knobs &e = env_knobs();
@@ -1272,8 +1277,8 @@ uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S)
 // depends on sizes only.
 uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     uint32_t m = 0;
-    for (Kind kd : {Kind::single, Kind::single_short, Kind::batched, Kind::paged, Kind::stream,
-                    Kind::batched_chunked}) {
+    for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::batched, Kind::paged,
+                    Kind::stream, Kind::batched_chunked}) {
         const uint32_t c = chunk_bound_for(knobs(D, kd), batch, H, S);
         if (c > m) m = c;
     }
@@ -1310,8 +1315,8 @@ size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
     if (batch > kBalancedMaxBatch) return 0;
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     size_t m = 0;
-    for (Kind kd : {Kind::single, Kind::single_short, Kind::batched, Kind::paged, Kind::stream,
-                    Kind::batched_chunked}) {
+    for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::batched, Kind::paged,
+                    Kind::stream, Kind::batched_chunked}) {
         const Knobs k = knobs(D, kd);
         const size_t n = (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
         if (n > m) m = n;
@@ -1455,7 +1460,8 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1 - (rope ? 1u : 0u);
     if (span == 0) span = 1;
     Kind kind = scores_in ? Kind::stream : pg ? Kind::paged : cp_dev ? Kind::batched
-              : (D > 64 && span <= kShortSpan) ? Kind::single_short : Kind::single;
+              : (D > 64 && span <= kShortSpan) ? Kind::single_short
+              : (D > 64 && rope) ? Kind::single_step : Kind::single;
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
