@@ -1186,10 +1186,11 @@ const Knobs &env_knobs() {
 // positions takes one head per workgroup: with so few positions per chunk
 // the narrower head block wins (4096 positions: 16.5 against 18.6 us; 8192:
 // 27.2 against 27.9; from 16384 on it loses).
-// A decode step of such a sequence over more positions than that wants
-// fewer workgroups than the plain decode, one per CU (32 heads x 32768
-// positions: 83.4 against 87.5 us; 64 x 16384: 88.9 against 94.9; head_dim
-// 256: 89.8 against 95.5).
+// A decode step over more positions than that, with 256-byte rows (head_dim
+// 128), wants fewer workgroups than the plain decode, one per CU (32 heads x
+// 32768 positions: 83.4 against 87.5 us; 64 x 16384: 88.9 against 94.9); at
+// head_dim 192 it loses (82.4 against 73.2 us), and head_dim 256 does as
+// well on its own row.
 enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short, single_step };
 constexpr uint32_t kShortSpan = 8192;
 
@@ -1205,7 +1206,12 @@ Knobs knobs(uint32_t D, Kind kind) {
     else if (kind == Kind::single_short && D > 64) k = Knobs{512, 8192, 1, 2, 0, 0};
     else if (kind == Kind::single_step && D > 64) k = Knobs{256, 8192, 2, 2, 1, 0};
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
-    else k = Knobs{512, 8192, 2, 2, 1, 0};                             // 256-byte rows and wider
+    else if (D < 256) k = Knobs{512, 8192, 2, 2, 1, 0};                // 256- to 510-byte rows
+    // 512-byte rows (head_dim 256): one head is already a 512-byte read, and
+    // one head per workgroup with more workgroups beats wider blocks (16
+    // heads x 32768 positions: 84.0 against 110.9 us; at head_dim 192 two
+    // heads per workgroup stay better, 70.2 against 73.3 us).
+    else k = Knobs{1024, 8192, 1, 2, 1, 0};
     const Knobs &e = env_knobs();
     if (e.wgs) k.wgs = e.wgs;
     if (e.cmax) k.cmax = e.cmax;
@@ -1461,7 +1467,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     if (span == 0) span = 1;
     Kind kind = scores_in ? Kind::stream : pg ? Kind::paged : cp_dev ? Kind::batched
               : (D > 64 && span <= kShortSpan) ? Kind::single_short
-              : (D > 64 && rope) ? Kind::single_step : Kind::single;
+              : (D > 64 && D <= 128 && rope) ? Kind::single_step : Kind::single;
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
