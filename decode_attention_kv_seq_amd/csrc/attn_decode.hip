@@ -1212,6 +1212,12 @@ Knobs knobs(uint32_t D, Kind kind) {
     // heads x 32768 positions: 84.0 against 110.9 us; at head_dim 192 two
     // heads per workgroup stay better, 70.2 against 73.3 us).
     else k = Knobs{1024, 8192, 1, 2, 1, 0};
+    // Head blocks on whole 128-byte cache lines: a block that ends mid-line
+    // shares that line with the next head block, whose workgroup (on another
+    // XCD, so another L2) fetches it again.  Rows of 64, 96, 128 or 256
+    // values already fit; head_dim 80 moves from 2 heads (320 bytes) to 4
+    // (640 bytes): 32 heads x 32768 positions 70.0 -> 58.5 us.
+    while (k.hpb < kMaxHeadsPerWG && (k.hpb * D * 2) % 128 != 0) k.hpb <<= 1;
     const Knobs &e = env_knobs();
     if (e.wgs) k.wgs = e.wgs;
     if (e.cmax) k.cmax = e.cmax;
