@@ -1191,8 +1191,17 @@ const Knobs &env_knobs() {
 // 32768 positions: 83.4 against 87.5 us; 64 x 16384: 88.9 against 94.9); at
 // head_dim 192 it loses (82.4 against 73.2 us), and head_dim 256 does as
 // well on its own row.
-enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short, single_step };
+// A single sequence short enough that one workgroup per head block streams
+// its whole span in about the time a combine launch costs (<= 256 KiB of K+V
+// per workgroup) takes one chunk per head block, double-buffered so that its
+// blocks' loads are in flight together: the split launch then writes the
+// output itself (4 heads x 101 positions: 3.7 us with the cache in the
+// caches, 4.9 us from DRAM, against 9.0 us for 16-position chunks and a
+// combine).
+enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short, single_step,
+                  single_tiny };
 constexpr uint32_t kShortSpan = 8192;
+constexpr uint64_t kOneChunkBytes = 256u << 10;
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
@@ -1205,6 +1214,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     else if (kind == Kind::scores) k = D <= 64 ? Knobs{1024, 8192, 4, 2, 1, 0} : Knobs{1024, 8192, 4, 8, 1, 0};
     else if (kind == Kind::single_short && D > 64) k = Knobs{512, 8192, 1, 2, 0, 0};
     else if (kind == Kind::single_step && D > 64) k = Knobs{256, 8192, 2, 2, 1, 0};
+    else if (kind == Kind::single_tiny) k = D <= 64 ? Knobs{1024, 8192, 4, 8, 1, 0} : Knobs{512, 8192, 1, 2, 1, 0};
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
     else if (D < 256) k = Knobs{512, 8192, 2, 2, 1, 0};                // 256- to 510-byte rows
     // 512-byte rows (head_dim 256): one head is already a 512-byte read, and
@@ -1289,8 +1299,8 @@ uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S)
 // depends on sizes only.
 uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     uint32_t m = 0;
-    for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::batched, Kind::paged,
-                    Kind::stream, Kind::batched_chunked}) {
+    for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::single_tiny, Kind::batched,
+                    Kind::paged, Kind::stream, Kind::batched_chunked}) {
         const uint32_t c = chunk_bound_for(knobs(D, kd), batch, H, S);
         if (c > m) m = c;
     }
@@ -1306,6 +1316,7 @@ Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span
     const uint64_t n_hb = H / heads_per_wg(H, best, k.hpb);
     const uint64_t nt = cdiv(k.wgs, (uint64_t)batch * n_hb);
     uint64_t c = cdiv(cdiv(span, nt), kChunkGranule) * kChunkGranule;
+    if (kind == Kind::single_tiny) c = cdiv(span, kChunkGranule) * kChunkGranule;   // one chunk
     if (c > k.cmax) c = k.cmax;
     if (c < kChunkGranule) c = kChunkGranule;
     Plan p;
@@ -1327,8 +1338,8 @@ size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
     if (batch > kBalancedMaxBatch) return 0;
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     size_t m = 0;
-    for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::batched, Kind::paged,
-                    Kind::stream, Kind::batched_chunked}) {
+    for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::single_tiny, Kind::batched,
+                    Kind::paged, Kind::stream, Kind::batched_chunked}) {
         const Knobs k = knobs(D, kd);
         const size_t n = (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
         if (n > m) m = n;
@@ -1474,6 +1485,11 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     Kind kind = scores_in ? Kind::stream : pg ? Kind::paged : cp_dev ? Kind::batched
               : (D > 64 && span <= kShortSpan) ? Kind::single_short
               : (D > 64 && D <= 128 && rope) ? Kind::single_step : Kind::single;
+    if (!scores_in && !pg && !cp_dev) {
+        const uint32_t tiny_hpb = heads_per_wg(H, choose_layout(D, nullptr, nullptr, nullptr),
+                                               knobs(D, Kind::single_tiny).hpb);
+        if ((uint64_t)span * tiny_hpb * D * 4 <= kOneChunkBytes) kind = Kind::single_tiny;
+    }
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
