@@ -1198,10 +1198,20 @@ const Knobs &env_knobs() {
 // output itself (4 heads x 101 positions: 3.7 us with the cache in the
 // caches, 4.9 us from DRAM, against 9.0 us for 16-position chunks and a
 // combine).
+// A batch (device lengths, contiguous or paged) whose capacity is that short
+// for one 256-byte head block takes the same plan: one chunk per sequence and
+// head block on the chunked grid, written out directly.  The balanced grid's
+// workgroups walk many short pieces one after another there, each with its
+// own query load and partial, and a combine follows (64 sequences x 32 heads
+// x 128 positions: 36.5 -> 15.9 us; 1024 x 32 x 32: 161.7 -> 50.7; 2 x 8 x
+// 512: 12.7 -> 4.9).  Many head blocks want wider blocks: at most
+// kShortGroups workgroups (1024 x 32 heads x 32 positions: 72.5 us at 32768,
+// 50.7 at 16384, 50.3 at 8192).
 enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short, single_step,
-                  single_tiny };
+                  single_tiny, batched_short };
 constexpr uint32_t kShortSpan = 8192;
 constexpr uint64_t kOneChunkBytes = 256u << 10;
+constexpr uint64_t kShortGroups = 8192;
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
@@ -1215,6 +1225,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     else if (kind == Kind::single_short && D > 64) k = Knobs{512, 8192, 1, 2, 0, 0};
     else if (kind == Kind::single_step && D > 64) k = Knobs{256, 8192, 2, 2, 1, 0};
     else if (kind == Kind::single_tiny) k = D <= 64 ? Knobs{1024, 8192, 4, 8, 1, 0} : Knobs{512, 8192, 1, 2, 1, 0};
+    else if (kind == Kind::batched_short) k = D <= 64 ? Knobs{256, 8192, 2, 2, 1, 0} : Knobs{256, 8192, 1, 2, 1, 0};
     else if (D <= 64) k = Knobs{1024, 8192, 4, 8, 0, 0};               // 128-byte rows
     else if (D < 256) k = Knobs{512, 8192, 2, 2, 1, 0};                // 256- to 510-byte rows
     // 512-byte rows (head_dim 256): one head is already a 512-byte read, and
@@ -1300,7 +1311,7 @@ uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S)
 uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     uint32_t m = 0;
     for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::single_tiny, Kind::batched,
-                    Kind::paged, Kind::stream, Kind::batched_chunked}) {
+                    Kind::paged, Kind::stream, Kind::batched_chunked, Kind::batched_short}) {
         const uint32_t c = chunk_bound_for(knobs(D, kd), batch, H, S);
         if (c > m) m = c;
     }
@@ -1316,7 +1327,8 @@ Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span
     const uint64_t n_hb = H / heads_per_wg(H, best, k.hpb);
     const uint64_t nt = cdiv(k.wgs, (uint64_t)batch * n_hb);
     uint64_t c = cdiv(cdiv(span, nt), kChunkGranule) * kChunkGranule;
-    if (kind == Kind::single_tiny) c = cdiv(span, kChunkGranule) * kChunkGranule;   // one chunk
+    if (kind == Kind::single_tiny || kind == Kind::batched_short)   // one chunk
+        c = cdiv(span, kChunkGranule) * kChunkGranule;
     if (c > k.cmax) c = k.cmax;
     if (c < kChunkGranule) c = kChunkGranule;
     Plan p;
@@ -1339,7 +1351,7 @@ size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     size_t m = 0;
     for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::single_tiny, Kind::batched,
-                    Kind::paged, Kind::stream, Kind::batched_chunked}) {
+                    Kind::paged, Kind::stream, Kind::batched_chunked, Kind::batched_short}) {
         const Knobs k = knobs(D, kd);
         const size_t n = (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
         if (n > m) m = n;
@@ -1490,8 +1502,19 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
                                                knobs(D, Kind::single_tiny).hpb);
         if ((uint64_t)span * tiny_hpb * D * 4 <= kOneChunkBytes) kind = Kind::single_tiny;
     }
+    if (kind == Kind::batched || kind == Kind::paged) {
+        const uint32_t short_hpb = heads_per_wg(H, choose_layout(D, nullptr, nullptr, nullptr),
+                                                knobs(D, Kind::batched_short).hpb);
+        if ((uint64_t)S * short_hpb * D * 4 <= kOneChunkBytes) kind = Kind::batched_short;
+    }
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
+    if (kind == Kind::batched_short)
+        for (uint32_t w = hpb * 2; (uint64_t)batch * (H / hpb) > kShortGroups && w <= H; w *= 2) {
+            const uint32_t h = heads_per_wg(H, ly, w);
+            if (h == hpb) break;
+            hpb = h;
+        }
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores_in && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);

@@ -338,9 +338,13 @@ def test_batched_matches_single_calls():
         assert_close(out[b], single.float().cpu().numpy(), "batched vs single b=%d" % b)
 
 
-def test_many_short_sequences():
+@pytest.mark.parametrize("S", [40, 600])
+def test_many_short_sequences(S):
+    """300 sequences of at most 45 positions.  A capacity of 40 takes one chunk
+    per sequence and head block; one of 600 the balanced grid, whose
+    workgroups then walk many short pieces each."""
     rng = np.random.default_rng(12)
-    B, S, H, D = 300, 40, 2, 64
+    B, H, D = 300, 2, 64
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
     pos = rng.integers(0, 45, B)
     cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
@@ -491,11 +495,13 @@ def test_batched_extreme_ragged_lengths():
         assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "b=%d" % b)
 
 
-def test_batched_more_sequences_than_balanced_grid_handles():
+@pytest.mark.parametrize("S", [24, 2100])
+def test_batched_more_sequences_than_balanced_grid_handles(S):
     """1100 short sequences: past the balanced grid's batch limit the chunked
-    grid serves the call."""
+    grid serves the call (a capacity of 24 with the short-capacity plan, one
+    of 2100 with the plain chunked plan)."""
     rng = np.random.default_rng(32)
-    B, S, H, D = 1100, 24, 2, 16
+    B, H, D = 1100, 2, 16
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
     pos = rng.integers(0, 30, B)
     cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
@@ -503,6 +509,24 @@ def test_batched_more_sequences_than_balanced_grid_handles():
     torch.cuda.synchronize()
     ref, _ = oracle.decode_batched(q, k, v, pos)
     assert_close(out, ref, "1100 sequences")
+
+
+def test_short_capacity_batch_with_many_head_blocks():
+    """512 sequences x 32 heads of head_dim 128 with a 16-position capacity:
+    one chunk per sequence and head block, and head blocks widened so that
+    the launch stays within its workgroup budget.  Every output row against
+    the oracle, with zero-length and past-capacity sequences among them."""
+    rng = np.random.default_rng(33)
+    B, S, H, D = 512, 16, 32, 128
+    q, k, v = randn16(rng, (B, H, D), 2.0), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, S, B)
+    pos[::5] = 0
+    pos[1::9] = S + 100
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_batched(q, k, v, pos, threads=8)
+    assert_close(out, ref, "512 x 32 heads, capacity 16")
 
 
 # ------------------------------------------------------------ paged cache
@@ -588,9 +612,12 @@ def test_paged_shared_pages_and_unused_table_entries():
     assert_close(out, ref, "shared pages")
 
 
-def test_paged_split_then_combine_and_many_sequences():
+@pytest.mark.parametrize("S", [32, 600])
+def test_paged_split_then_combine_and_many_sequences(S):
+    """1030 sequences, past the balanced grid's batch limit: a capacity of 32
+    takes the short-capacity plan, one of 600 the plain chunked plan."""
     rng = np.random.default_rng(44)
-    B, S, H, D, P = 1030, 32, 2, 64, 8   # past the balanced grid's batch limit
+    B, H, D, P = 1030, 2, 64, 8
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
     pos = rng.integers(0, 40, B)
     cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
