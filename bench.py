@@ -138,16 +138,30 @@ def cpu_baseline(w, seconds: float, path: str = "fused"):
             reps += 1
             dt = time.perf_counter() - t0
     total_bytes *= reps
+    # the same oracle on one thread: whole units of the sample, about 1/8 of
+    # the time budget, repeated for small workloads as above
+    n1 = max(1, min(len(sample), int(seconds / 8 / max(t1, 1e-6))))
+    reps1, dt1 = 0, 0.0
+    t0 = time.perf_counter()
+    while reps1 == 0 or (dt1 < seconds / 16 and reps1 < 10000):
+        for s1 in sample[:n1]:
+            run(s1)
+        reps1 += 1
+        dt1 = time.perf_counter() - t0
+    bytes1 = sum(s1[4] for s1 in sample[:n1]) * reps1
     return {
         "value": round(total_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
+        "value_1thread": round(bytes1 / dt1 / 1e9, 4),
         "sample": "%d of %d (sequence, head) units%s, %.1f MB of K+V, %.2f s on %d threads of "
-                  "%s (fp64 scalar C oracle%s)" % (
+                  "%s (fp64 scalar C oracle%s); one thread: %d unit%s%s, %.1f MB in %.2f s" % (
                       n_units, len(units), "" if reps == 1 else " x %d passes" % reps,
                       total_bytes / 1e6, dt, cores, cpu_model(),
-                      ": rotate, append, attend" if path == "step" else ""),
+                      ": rotate, append, attend" if path == "step" else "",
+                      n1, "" if n1 == 1 else "s", "" if reps1 == 1 else " x %d passes" % reps1,
+                      bytes1 / 1e6, dt1),
     }
 
 
