@@ -737,6 +737,57 @@ def test_batch_at_the_size_limit():
     assert_close(out[torch.from_numpy(pick)], ref, "batch 65535")
 
 
+def test_cache_past_2_31_elements():
+    """One cache of 2^31 elements per tensor (4 Mi positions x 64 heads x
+    head_dim 8: K and V 4 GiB each), so element offsets pass 2^31 and every
+    chunk's row arithmetic must be 64-bit.  Four heads, the last among them,
+    against the oracle: output and score dump."""
+    w = wl.Workload("h64_d8_s4194304", n_heads=64, head_dim=8, seq_len=1 << 22,
+                    cur_pos=(1 << 22) - 3, seed=9)
+    q = wl.make_q(w, DEV)[0]
+    k, v = wl.make_kv(w, DEV)
+    out, dump = ad.decode(q, k[0], v[0], w.cur_pos, dump=True)
+    torch.cuda.synchronize()
+    del k, v
+    for h in (0, 31, 62, 63):
+        qs, ks, vs = wl.head_slice(w, 0, h)
+        ref, ref_s, _ = oracle.decode(qs[0], ks, vs, w.cur_pos, want_scores=True)
+        assert_close(out[h:h + 1], ref, "h=%d" % h)
+        assert_dump_close(dump[h:h + 1], ref_s, qs[0].numpy(), ks.numpy(), w.cur_pos, "h=%d" % h)
+    del dump
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("page_size", [0, 256], ids=["dense", "paged256"])
+def test_batch_past_2_31_elements(page_size):
+    """Six sequences of capacity 2^20 x 64 heads x head_dim 8 (3 x 2^30
+    elements per cache tensor, dense or as a page pool): the last two
+    sequences, or their pages, start past element 2^31.  Ragged lengths; two
+    heads of each of those sequences against the oracle."""
+    w = wl.Workload("b6_h64_d8_cap1048576", n_heads=64, head_dim=8, seq_len=1 << 20,
+                    cur_pos=None, seed=10, batch=6, page_size=page_size)
+    q = wl.make_q(w, DEV)
+    cp = w.positions().to(torch.int32).to(DEV)
+    if page_size:
+        kp, vp = wl.make_kv_paged(w, DEV)
+        bt = w.block_table()
+        out = ad.decode_paged(q, kp, vp, bt.to(torch.int32).to(DEV), cp)
+        torch.cuda.synchronize()
+        del kp, vp
+    else:
+        k, v = wl.make_kv(w, DEV)
+        out = ad.decode_batched(q, k, v, cp)
+        torch.cuda.synchronize()
+        del k, v
+    pos = w.positions()
+    for b in (4, 5):
+        for h in (1, 63):
+            qs, ks, vs = wl.head_slice_paged(w, b, h, bt) if page_size else wl.head_slice(w, b, h)
+            ref, _, _ = oracle.decode(qs[0], ks, vs, int(pos[b]))
+            assert_close(out[b, h:h + 1], ref, "b=%d h=%d" % (b, h))
+    torch.cuda.empty_cache()
+
+
 def test_two_dispatches_full_size_sampled():
     """The page's two dispatches on the 131072-position cache (the bench's
     --path two_dispatch launch): every stored score of 4 sampled heads is an
