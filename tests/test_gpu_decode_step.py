@@ -329,6 +329,16 @@ def test_step_long_context_sampled():
     sampled_heads_step(w, [0, 21, 42, 63], w.seq_len - 1)
 
 
+def test_step_past_2_32_elements():
+    """The step on a cache of 8 Mi + 4096 positions x 64 heads x head_dim 8
+    (8 GiB per tensor): the rows read and the new token's appended rows lie
+    past element 2^32."""
+    S = (1 << 23) + 4096
+    w = wl.Workload("h64_d8_s8392704", n_heads=64, head_dim=8, seq_len=S, cur_pos=S - 3, seed=9)
+    assert w.cur_pos * 64 * 8 > 1 << 32
+    sampled_heads_step(w, [0, 63], w.cur_pos)
+
+
 def test_step_masked_garbage_sampled():
     w = wl.WORKLOADS["h32_d128_s32768_cp20000_garbage"]
     sampled_heads_step(w, [0, 31], w.cur_pos, trad=True)

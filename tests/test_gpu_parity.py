@@ -737,13 +737,20 @@ def test_batch_at_the_size_limit():
     assert_close(out[torch.from_numpy(pick)], ref, "batch 65535")
 
 
-def test_cache_past_2_31_elements():
-    """One cache of 2^31 elements per tensor (4 Mi positions x 64 heads x
-    head_dim 8: K and V 4 GiB each), so element offsets pass 2^31 and every
-    chunk's row arithmetic must be 64-bit.  Four heads, the last among them,
-    against the oracle: output and score dump."""
-    w = wl.Workload("h64_d8_s4194304", n_heads=64, head_dim=8, seq_len=1 << 22,
-                    cur_pos=(1 << 22) - 3, seed=9)
+# A cache row offset is (position * n_heads + head) * head_dim elements: the
+# caches below put rows past element 2^31 and 2^32, where 32-bit offset
+# arithmetic, signed or unsigned, would wrap.
+BIG_S = (1 << 23) + 4096   # x 64 heads x head_dim 8: 4.3e9 elements per tensor
+
+
+def test_cache_past_2_32_elements():
+    """One cache of 8 Mi + 4096 positions x 64 heads x head_dim 8 (8 GiB per
+    tensor), the newest position near the end, so the rows read run past
+    element 2^32.  Four heads, the last among them, against the oracle:
+    output and score dump."""
+    w = wl.Workload("h64_d8_s8392704", n_heads=64, head_dim=8, seq_len=BIG_S,
+                    cur_pos=BIG_S - 3, seed=9)
+    assert (w.cur_pos * 64 + 63) * 8 > 1 << 32
     q = wl.make_q(w, DEV)[0]
     k, v = wl.make_kv(w, DEV)
     out, dump = ad.decode(q, k[0], v[0], w.cur_pos, dump=True)
@@ -759,13 +766,14 @@ def test_cache_past_2_31_elements():
 
 
 @pytest.mark.parametrize("page_size", [0, 256], ids=["dense", "paged256"])
-def test_batch_past_2_31_elements(page_size):
-    """Six sequences of capacity 2^20 x 64 heads x head_dim 8 (3 x 2^30
-    elements per cache tensor, dense or as a page pool): the last two
-    sequences, or their pages, start past element 2^31.  Ragged lengths; two
-    heads of each of those sequences against the oracle."""
-    w = wl.Workload("b6_h64_d8_cap1048576", n_heads=64, head_dim=8, seq_len=1 << 20,
-                    cur_pos=None, seed=10, batch=6, page_size=page_size)
+def test_batch_past_2_32_elements(page_size):
+    """Ten sequences of capacity 2^20 x 64 heads x head_dim 8 (5 x 2^30
+    elements per cache tensor, dense or as a page pool): sequence 4 starts at
+    element 2^31 and sequences 8 and 9 past 2^32 (in the pool, the pages are
+    scattered through all of it).  Ragged lengths; two heads of sequences 4
+    and 9 against the oracle."""
+    w = wl.Workload("b10_h64_d8_cap1048576", n_heads=64, head_dim=8, seq_len=1 << 20,
+                    cur_pos=None, seed=10, batch=10, page_size=page_size)
     q = wl.make_q(w, DEV)
     cp = w.positions().to(torch.int32).to(DEV)
     if page_size:
@@ -780,7 +788,7 @@ def test_batch_past_2_31_elements(page_size):
         torch.cuda.synchronize()
         del k, v
     pos = w.positions()
-    for b in (4, 5):
+    for b in (4, 9):
         for h in (1, 63):
             qs, ks, vs = wl.head_slice_paged(w, b, h, bt) if page_size else wl.head_slice(w, b, h)
             ref, _, _ = oracle.decode(qs[0], ks, vs, int(pos[b]))
