@@ -765,6 +765,34 @@ def test_cache_past_2_32_elements():
     torch.cuda.empty_cache()
 
 
+def test_two_dispatches_past_2_32_elements():
+    """The page's two dispatches on the same 8 GiB-per-tensor cache: the
+    scores pass reads K rows past element 2^32, softmax.V reads V rows there.
+    Two heads: every stored score an fp16 neighbour of the oracle's, the
+    output against softmax.V of the oracle's scores rounded to fp16."""
+    w = wl.Workload("h64_d8_s8392704", n_heads=64, head_dim=8, seq_len=BIG_S,
+                    cur_pos=BIG_S - 3, seed=9)
+    q = wl.make_q(w, DEV)[0]
+    k, v = wl.make_kv(w, DEV)
+    sc = ad.qk(q, k[0], w.cur_pos)
+    out = ad.pv(sc, v[0], w.cur_pos)
+    torch.cuda.synchronize()
+    del k, v
+    for h in (0, 63):
+        qh, kh, vh = wl.head_slice(w, 0, h)
+        _, s_ref, _ = oracle.decode(qh[0], kh, vh, w.cur_pos, want_scores=True)
+        L = w.cur_pos + 1
+        got = sc[h].cpu().numpy().astype(np.float64)
+        assert np.all(got[L:] == -np.inf)
+        err = np.abs(got[:L] - s_ref[0, :L])
+        cond = np.abs(kh[:, 0].numpy().astype(np.float64)) @ np.abs(qh[0, 0].numpy().astype(np.float64)) / np.sqrt(8.0)
+        assert np.all(err < f16_ulp(s_ref[0, :L]) + 8 * 2.0 ** -24 * cond), h
+        ref = oracle.pv_from_scores(s_ref.astype(np.float16), vh, w.cur_pos)
+        assert_close(out[h:h + 1], ref, "two dispatches head %d" % h)
+    del sc
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("page_size", [0, 256], ids=["dense", "paged256"])
 def test_batch_past_2_32_elements(page_size):
     """Ten sequences of capacity 2^20 x 64 heads x head_dim 8 (5 x 2^30

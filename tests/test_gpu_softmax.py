@@ -173,3 +173,30 @@ def test_softmax_million_short_rows():
     torch.cuda.synchronize()
     pick = np.concatenate([[0, rows - 1], rng.choice(rows, 2000, replace=False)])
     check(got[torch.from_numpy(pick).to(DEV)], np.ascontiguousarray(x[pick]), "2^20 rows")
+
+
+@pytest.mark.parametrize("rows,cols,check_rows", [
+    ((1 << 17) + 1, 32768, (0, 1 << 16, 1 << 17)),   # a workgroup per row
+    (64, (1 << 26) + 64, (32, 63)),                  # split path, 4096-column chunks
+], ids=["row_path", "split_path"])
+def test_softmax_past_2_32_elements(rows, cols, check_rows):
+    """Inputs of just over 2^32 fp32 elements (17 GB in, 17 GB out), filled on
+    the device by the shared generator: the checked rows start at or cross
+    elements 2^31 and 2^32, where 32-bit offsets would wrap.  The oracle
+    regenerates only those rows on the host."""
+    assert rows * cols > 1 << 32
+    print("softmax past 2^32", rows, cols, flush=True)
+    x = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    flat = x.view(-1)
+    step = 1 << 26
+    for lo in range(0, flat.numel(), step):
+        hi = min(flat.numel(), lo + step)
+        flat[lo:hi] = wl.normal_f32(77, 0, torch.arange(lo, hi, dtype=torch.int64, device=DEV), 3.0)
+    got = ad.softmax(x)
+    torch.cuda.synchronize()
+    del x
+    for r in check_rows:
+        xr = wl.normal_f32(77, 0, torch.arange(r * cols, (r + 1) * cols, dtype=torch.int64), 3.0)
+        check(got[r:r + 1], xr.numpy().reshape(1, cols), "row %d" % r)
+    del got
+    torch.cuda.empty_cache()
