@@ -134,6 +134,56 @@ def test_graph_paged_and_two_dispatches():
     replay_and_check(g, [out_p, sc, out1], [e_p, e_sc, e_o], disturb)
 
 
+def test_graph_one_launch_plans():
+    """The plans that finish in the split launch alone, captured together: a
+    tiny single sequence (one chunk per head block), a dense batch of short
+    capacity (one chunk per sequence and head block), and a decode step on a
+    short-capacity batch (its combine appends the new rows)."""
+    rng = np.random.default_rng(5)
+
+    def t16(shape):
+        return torch.from_numpy(rng.standard_normal(shape).astype(np.float16)).to(DEV)
+
+    q1, k1, v1 = t16((4, 64)), t16((128, 4, 64)), t16((128, 4, 64))
+    ws1 = ad.alloc_workspace(1, 4, 64, 128, DEV)
+    B, S, H, D = 16, 256, 8, 128
+    qb, kb, vb = t16((B, H, D)), t16((B, S, H, D)), t16((B, S, H, D))
+    cpb = torch.from_numpy(rng.integers(0, S + 3, B).astype(np.int32)).to(DEV)
+    wsb = ad.alloc_workspace(B, H, D, S, DEV)
+    Bs, Ss, Hs, Ds = 8, 64, 4, 64
+    qs, kn, vn = t16((Bs, Hs, Ds)), t16((Bs, Hs, Ds)), t16((Bs, Hs, Ds))
+    k0, v0 = t16((Bs, Ss, Hs, Ds)), t16((Bs, Ss, Hs, Ds))
+    kc, vc = k0.clone(), v0.clone()
+    cps = torch.from_numpy(rng.integers(0, Ss, Bs).astype(np.int32)).to(DEV)
+    wss = ad.alloc_workspace(Bs, Hs, Ds, Ss, DEV)
+    e1 = ad.decode(q1, k1, v1, 100, workspace=ws1).clone()
+    eb = ad.decode_batched(qb, kb, vb, cpb, workspace=wsb).clone()
+    es = ad.decode_step(qs, kn, vn, kc, vc, cps, workspace=wss).clone()
+    e_k, e_v = kc.clone(), vc.clone()
+    out1 = torch.empty_like(e1)
+    outb = torch.empty_like(eb)
+    outs = torch.empty_like(es)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ad.decode(q1, k1, v1, 100, out=out1, workspace=ws1)
+        ad.decode_batched(qb, kb, vb, cpb, out=outb, workspace=wsb)
+        ad.decode_step(qs, kn, vn, kc, vc, cps, out=outs, workspace=wss)
+
+    def disturb():   # eager calls on the same workspaces, caches restored
+        ad.decode(q1, k1, v1, 3, workspace=ws1)
+        ad.decode_batched(qb, kb, vb, torch.zeros_like(cpb), workspace=wsb)
+        kc.copy_(k0)
+        vc.copy_(v0)
+
+    disturb()
+    torch.cuda.synchronize()
+    replay_and_check(g, [out1, outb, outs], [e1, eb, es], disturb)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(kc, e_k) and torch.equal(vc, e_v)
+
+
 def test_two_streams_at_once():
     """Calls enqueued on two streams at once, each stream with its own
     workspace, give the bits of the same calls run one after another: the
