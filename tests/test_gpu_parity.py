@@ -349,9 +349,13 @@ def test_many_short_sequences(S):
     pos = rng.integers(0, 45, B)
     cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
     out = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    out_d, dump = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp, dump=True)
     torch.cuda.synchronize()
-    ref, _ = oracle.decode_batched(q, k, v, pos)
+    assert torch.equal(out, out_d), "dump variant differs"
+    ref, ref_s = oracle.decode_batched(q, k, v, pos, want_scores=True)
     assert_close(out, ref, "300 sequences")
+    for b in (0, 1, 150, 299):
+        assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "b=%d" % b)
 
 
 @pytest.mark.parametrize("D", [64, 128])
