@@ -1206,12 +1206,18 @@ const Knobs &env_knobs() {
 // x 128 positions: 36.5 -> 15.9 us; 1024 x 32 x 32: 161.7 -> 50.7; 2 x 8 x
 // 512: 12.7 -> 4.9).  Many head blocks want wider blocks: at most
 // kShortGroups workgroups (1024 x 32 heads x 32 positions: 72.5 us at 32768,
-// 50.7 at 16384, 50.3 at 8192).
+// 50.7 at 16384, 50.3 at 8192).  Up to twice that capacity the plan still
+// wins for head_dim <= 128 once the workgroups cover every CU (8 x 32 x
+// 1024: 27.4 -> 21.3 us; 48 x 8 x 1024: 29.4 -> 23.9); with fewer it is a
+// toss-up, and at head_dim 256 it loses.  A paged cache needs more
+// workgroups than CUs there: at exactly one per CU it lost 8-28% on four of
+// five shapes, from 300 workgroups on it won 3-43%.
 enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short, single_step,
                   single_tiny, batched_short };
 constexpr uint32_t kShortSpan = 8192;
 constexpr uint64_t kOneChunkBytes = 256u << 10;
 constexpr uint64_t kShortGroups = 8192;
+constexpr uint64_t kShortMinGroups = 256;   // the CU count
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
@@ -1505,7 +1511,12 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     if (kind == Kind::batched || kind == Kind::paged) {
         const uint32_t short_hpb = heads_per_wg(H, choose_layout(D, nullptr, nullptr, nullptr),
                                                 knobs(D, Kind::batched_short).hpb);
-        if ((uint64_t)S * short_hpb * D * 4 <= kOneChunkBytes) kind = Kind::batched_short;
+        const uint64_t wg_bytes = (uint64_t)S * short_hpb * D * 4;
+        const uint64_t groups = (uint64_t)batch * (H / short_hpb);
+        if (wg_bytes <= kOneChunkBytes ||
+            (D <= 128 && wg_bytes <= 2 * kOneChunkBytes &&
+             (pg ? groups > kShortMinGroups : groups >= kShortMinGroups)))
+            kind = Kind::batched_short;
     }
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);

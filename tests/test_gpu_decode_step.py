@@ -279,10 +279,11 @@ def test_step_batched_every_sequence_at_position_zero():
     assert np.array_equal(kg[:, 0].view(np.uint16), kn.view(np.uint16))
 
 
-@pytest.mark.parametrize("S", [24, 600])
+@pytest.mark.parametrize("S", [24, 600, 1100])
 def test_step_batched_more_sequences_than_balanced_grid_handles(S):
     """1030 sequences take the chunked grid with per-sequence lengths, some 0
-    (a capacity of 24: the short-capacity plan; 600: the plain chunked one)."""
+    (capacities of 24 and 600: the short-capacity plan; 1100: the plain
+    chunked one)."""
     rng = np.random.default_rng(10)
     B, H, D = 1030, 2, 64
     cps = rng.integers(0, S, B)

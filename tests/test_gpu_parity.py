@@ -338,11 +338,12 @@ def test_batched_matches_single_calls():
         assert_close(out[b], single.float().cpu().numpy(), "batched vs single b=%d" % b)
 
 
-@pytest.mark.parametrize("S", [40, 600])
+@pytest.mark.parametrize("S", [40, 600, 1100])
 def test_many_short_sequences(S):
-    """300 sequences of at most 45 positions.  A capacity of 40 takes one chunk
-    per sequence and head block; one of 600 the balanced grid, whose
-    workgroups then walk many short pieces each."""
+    """300 sequences of at most 45 positions.  Capacities of 40 and 600 take
+    one chunk per sequence and head block (600: 300 KiB of K+V per workgroup,
+    over 256 workgroups); one of 1100 the balanced grid, whose workgroups then
+    walk many short pieces each."""
     rng = np.random.default_rng(12)
     B, H, D = 300, 2, 64
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
@@ -499,11 +500,11 @@ def test_batched_extreme_ragged_lengths():
         assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "b=%d" % b)
 
 
-@pytest.mark.parametrize("S", [24, 2100])
+@pytest.mark.parametrize("S", [24, 4200])
 def test_batched_more_sequences_than_balanced_grid_handles(S):
     """1100 short sequences: past the balanced grid's batch limit the chunked
     grid serves the call (a capacity of 24 with the short-capacity plan, one
-    of 2100 with the plain chunked plan)."""
+    of 4200 with the plain chunked plan)."""
     rng = np.random.default_rng(32)
     B, H, D = 1100, 2, 16
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
@@ -616,10 +617,10 @@ def test_paged_shared_pages_and_unused_table_entries():
     assert_close(out, ref, "shared pages")
 
 
-@pytest.mark.parametrize("S", [32, 600])
+@pytest.mark.parametrize("S", [32, 600, 1104])
 def test_paged_split_then_combine_and_many_sequences(S):
-    """1030 sequences, past the balanced grid's batch limit: a capacity of 32
-    takes the short-capacity plan, one of 600 the plain chunked plan."""
+    """1030 sequences, past the balanced grid's batch limit: capacities of 32
+    and 600 take the short-capacity plan, one of 1104 the plain chunked plan."""
     rng = np.random.default_rng(44)
     B, H, D, P = 1030, 2, 64, 8
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
