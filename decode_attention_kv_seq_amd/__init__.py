@@ -40,6 +40,17 @@ class AttnError(RuntimeError):
 _lib = None
 
 
+class PlanInfo(ctypes.Structure):
+    """attn_plan_info of include/attn_decode.h."""
+    _fields_ = [("balanced", ctypes.c_uint32), ("heads_per_workgroup", ctypes.c_uint32),
+                ("workgroups", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
+                ("chunks", ctypes.c_uint32), ("launches", ctypes.c_uint32),
+                ("partial_slots", ctypes.c_uint64), ("workspace_slots", ctypes.c_uint64)]
+
+
+PLAN_DEVICE_POS, PLAN_PAGED, PLAN_STEP, PLAN_FROM_SCORES = 1, 2, 4, 8
+
+
 def load_library(path: str = LIB_PATH):
     """Load the HIP library.  There is no fallback: a missing library is an error."""
     global _lib
@@ -87,6 +98,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_softmax_workspace_bytes.restype = sz
     lib.attn_softmax_f32.argtypes = [vp, vp, u32, u32, vp, sz, vp]
     lib.attn_softmax_f32.restype = ctypes.c_int
+    lib.attn_decode_plan.argtypes = [u32, u32, u32, u32, u32, u32, ctypes.POINTER(PlanInfo)]
+    lib.attn_decode_plan.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -140,6 +153,16 @@ def _req_dump(dump, shape, device):
         _req(dump, "dump", torch.float32, device)
         if tuple(dump.shape) != tuple(shape):
             raise ValueError("dump must be %s" % list(shape))
+
+
+def plan(batch: int, n_heads: int, head_dim: int, seq_len: int, current_pos: int = 0,
+         flags: int = 0) -> dict:
+    """attn_decode_plan: how a call with these sizes runs (host only).
+    flags: PLAN_* bits naming the call (0: the single-sequence decode)."""
+    info = PlanInfo()
+    _check(load_library().attn_decode_plan(batch, n_heads, head_dim, seq_len, current_pos, flags,
+                                           ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
 
 
 def workspace_bytes(batch: int, n_heads: int, head_dim: int, seq_len: int) -> int:

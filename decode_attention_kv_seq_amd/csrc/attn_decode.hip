@@ -1350,6 +1350,7 @@ Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span
 // (per-sequence lengths, batch <= kBalancedMaxBatch).
 struct WsLayout {
     size_t o_off, ml_off, total;
+    size_t slots;   // partial states the workspace holds
 };
 
 size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
@@ -1372,7 +1373,7 @@ WsLayout workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     const size_t hdr = kHeaderBytes;
     const size_t o_bytes = (slots * D * sizeof(float) + 255) / 256 * 256;
     const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
-    return WsLayout{hdr, hdr + o_bytes, hdr + o_bytes + ml_bytes};
+    return WsLayout{hdr, hdr + o_bytes, hdr + o_bytes + ml_bytes, slots};
 }
 
 attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
@@ -1489,21 +1490,30 @@ struct Paging {
     uint32_t max_blocks, num_blocks, page_shift;
 };
 
-attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                           const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
-                           uint32_t D, uint32_t S, float *dump, void *ws, uint16_t *out,
-                           const Paging *pg, hipStream_t stream, bool *wrote_out,
-                           const uint16_t *scores_in = nullptr, const RopeArgs *rope = nullptr) {
-    const Layout ly = scores_in ? choose_layout(D, v, v, v) : choose_layout(D, q, k, v);
+// Everything a split launch decides from the sizes and the tensors' lane
+// layout: the knob row, heads per workgroup, the grid and the chunking.
+struct SplitPlan {
+    Kind kind;
+    Knobs kn;
+    uint32_t hpb;
+    bool bal;   // balanced grid
+    Plan plan;
+};
+
+// dev_pos: per-sequence current_pos on the device (batched or paged);
+// paged: a paged cache; rope: a decode step; scores: softmax.V from stored
+// scores (the second dispatch).
+SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool paged, bool rope,
+                     bool scores, uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     // host current_pos: plan the exact span (a decode step streams one
     // position less; at least one chunk is launched, so the header is
     // written); device array: plan the capacity
-    uint32_t span = cp_dev ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1 - (rope ? 1u : 0u);
+    uint32_t span = dev_pos ? S : (cp_host < S - 1 ? cp_host : S - 1) + 1 - (rope ? 1u : 0u);
     if (span == 0) span = 1;
-    Kind kind = scores_in ? Kind::stream : pg ? Kind::paged : cp_dev ? Kind::batched
+    Kind kind = scores ? Kind::stream : paged ? Kind::paged : dev_pos ? Kind::batched
               : (D > 64 && span <= kShortSpan) ? Kind::single_short
               : (D > 64 && D <= 128 && rope) ? Kind::single_step : Kind::single;
-    if (!scores_in && !pg && !cp_dev) {
+    if (!scores && !paged && !dev_pos) {
         const uint32_t tiny_hpb = heads_per_wg(H, choose_layout(D, nullptr, nullptr, nullptr),
                                                knobs(D, Kind::single_tiny).hpb);
         if ((uint64_t)span * tiny_hpb * D * 4 <= kOneChunkBytes) kind = Kind::single_tiny;
@@ -1515,7 +1525,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
         const uint64_t groups = (uint64_t)batch * (H / short_hpb);
         if (wg_bytes <= kOneChunkBytes ||
             (D <= 128 && wg_bytes <= 2 * kOneChunkBytes &&
-             (pg ? groups > kShortMinGroups : groups >= kShortMinGroups)))
+             (paged ? groups > kShortMinGroups : groups >= kShortMinGroups)))
             kind = Kind::batched_short;
     }
     Knobs kn = knobs(D, kind);
@@ -1527,13 +1537,28 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
             hpb = h;
         }
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
-    const bool bal = !scores_in && kn.bal && batch <= kBalancedMaxBatch &&
+    const bool bal = !scores && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
     if (!bal && (kind == Kind::batched || kind == Kind::paged)) {   // a batch on the chunked grid
         kind = Kind::batched_chunked;
         kn = knobs(D, kind);
         hpb = heads_per_wg(H, ly, kn.hpb);
     }
+    return SplitPlan{kind, kn, hpb, bal, make_plan(batch, H, D, S, span, kind)};
+}
+
+attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
+                           uint32_t D, uint32_t S, float *dump, void *ws, uint16_t *out,
+                           const Paging *pg, hipStream_t stream, bool *wrote_out,
+                           const uint16_t *scores_in = nullptr, const RopeArgs *rope = nullptr) {
+    const Layout ly = scores_in ? choose_layout(D, v, v, v) : choose_layout(D, q, k, v);
+    const SplitPlan sp = plan_split(ly, cp_dev != nullptr, cp_host, pg != nullptr, rope != nullptr,
+                                    scores_in != nullptr, batch, H, D, S);
+    const Knobs &kn = sp.kn;
+    const uint32_t hpb = sp.hpb;
+    const bool bal = sp.bal;
+    const Plan &plan = sp.plan;
     const SplitFn fn =
         scores_in ? pick_split<false, false, kModePv>(ly, kn, false)
         : rope    ? (pg ? pick_split<false, true, kModeStep>(ly, kn, bal)
@@ -1543,7 +1568,6 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
              : (dump ? pick_split<true, false, kModeDecode>(ly, kn, bal)
                      : pick_split<false, false, kModeDecode>(ly, kn, bal));
     if (!fn) return fail(ATTN_ERR_DIM, "no kernel for head_dim=%u", D);
-    const Plan plan = make_plan(batch, H, D, S, span, kind);
     const WsLayout wl = workspace_layout(batch, H, D, S);
 
     SplitArgs a;
@@ -1723,6 +1747,43 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t n_heads, uint32_t he
                                    uint32_t seq_len) {
     if (check_sizes(batch, n_heads, head_dim, seq_len) != ATTN_OK) return 0;
     return workspace_layout(batch, n_heads, head_dim, seq_len).total;
+}
+
+attn_status_t attn_decode_plan(uint32_t batch, uint32_t n_heads, uint32_t head_dim,
+                               uint32_t seq_len, uint32_t current_pos, uint32_t flags,
+                               attn_plan_info *info) {
+    if (!info) return fail(ATTN_ERR_NULL, "info must be non-NULL");
+    attn_status_t s = check_sizes(batch, n_heads, head_dim, seq_len);
+    if (s != ATTN_OK) return s;
+    if (flags & ~(ATTN_PLAN_DEVICE_POS | ATTN_PLAN_PAGED | ATTN_PLAN_STEP | ATTN_PLAN_FROM_SCORES))
+        return fail(ATTN_ERR_DIM, "unknown plan flags 0x%x", flags);
+    const bool paged = flags & ATTN_PLAN_PAGED;
+    const bool dev_pos = paged || (flags & ATTN_PLAN_DEVICE_POS);
+    const bool step = flags & ATTN_PLAN_STEP;
+    const bool scores = flags & ATTN_PLAN_FROM_SCORES;
+    if (scores && (dev_pos || step || batch != 1))
+        return fail(ATTN_ERR_DIM, "softmax.V from stored scores is a single-sequence call");
+    if (step && !dev_pos && current_pos >= seq_len)
+        return fail(ATTN_ERR_DIM, "current_pos=%u must be < seq_len=%u (the new token's slot)",
+                    current_pos, seq_len);
+    const Layout ly = choose_layout(head_dim, nullptr, nullptr, nullptr);
+    const SplitPlan sp = plan_split(ly, dev_pos, current_pos, paged, step, scores, batch, n_heads,
+                                    head_dim, seq_len);
+    const uint64_t n_hb = n_heads / sp.hpb;
+    const bool direct = !sp.bal && !step && sp.plan.n_chunks == 1;
+    info->balanced = sp.bal ? 1u : 0u;
+    info->heads_per_workgroup = sp.hpb;
+    info->workgroups = sp.bal ? sp.kn.wgs : (uint32_t)(n_hb * sp.plan.n_chunks * batch);
+    info->chunk = sp.bal ? 0u : sp.plan.chunk;
+    info->chunks = sp.bal ? 0u : sp.plan.n_chunks;
+    info->launches = direct ? 1u : 2u;
+    // one past the highest partial slot the split launch writes: balanced,
+    // (w + segment) * hpb + head for w < grid; chunked, (b*H + h) * stride + c
+    info->partial_slots = direct ? 0
+                        : sp.bal ? ((uint64_t)sp.kn.wgs + (uint64_t)batch * n_hb - 1) * sp.hpb
+                                 : ((uint64_t)batch * n_heads - 1) * sp.plan.nc_stride + sp.plan.n_chunks;
+    info->workspace_slots = workspace_layout(batch, n_heads, head_dim, seq_len).slots;
+    return ok();
 }
 
 attn_status_t attn_decode_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,

@@ -78,6 +78,56 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t n_heads, uint32_t he
                                    uint32_t seq_len);
 
 /*
+ * How a call with these sizes is carried out: the grid of its streaming
+ * (split) launch, whether a merge (combine) launch follows, and how many
+ * partial softmax states it leaves in the workspace.  For callers that
+ * budget launches or graph nodes, and for checking that every plan's
+ * partial states fit the workspace attn_decode_workspace_bytes sizes.
+ * Host only: no HIP call is made and no device is needed.  The plan assumes
+ * tensors aligned for 16-byte loads (as a caching allocator returns them);
+ * with less aligned tensors a call may put fewer heads in a workgroup.
+ *   flags        which call is meant, ATTN_PLAN_* bits (0: attn_decode_f16,
+ *                or attn_decode_f16_split with one host current_pos for the
+ *                whole batch):
+ *                DEVICE_POS attn_decode_f16_batched; PAGED attn_decode_f16_paged
+ *                (seq_len = max_blocks * page_size); STEP the decode step
+ *                (with DEVICE_POS or PAGED, its batched or paged form);
+ *                FROM_SCORES attn_pv_f16.
+ *   current_pos  the host current_pos of a single-sequence call; ignored
+ *                with DEVICE_POS or PAGED, whose plans cover the capacity.
+ *   info         written on ATTN_OK.
+ * Errors: ATTN_ERR_NULL (info), ATTN_ERR_DIM (sizes as for the calls,
+ * unknown flags, FROM_SCORES with other flags or batch != 1, a
+ * single-sequence STEP with current_pos >= seq_len).
+ * Not counted: the fill launch a score dump adds.
+ */
+#define ATTN_PLAN_DEVICE_POS 1u
+#define ATTN_PLAN_PAGED 2u
+#define ATTN_PLAN_STEP 4u
+#define ATTN_PLAN_FROM_SCORES 8u
+
+typedef struct attn_plan_info {
+    uint32_t balanced;             /* 1: balanced grid (equal positions per
+                                      workgroup across the batch); 0: chunked */
+    uint32_t heads_per_workgroup;  /* heads one split workgroup reads together */
+    uint32_t workgroups;           /* workgroups of the split launch          */
+    uint32_t chunk;                /* chunked grid: positions per chunk (0 if
+                                      balanced)                                */
+    uint32_t chunks;               /* chunked grid: chunks per (sequence, head
+                                      block) (0 if balanced)                   */
+    uint32_t launches;             /* 1: the split launch writes out; 2: a
+                                      combine launch follows                   */
+    uint64_t partial_slots;        /* one past the highest partial state the
+                                      split launch may write (0 with one
+                                      launch)                                  */
+    uint64_t workspace_slots;      /* partial states the workspace holds      */
+} attn_plan_info;
+
+attn_status_t attn_decode_plan(uint32_t batch, uint32_t n_heads, uint32_t head_dim,
+                               uint32_t seq_len, uint32_t current_pos, uint32_t flags,
+                               attn_plan_info *info);
+
+/*
  * One sequence.
  *   q            [n_heads, head_dim] fp16
  *   k_cache      [seq_len, n_heads, head_dim] fp16

@@ -59,6 +59,16 @@ int main(void) {
     st = attn_rope_f16(h, h, NULL, 1, 4, 64, 64, 10000.0, 0, NULL);
     CHECK(st == ATTN_ERR_NULL);
 
+    {   /* the plan query: host only, C struct layout as declared */
+        attn_plan_info pi;
+        CHECK(attn_decode_plan(1, 4, 64, 128, 100, 0, &pi) == ATTN_OK);
+        CHECK(pi.launches == 1 && pi.chunks == 1 && pi.partial_slots == 0);
+        CHECK(attn_decode_plan(64, 32, 128, 8192, 0, ATTN_PLAN_DEVICE_POS, &pi) == ATTN_OK);
+        CHECK(pi.balanced == 1 && pi.launches == 2 && pi.partial_slots <= pi.workspace_slots);
+        CHECK(attn_decode_plan(1, 4, 64, 128, 0, 0, NULL) == ATTN_ERR_NULL);
+        CHECK(attn_decode_plan(1, 4, 64, 128, 0, 16u, &pi) == ATTN_ERR_DIM);
+    }
+
     printf("%s\n", fails ? "FAILED" : "ok");
     return fails != 0;
 }

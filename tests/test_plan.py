@@ -1,0 +1,150 @@
+"""The launch planner on the host, through attn_decode_plan (no GPU): the
+plans the measured rules pick for the five workloads and at the edge of each
+rule, and, over a seeded sweep of sizes and calls, the invariants the
+kernels rely on -- every partial softmax state a split launch writes has a
+slot in the workspace attn_decode_workspace_bytes sizes, the chunks cover
+the positions streamed, and a call that finishes in one launch writes no
+partial states."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import decode_attention_kv_seq_amd as ad
+from decode_attention_kv_seq_amd import PLAN_DEVICE_POS, PLAN_FROM_SCORES, PLAN_PAGED, PLAN_STEP
+
+ATTN_ERR_NULL, ATTN_ERR_DIM = 1, 2
+
+
+def plan(B, H, D, S, cp=0, flags=0):
+    return ad.plan(B, H, D, S, cp, flags)
+
+
+@pytest.mark.parametrize("args,expect", [
+    # 4 heads x 101 positions: one chunk per head block, the split writes out
+    ((1, 4, 64, 128, 100), dict(balanced=0, workgroups=1, chunks=1, launches=1)),
+    # 4096 positions, head_dim 128: one head per workgroup, 512 workgroups
+    ((1, 32, 128, 4096, 4095), dict(balanced=0, heads_per_workgroup=1, workgroups=512, launches=2)),
+    # 20001 of 32768 positions: 512 workgroups of two heads
+    ((1, 32, 128, 32768, 20000), dict(balanced=0, heads_per_workgroup=2, workgroups=512, launches=2)),
+    # 131072 positions, head_dim 64: 1024 workgroups of four heads (512-byte rows)
+    ((1, 64, 64, 131072, 131071), dict(balanced=0, heads_per_workgroup=4, workgroups=1024, launches=2)),
+])
+def test_single_sequence_workload_plans(args, expect):
+    p = plan(*args)
+    assert {k: p[k] for k in expect} == expect, p
+
+
+def test_ragged_batch_workload_takes_the_balanced_grid():
+    p = plan(64, 32, 128, 8192, flags=PLAN_DEVICE_POS)
+    assert (p["balanced"], p["workgroups"], p["heads_per_workgroup"], p["launches"]) == (1, 256, 8, 2)
+    assert plan(64, 32, 128, 8192, flags=PLAN_PAGED)["balanced"] == 1
+
+
+@pytest.mark.parametrize("B,H,D,S,flags,one_chunk", [
+    # <= 256 KiB of K+V per 256-byte head block: one chunk, any workgroup count
+    (64, 32, 128, 128, PLAN_DEVICE_POS, True),
+    (2, 8, 128, 512, PLAN_DEVICE_POS, True),
+    (2, 8, 128, 512, PLAN_PAGED, True),
+    (64, 16, 256, 128, PLAN_DEVICE_POS, True),
+    # 512 KiB per workgroup: one chunk from 256 workgroups on (paged: more than 256)
+    (8, 32, 128, 1024, PLAN_DEVICE_POS, True),
+    (4, 32, 128, 1024, PLAN_DEVICE_POS, False),
+    (8, 64, 64, 1024, PLAN_DEVICE_POS, True),
+    (8, 64, 64, 1024, PLAN_PAGED, False),
+    (300, 2, 64, 608, PLAN_PAGED, True),
+    (16, 32, 128, 1024, PLAN_PAGED, True),
+    # head_dim 256 keeps the balanced grid past 256 KiB
+    (64, 8, 256, 512, PLAN_DEVICE_POS, False),
+    # 1 MiB per workgroup: balanced
+    (64, 8, 128, 2048, PLAN_DEVICE_POS, False),
+])
+def test_short_capacity_rule(B, H, D, S, flags, one_chunk):
+    p = plan(B, H, D, S, flags=flags)
+    got = p["balanced"] == 0 and p["chunks"] == 1 and p["launches"] == 1
+    assert got == one_chunk, p
+    if not one_chunk:
+        assert p["balanced"] == 1
+
+
+def test_many_head_blocks_are_widened():
+    """1024 x 32 heads x 32 positions: one head per workgroup would launch
+    32768 workgroups; head blocks are doubled until at most 8192 remain."""
+    p = plan(1024, 32, 128, 32, flags=PLAN_DEVICE_POS)
+    assert (p["heads_per_workgroup"], p["workgroups"], p["launches"]) == (4, 8192, 1)
+
+
+def test_batches_past_the_balanced_limit_take_the_chunked_grid():
+    for S in (24, 4200, 100000):
+        p = plan(1100, 2, 16, S, flags=PLAN_DEVICE_POS)
+        assert p["balanced"] == 0, (S, p)
+        assert p["chunks"] * p["chunk"] >= S
+
+
+def test_decode_steps_always_merge_in_a_second_launch():
+    for args, flags in [((1, 4, 64, 128, 100), PLAN_STEP), ((64, 32, 128, 128, 0), PLAN_STEP | PLAN_DEVICE_POS),
+                        ((2, 8, 64, 64, 0), PLAN_STEP | PLAN_PAGED)]:
+        assert plan(*args, flags=flags)["launches"] == 2
+
+
+def span_of(S, cp, flags):
+    if flags & (PLAN_DEVICE_POS | PLAN_PAGED):
+        return S
+    L = min(cp, S - 1) + 1 - (1 if flags & PLAN_STEP else 0)
+    return max(L, 1)
+
+
+FLAG_SETS = [0, PLAN_STEP, PLAN_FROM_SCORES, PLAN_DEVICE_POS, PLAN_PAGED, PLAN_DEVICE_POS | PLAN_STEP,
+             PLAN_PAGED | PLAN_STEP]
+
+
+def test_partial_states_fit_the_workspace():
+    rng = np.random.default_rng(4242)
+    dims = [1, 2, 3, 7, 8, 16, 24, 40, 48, 64, 72, 80, 96, 100, 112, 128, 136, 192, 250, 256]
+    n = 0
+    for _ in range(4000):
+        flags = int(rng.choice(FLAG_SETS))
+        D = int(rng.choice(dims))
+        H = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 32, 40, 64, 128]))
+        S = int(np.exp(rng.uniform(0, np.log(1 << 21))))
+        S = max(S, 2 if flags == PLAN_STEP else 1)
+        single = not flags & (PLAN_DEVICE_POS | PLAN_PAGED)
+        B = 1 if flags & PLAN_FROM_SCORES else int(rng.choice([1, 2, 5, 64, 300, 1024, 1025, 4096]))
+        if single and flags & PLAN_STEP:
+            B = 1
+        cp = int(rng.integers(0, S - 1 if flags == PLAN_STEP else S + 3)) if S > 1 else 0
+        p = plan(B, H, D, S, cp, flags)
+        what = (B, H, D, S, cp, flags, p)
+        hpb = p["heads_per_workgroup"]
+        assert hpb >= 1 and hpb & (hpb - 1) == 0 and H % hpb == 0, what
+        assert p["workgroups"] >= 1, what
+        assert p["launches"] in (1, 2), what
+        assert p["partial_slots"] <= p["workspace_slots"], what
+        need = 256 + p["workspace_slots"] * (D + 2) * 4
+        assert ad.workspace_bytes(B, H, D, S) >= need, what
+        if p["balanced"]:
+            assert p["chunk"] == 0 and p["chunks"] == 0 and p["launches"] == 2, what
+        else:
+            assert p["chunk"] % 16 == 0 and p["chunks"] >= 1, what
+            assert p["chunks"] * p["chunk"] >= span_of(S, cp, flags), what
+            assert (p["chunks"] - 1) * p["chunk"] < span_of(S, cp, flags), what
+            assert p["workgroups"] == (H // hpb) * p["chunks"] * B, what
+        if p["launches"] == 1:
+            assert not p["balanced"] and p["chunks"] == 1 and p["partial_slots"] == 0, what
+            assert not flags & PLAN_STEP, what
+        n += 1
+    assert n == 4000
+
+
+def test_plan_errors():
+    lib = ad.load_library()
+    info = ad.PlanInfo()
+    assert lib.attn_decode_plan(1, 4, 64, 128, 0, 0, None) == ATTN_ERR_NULL
+    for args in [(0, 4, 64, 128, 0, 0), (1, 4, 257, 128, 0, 0), (1, 4, 64, 0, 0, 0),
+                 (1, 4, 64, 128, 0, 16), (2, 4, 64, 128, 0, PLAN_FROM_SCORES),
+                 (1, 4, 64, 128, 0, PLAN_FROM_SCORES | PLAN_DEVICE_POS),
+                 (1, 4, 64, 128, 128, PLAN_STEP)]:
+        assert lib.attn_decode_plan(*args, ctypes.byref(info)) == ATTN_ERR_DIM, args
+        assert lib.attn_last_error()
+    with pytest.raises(ad.AttnError):
+        ad.plan(1, 4, 64, 128, 128, PLAN_STEP)
