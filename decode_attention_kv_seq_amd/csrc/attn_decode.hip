@@ -1770,7 +1770,9 @@ attn_status_t attn_decode_plan(uint32_t batch, uint32_t n_heads, uint32_t head_d
     const SplitPlan sp = plan_split(ly, dev_pos, current_pos, paged, step, scores, batch, n_heads,
                                     head_dim, seq_len);
     const uint64_t n_hb = n_heads / sp.hpb;
-    const bool direct = !sp.bal && !step && sp.plan.n_chunks == 1;
+    // one launch: a one-call entry point (a batch with one host current_pos
+    // exists only as the split / combine pair) whose plan has one chunk
+    const bool direct = !sp.bal && !step && sp.plan.n_chunks == 1 && (dev_pos || batch == 1);
     info->balanced = sp.bal ? 1u : 0u;
     info->heads_per_workgroup = sp.hpb;
     info->workgroups = sp.bal ? sp.kn.wgs : (uint32_t)(n_hb * sp.plan.n_chunks * batch);

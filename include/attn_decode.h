@@ -116,7 +116,10 @@ typedef struct attn_plan_info {
     uint32_t chunks;               /* chunked grid: chunks per (sequence, head
                                       block) (0 if balanced)                   */
     uint32_t launches;             /* 1: the split launch writes out; 2: a
-                                      combine launch follows                   */
+                                      combine launch follows.  For the
+                                      one-call entry points; the split /
+                                      combine pair is always two launches, its
+                                      split writing partial states            */
     uint64_t partial_slots;        /* one past the highest partial state the
                                       split launch may write (0 with one
                                       launch)                                  */

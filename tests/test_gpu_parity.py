@@ -379,6 +379,26 @@ def test_split_then_combine_matches_single_call(D):
     assert torch.equal(one, out)
 
 
+@pytest.mark.parametrize("S,H,D,cp", [(128, 4, 64, 100), (4096, 8, 128, 4095), (40000, 4, 64, 33333)],
+                         ids=["tiny", "short", "long"])
+def test_split_with_one_host_position_for_a_batch(S, H, D, cp):
+    """attn_decode_f16_split with a batch and one host current_pos for all of
+    it (the single-sequence plans, tiny, short and long, on a grid with a row
+    per sequence), then the combine: each sequence against the oracle."""
+    rng = np.random.default_rng(S + H)
+    B = 3
+    q, k, v = randn16(rng, (B, H, D), 2.0), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    ws = ad.alloc_workspace(B, H, D, S, DEV)
+    out = torch.empty((B, H, D), dtype=torch.float16, device=DEV)
+    ad.split(qd, kd, vd, cp, ws)
+    ad.combine(out, cp, B, H, D, S, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref, _, _ = oracle.decode(q[b], k[b], v[b], cp)
+        assert_close(out[b], ref, "b=%d" % b)
+
+
 def test_workspace_reuse_across_sizes_and_repeats():
     """One workspace reused by 72 calls of changing sizes and positions: every
     output matches its first run bit for bit."""

@@ -87,6 +87,17 @@ def test_decode_steps_always_merge_in_a_second_launch():
         assert plan(*args, flags=flags)["launches"] == 2
 
 
+def test_a_batch_with_one_host_position_is_the_split_pair():
+    """flags 0 with batch > 1 exists only as attn_decode_f16_split + combine:
+    two launches, partial states written, even when one chunk covers it."""
+    p1 = plan(1, 4, 64, 128, 100)
+    p3 = plan(3, 4, 64, 128, 100)
+    assert p1["launches"] == 1 and p1["partial_slots"] == 0
+    assert p3["launches"] == 2 and p3["chunks"] == 1
+    # one partial per (sequence, head) at least, every one with its slot
+    assert 3 * 4 <= p3["partial_slots"] <= p3["workspace_slots"]
+
+
 def span_of(S, cp, flags):
     if flags & (PLAN_DEVICE_POS | PLAN_PAGED):
         return S
