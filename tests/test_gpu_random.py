@@ -204,3 +204,70 @@ def test_random_softmax_and_rope(case):
     exact = oracle.rope(xr, pos[:, None].astype(np.int64), dims=dims, traditional=trad)
     assert_rotation(got.cpu().numpy().view(np.uint16), xr, exact, oracle.double_to_half(exact),
                     dims, trad, "rope case %d" % case)
+
+
+N_BATCH_CASES = 30
+
+
+def large_batch_draw(case, rng):
+    """Sizes for test_random_large_batches; the case number picks the region:
+    0 <= 256 KiB of K+V per 256-byte head block, 1 the 512 KiB band with just
+    enough sequences x heads for 256 workgroups (paged: one more), 2 longer
+    capacities with few sequences."""
+    paged = bool(case % 2)
+    region = case % 3
+    if region == 0:
+        D = int(rng.choice([8, 16, 32, 48, 64, 96, 128]))
+        H = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        B = int(rng.choice([16, 64, 200, 700]))
+        S = int(rng.choice([1, 16, 100, 300, 512]))
+        while B * S * H * D > 24 << 20:
+            S = max(1, S // 2)
+    elif region == 1:
+        D = int(rng.choice([64, 128]))
+        H = int(rng.choice([8, 16, 32]))
+        S = int(rng.choice([520, 600, 1000, 1024]))
+        heads_per_group = 2 if D == 64 else 1
+        B = -(-256 * heads_per_group // H) + int(rng.integers(0, 12)) + (1 if paged else 0)
+    else:
+        D = int(rng.choice([32, 64, 128]))
+        H = int(rng.choice([2, 4, 8]))
+        B = int(rng.choice([4, 16, 64]))
+        S = int(rng.choice([1100, 2048, 3000]))
+    if paged:   # whole pages
+        S = max(16, S // 16 * 16) if S >= 16 else S
+    return paged, B, S, H, D
+
+
+@pytest.mark.parametrize("case", range(N_BATCH_CASES))
+def test_random_large_batches(case):
+    """Batches of 4-700 sequences, dense or paged, drawn on both sides of the
+    one-chunk plans' edges (256 and 512 KiB of K+V per workgroup, 256
+    workgroups, head blocks widened past 8192 workgroups) and on the balanced
+    grid: every output against the oracle."""
+    rng = np.random.default_rng(5000 + case)
+    paged, B, S, H, D = large_batch_draw(case, rng)
+    pos = rng.integers(0, S + 2, B)
+    flags = ad.PLAN_PAGED if paged else ad.PLAN_DEVICE_POS
+    print("case", case, dict(B=B, S=S, H=H, D=D, paged=paged), ad.plan(B, H, D, S, 0, flags), flush=True)
+    q = randn16(rng, (B, H, D))
+    k = randn16(rng, (B, S, H, D))
+    v = randn16(rng, (B, S, H, D))
+    ref, _ = oracle.decode_batched(q, k, v, pos, threads=8)
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    if paged:
+        P = int(rng.choice([p for p in (1, 4, 16) if S % p == 0]))
+        MB = S // P
+        perm = rng.permutation(B * MB)
+        kp = np.empty((B * MB, P, H, D), np.float16)
+        vp = np.empty((B * MB, P, H, D), np.float16)
+        kp[perm] = k.reshape(B * MB, P, H, D)
+        vp[perm] = v.reshape(B * MB, P, H, D)
+        bt = perm.reshape(B, MB).astype(np.int32)
+        out = ad.decode_paged(torch.from_numpy(q).to(DEV), torch.from_numpy(kp).to(DEV),
+                              torch.from_numpy(vp).to(DEV), torch.from_numpy(bt).to(DEV), cp)
+    else:
+        out = ad.decode_batched(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                                torch.from_numpy(v).to(DEV), cp)
+    torch.cuda.synchronize()
+    close(out, ref, "large batch case %d" % case)
