@@ -1212,12 +1212,18 @@ const Knobs &env_knobs() {
 // toss-up, and at head_dim 256 it loses.  A paged cache needs more
 // workgroups than CUs there: at exactly one per CU it lost 8-28% on four of
 // five shapes, from 300 workgroups on it won 3-43%.
+// Other batches whose caches hold at most kMidBatchBytes of K+V take the
+// chunked grid aimed at 512 workgroups, with a combine: the balanced grid's
+// length scan and piece walk are not repaid at that size (16 x 8 heads x
+// 1024 positions: 18.7 -> 13.8 us; 4 x 32 x 1024: 19.5 -> 14.8; paged and
+// decode steps alike), while from 256 MiB on it is level or ahead.
 enum class Kind { single, batched, paged, stream, batched_chunked, scores, single_short, single_step,
-                  single_tiny, batched_short };
+                  single_tiny, batched_short, batched_mid };
 constexpr uint32_t kShortSpan = 8192;
 constexpr uint64_t kOneChunkBytes = 256u << 10;
 constexpr uint64_t kShortGroups = 8192;
 constexpr uint64_t kShortMinGroups = 256;   // the CU count
+constexpr uint64_t kMidBatchBytes = 128ull << 20;
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
@@ -1226,6 +1232,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     // workgroup per sequence and head block; smaller head blocks balance
     // ragged lengths better (2048 x 512 positions: +10% ragged, +4% full)
     else if (kind == Kind::batched_chunked) k = Knobs{256, 8192, 4, 2, 1, 0};
+    else if (kind == Kind::batched_mid) k = Knobs{512, 8192, 4, 2, 1, 0};
     else if (kind == Kind::stream) k = D <= 64 ? Knobs{1024, 8192, 8, 2, 1, 0} : Knobs{1024, 8192, 2, 2, 1, 0};
     else if (kind == Kind::scores) k = D <= 64 ? Knobs{1024, 8192, 4, 2, 1, 0} : Knobs{1024, 8192, 4, 8, 1, 0};
     else if (kind == Kind::single_short && D > 64) k = Knobs{512, 8192, 1, 2, 0, 0};
@@ -1317,7 +1324,8 @@ uint32_t chunk_bound_for(const Knobs &k, uint32_t batch, uint32_t H, uint32_t S)
 uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     uint32_t m = 0;
     for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::single_tiny, Kind::batched,
-                    Kind::paged, Kind::stream, Kind::batched_chunked, Kind::batched_short}) {
+                    Kind::paged, Kind::stream, Kind::batched_chunked, Kind::batched_short,
+                    Kind::batched_mid}) {
         const uint32_t c = chunk_bound_for(knobs(D, kd), batch, H, S);
         if (c > m) m = c;
     }
@@ -1358,7 +1366,8 @@ size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     size_t m = 0;
     for (Kind kd : {Kind::single, Kind::single_short, Kind::single_step, Kind::single_tiny, Kind::batched,
-                    Kind::paged, Kind::stream, Kind::batched_chunked, Kind::batched_short}) {
+                    Kind::paged, Kind::stream, Kind::batched_chunked, Kind::batched_short,
+                    Kind::batched_mid}) {
         const Knobs k = knobs(D, kd);
         const size_t n = (size_t)k.wgs * heads_per_wg(H, best, k.hpb) + (size_t)batch * H;
         if (n > m) m = n;
@@ -1527,6 +1536,8 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
             (D <= 128 && wg_bytes <= 2 * kOneChunkBytes &&
              (paged ? groups > kShortMinGroups : groups >= kShortMinGroups)))
             kind = Kind::batched_short;
+        else if ((uint64_t)batch * S * H * D * 4 <= kMidBatchBytes)
+            kind = Kind::batched_mid;
     }
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);

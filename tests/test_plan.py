@@ -41,30 +41,43 @@ def test_ragged_batch_workload_takes_the_balanced_grid():
     assert plan(64, 32, 128, 8192, flags=PLAN_PAGED)["balanced"] == 1
 
 
-@pytest.mark.parametrize("B,H,D,S,flags,one_chunk", [
+def kind_of(p):
+    if p["balanced"]:
+        return "balanced"
+    return "one" if p["launches"] == 1 and p["chunks"] == 1 else "chunked"
+
+
+@pytest.mark.parametrize("B,H,D,S,flags,kind", [
     # <= 256 KiB of K+V per 256-byte head block: one chunk, any workgroup count
-    (64, 32, 128, 128, PLAN_DEVICE_POS, True),
-    (2, 8, 128, 512, PLAN_DEVICE_POS, True),
-    (2, 8, 128, 512, PLAN_PAGED, True),
-    (64, 16, 256, 128, PLAN_DEVICE_POS, True),
-    # 512 KiB per workgroup: one chunk from 256 workgroups on (paged: more than 256)
-    (8, 32, 128, 1024, PLAN_DEVICE_POS, True),
-    (4, 32, 128, 1024, PLAN_DEVICE_POS, False),
-    (8, 64, 64, 1024, PLAN_DEVICE_POS, True),
-    (8, 64, 64, 1024, PLAN_PAGED, False),
-    (300, 2, 64, 608, PLAN_PAGED, True),
-    (16, 32, 128, 1024, PLAN_PAGED, True),
-    # head_dim 256 keeps the balanced grid past 256 KiB
-    (64, 8, 256, 512, PLAN_DEVICE_POS, False),
-    # 1 MiB per workgroup: balanced
-    (64, 8, 128, 2048, PLAN_DEVICE_POS, False),
+    (64, 32, 128, 128, PLAN_DEVICE_POS, "one"),
+    (2, 8, 128, 512, PLAN_DEVICE_POS, "one"),
+    (2, 8, 128, 512, PLAN_PAGED, "one"),
+    (64, 16, 256, 128, PLAN_DEVICE_POS, "one"),
+    # 512 KiB per workgroup: one chunk from 256 workgroups on (paged: more
+    # than 256); with fewer, a cache of <= 128 MiB takes the chunked grid
+    (8, 32, 128, 1024, PLAN_DEVICE_POS, "one"),
+    (4, 32, 128, 1024, PLAN_DEVICE_POS, "chunked"),
+    (8, 64, 64, 1024, PLAN_DEVICE_POS, "one"),
+    (8, 64, 64, 1024, PLAN_PAGED, "chunked"),
+    (300, 2, 64, 608, PLAN_PAGED, "one"),
+    (16, 32, 128, 1024, PLAN_PAGED, "one"),
+    # head_dim 256 past 256 KiB: 268 MB of K+V, the balanced grid
+    (64, 8, 256, 512, PLAN_DEVICE_POS, "balanced"),
+    # 1 MiB per workgroup: 537 MB, balanced
+    (64, 8, 128, 2048, PLAN_DEVICE_POS, "balanced"),
+    # caches of <= 128 MiB of K+V outside the one-chunk rules: chunked grid
+    (16, 8, 128, 1024, PLAN_DEVICE_POS, "chunked"),
+    (16, 16, 64, 2048, PLAN_PAGED, "chunked"),
+    (4, 8, 128, 4096, PLAN_DEVICE_POS | PLAN_STEP, "chunked"),
+    # 268 MB: balanced
+    (32, 8, 128, 2048, PLAN_DEVICE_POS, "balanced"),
+    (8, 8, 128, 8192, PLAN_PAGED, "balanced"),
 ])
-def test_short_capacity_rule(B, H, D, S, flags, one_chunk):
+def test_batch_plan_rules(B, H, D, S, flags, kind):
     p = plan(B, H, D, S, flags=flags)
-    got = p["balanced"] == 0 and p["chunks"] == 1 and p["launches"] == 1
-    assert got == one_chunk, p
-    if not one_chunk:
-        assert p["balanced"] == 1
+    assert kind_of(p) == kind, p
+    if kind == "chunked" and not flags & PLAN_STEP and B * H <= 512:
+        assert 256 < p["workgroups"] <= 1024, p   # aimed at 512
 
 
 def test_many_head_blocks_are_widened():
