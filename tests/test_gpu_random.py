@@ -11,7 +11,7 @@ import torch
 
 import decode_attention_kv_seq_amd as ad
 import oracle
-from test_gpu_decode_step import assert_rotation
+from test_gpu_decode_step import assert_rotation, check_step, run_step_batched
 from test_gpu_softmax import check as softmax_check
 
 pytestmark = pytest.mark.gpu
@@ -271,3 +271,22 @@ def test_random_large_batches(case):
                                 torch.from_numpy(v).to(DEV), cp)
     torch.cuda.synchronize()
     close(out, ref, "large batch case %d" % case)
+
+
+@pytest.mark.parametrize("case", range(18))
+def test_random_large_batch_steps(case):
+    """The decode step on batches drawn like test_random_large_batches (the
+    one-chunk, mid-size and balanced plans), dense caches: six sampled
+    sequences, the first and last among them, against the oracle's step --
+    output, the appended rows, every other row unchanged."""
+    rng = np.random.default_rng(7000 + case)
+    _, B, S, H, D = large_batch_draw(case * 2, rng)   # the dense draws
+    cps = rng.integers(0, S + 2, B)
+    print("case", case, dict(B=B, S=S, H=H, D=D), ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS | ad.PLAN_STEP),
+          flush=True)
+    q, kn, vn = (randn16(rng, (B, H, D)) for _ in range(3))
+    kc, vc = randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    out, kg, vg = run_step_batched(q, kn, vn, kc, vc, cps, D)
+    for b in sorted({0, B - 1, *rng.choice(B, 4, replace=False).tolist()}):
+        check_step(out[b], kg[b], vg[b], kc[b], vc[b], q[b], kn[b], vn[b], int(cps[b]), D, False,
+                   what="case %d sequence %d" % (case, b))
