@@ -503,6 +503,37 @@ def test_combine_with_many_chunks(S, D):
     assert_close(out[0], ref, "S=%d D=%d" % (S, D))
 
 
+@pytest.mark.parametrize("B,S,H,D,offset", [(64, 2048, 4, 100, 0), (40, 8192, 2, 72, 1), (48, 2048, 8, 48, 2),
+                                             (48, 2048, 4, 136, 4), (24, 4096, 4, 250, 0)],
+                         ids=["d100_8B", "d72_off2B", "d48_off4B", "d136_off8B", "d250_4B"])
+def test_balanced_grid_with_narrow_loads(B, S, H, D, offset):
+    """The balanced grid on the lane layouts below 16-byte loads: head_dims
+    that are not multiples of 8 and tensors offset by 2, 4 or 8 bytes.  The
+    caches (150-400 MB of K+V) are past the chunked plans, which the plan
+    query confirms; every output against the oracle, and the score dump of
+    four sequences."""
+    assert ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS)["balanced"] == 1
+    rng = np.random.default_rng(B * S + D)
+    q, k, v = randn16(rng, (B, H, D), 2.0), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, S + 2, B)
+    pos[::7] = 0
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+
+    def place(a):
+        flat = torch.empty(a.size + offset, dtype=torch.float16, device=DEV)
+        t = flat[offset:].view(a.shape)
+        t.copy_(torch.from_numpy(a))
+        return t
+
+    out, dump = ad.decode_batched(place(q), place(k), place(v), cp, dump=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_batched(q, k, v, pos, threads=8)
+    assert_close(out, ref, "D=%d offset=%d" % (D, offset))
+    for b in (0, 1, B // 2, B - 1):
+        _, ref_s, _ = oracle.decode(q[b], k[b], v[b], int(pos[b]), want_scores=True)
+        assert_dump_close(dump[b], ref_s, q[b], k[b], int(pos[b]), "b=%d" % b)
+
+
 def test_batched_extreme_ragged_lengths():
     """One long sequence among many of length 1 and a few in between: the
     balanced grid splits the long one across many workgroups."""
@@ -591,6 +622,25 @@ def test_paged_equals_dense_batched(page_size):
     assert torch.equal(paged, dense)
     for b in range(B):
         assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "page %d b=%d" % (page_size, b))
+
+
+@pytest.mark.parametrize("B,S,H,D", [(64, 2048, 4, 100), (24, 4096, 4, 250)], ids=["d100", "d250"])
+def test_paged_balanced_grid_with_narrow_loads(B, S, H, D):
+    """A paged pool (16-position pages, shuffled) on the balanced grid with
+    head_dims that take 8- and 4-byte loads: every output against the
+    oracle and bitwise equal to the dense call on the same values."""
+    assert ad.plan(B, H, D, S, 0, ad.PLAN_PAGED)["balanced"] == 1
+    rng = np.random.default_rng(S + D)
+    q, k, v = randn16(rng, (B, H, D), 2.0), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, S + 2, B)
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    kp, vp, bt = page_dense_cache(k, v, 16, rng)
+    paged = ad.decode_paged(to_dev(q), to_dev(kp), to_dev(vp), to_dev(bt), cp)
+    dense = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_batched(q, k, v, pos, threads=8)
+    assert_close(paged, ref, "paged D=%d" % D)
+    assert torch.equal(paged, dense)
 
 
 def test_paged_workload_sampled():
