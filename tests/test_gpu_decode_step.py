@@ -270,6 +270,23 @@ def test_step_batched_ragged(D, dims, trad):
                    trad, what="sequence %d" % b)
 
 
+@pytest.mark.parametrize("D,dims,trad", [(48, 48, False), (64, 32, True)])
+def test_step_batched_on_the_balanced_grid(D, dims, trad):
+    """The batched step with caches past the chunked plans (9 sequences x 8
+    heads x 16384 positions, 226-302 MB of K+V: the balanced grid, as the
+    plan query confirms), head_dim 48 taking 8-byte loads: every sequence
+    against the oracle's step."""
+    rng = np.random.default_rng(D + dims + 1)
+    B, S, H = 9, 16384, 8
+    assert ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS | ad.PLAN_STEP)["balanced"] == 1
+    cps = [0, 1, 16383, 20000, 5, 8192, 77, 16382, 4000]
+    q, kn, vn, kc, vc, cps = batched_inputs(rng, B, S, H, D, cps)
+    out, kg, vg = run_step_batched(q, kn, vn, kc, vc, cps, dims, trad)
+    for b in range(B):
+        check_step(out[b], kg[b], vg[b], kc[b], vc[b], q[b], kn[b], vn[b], int(cps[b]), dims,
+                   trad, what="sequence %d" % b)
+
+
 def test_step_batched_every_sequence_at_position_zero():
     """No earlier positions anywhere: the split launch streams nothing."""
     rng = np.random.default_rng(9)
