@@ -74,8 +74,16 @@ def assert_rotation(got_bits, x, exact, oracle_bits, dims, traditional, what="")
     assert diff.sum() <= max(2, n_rot // 100), "%s: %d of %d fp16 words differ" % (
         what, int(diff.sum()), n_rot)
     if diff.any():
-        steps = np.abs(got_bits[diff].astype(np.int64) - oracle_bits[diff].astype(np.int64))
-        assert steps.max() <= 1, "%s: rounding differs by more than one step" % what
+        # fp16 steps apart on the ordered line (+0 and -0 equal), against one
+        # step of rounding, or the width of the bound in steps where it spans
+        # more: a rotation that cancels (|exact| far below |a|+|b|) keeps the
+        # fp32 rotation's error, which is of the inputs' size
+        def ordered(bits):
+            b = bits.astype(np.int64)
+            return np.where(b & 0x8000, -(b & 0x7FFF), b)
+        steps = np.abs(ordered(got_bits[diff]) - ordered(oracle_bits[diff]))
+        allowed = np.maximum(1.0, np.ceil(bound / f16_ulp(np.abs(exact))))[diff]
+        assert np.all(steps <= allowed), "%s: rounding differs by more steps than the bound spans" % what
 
 
 def assert_close(got_f16, ref, what=""):

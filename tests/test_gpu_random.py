@@ -94,7 +94,9 @@ def test_random_paged(case):
     close(out, ref, "paged case %d" % case)
 
 
-@pytest.mark.parametrize("case", range(N_CASES))
+# case 74 adds a rotation that cancels (-2.0e-4 from inputs near 1.8), where
+# the fp32 rotation's error spans many fp16 steps of the result
+@pytest.mark.parametrize("case", list(range(N_CASES)) + [74])
 def test_random_decode_step(case):
     rng = np.random.default_rng(3000 + case)
     D, H, S = shape_draw(rng)
