@@ -349,6 +349,10 @@ WORKLOADS = {
         # scattered through one pool
         Workload("b64_h32_d128_cap8192_ragged_paged16", n_heads=32, head_dim=128,
                  seq_len=8192, cur_pos=None, seed=4, batch=64, page_size=16),
+        # a batch of short capacity: one launch, one chunk per sequence and
+        # head block
+        Workload("b256_h32_d128_cap64_ragged", n_heads=32, head_dim=128,
+                 seq_len=64, cur_pos=None, seed=6, batch=256),
     ]
 }
 
