@@ -43,7 +43,7 @@ _lib = None
 class PlanInfo(ctypes.Structure):
     """attn_plan_info of include/attn_decode.h."""
     _fields_ = [("balanced", ctypes.c_uint32), ("heads_per_workgroup", ctypes.c_uint32),
-                ("workgroups", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
+                ("workgroups", ctypes.c_uint64), ("chunk", ctypes.c_uint32),
                 ("chunks", ctypes.c_uint32), ("launches", ctypes.c_uint32),
                 ("partial_slots", ctypes.c_uint64), ("workspace_slots", ctypes.c_uint64)]
 

@@ -1224,6 +1224,8 @@ constexpr uint64_t kOneChunkBytes = 256u << 10;
 constexpr uint64_t kShortGroups = 8192;
 constexpr uint64_t kShortMinGroups = 256;   // the CU count
 constexpr uint64_t kMidBatchBytes = 128ull << 20;
+// A dispatch holds its grid size in work-items, 32 bits per dimension.
+constexpr uint64_t kMaxGridItems = 0xFFFFFFFFull;
 
 Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
@@ -1399,8 +1401,9 @@ attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
         return fail(ATTN_ERR_DIM, "seq_len=%u exceeds 2^31", S);
     if (batch > 65535u)
         return fail(ATTN_ERR_DIM, "batch=%u exceeds 65535", batch);
-    if ((uint64_t)batch * H > 0x7fffffffull)
-        return fail(ATTN_ERR_DIM, "batch*n_heads too large");
+    if (cdiv((uint64_t)batch * H, 4) * 256 > kMaxGridItems)   // the combine's wave grid
+        return fail(ATTN_ERR_DIM, "batch*n_heads=%llu exceeds %llu", (unsigned long long)batch * H,
+                    (unsigned long long)(kMaxGridItems / 256 * 4));
     return ok();
 }
 
@@ -1570,6 +1573,10 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     const uint32_t hpb = sp.hpb;
     const bool bal = sp.bal;
     const Plan &plan = sp.plan;
+    const uint64_t grid_x = bal ? kn.wgs : (uint64_t)(H / hpb) * plan.n_chunks;
+    if (grid_x * kThreads > kMaxGridItems)
+        return fail(ATTN_ERR_DIM, "%llu workgroups per sequence exceed the dispatch limit of %llu",
+                    (unsigned long long)grid_x, (unsigned long long)(kMaxGridItems / kThreads));
     const SplitFn fn =
         scores_in ? pick_split<false, false, kModePv>(ly, kn, false)
         : rope    ? (pg ? pick_split<false, true, kModeStep>(ly, kn, bal)
@@ -1781,12 +1788,16 @@ attn_status_t attn_decode_plan(uint32_t batch, uint32_t n_heads, uint32_t head_d
     const SplitPlan sp = plan_split(ly, dev_pos, current_pos, paged, step, scores, batch, n_heads,
                                     head_dim, seq_len);
     const uint64_t n_hb = n_heads / sp.hpb;
+    const uint64_t grid_x = sp.bal ? sp.kn.wgs : n_hb * sp.plan.n_chunks;
+    if (grid_x * kThreads > kMaxGridItems)
+        return fail(ATTN_ERR_DIM, "%llu workgroups per sequence exceed the dispatch limit of %llu",
+                    (unsigned long long)grid_x, (unsigned long long)(kMaxGridItems / kThreads));
     // one launch: a one-call entry point (a batch with one host current_pos
     // exists only as the split / combine pair) whose plan has one chunk
     const bool direct = !sp.bal && !step && sp.plan.n_chunks == 1 && (dev_pos || batch == 1);
     info->balanced = sp.bal ? 1u : 0u;
     info->heads_per_workgroup = sp.hpb;
-    info->workgroups = sp.bal ? sp.kn.wgs : (uint32_t)(n_hb * sp.plan.n_chunks * batch);
+    info->workgroups = sp.bal ? (uint64_t)sp.kn.wgs : grid_x * batch;
     info->chunk = sp.bal ? 0u : sp.plan.chunk;
     info->chunks = sp.bal ? 0u : sp.plan.n_chunks;
     info->launches = direct ? 1u : 2u;
@@ -1921,10 +1932,14 @@ attn_status_t attn_qk_f16(const uint16_t *q, const uint16_t *k_cache, uint16_t *
     a.scale = (float)(1.0 / sqrt((double)head_dim));
     a.scores_out = scores;
     a.batch = 1;
-    a.grid = a.n_hb * plan.n_chunks;
     const uint64_t masked = (uint64_t)(seq_len - L) * n_heads;
     const uint64_t fill = masked ? cdiv(masked, (uint64_t)kThreads * 16) : 0;
     const uint32_t n_fill = (uint32_t)(fill < 1024 ? fill : 1024);
+    const uint64_t grid_x = (uint64_t)a.n_hb * plan.n_chunks;
+    if ((grid_x + n_fill) * kThreads > kMaxGridItems)
+        return fail(ATTN_ERR_DIM, "%llu workgroups exceed the dispatch limit of %llu",
+                    (unsigned long long)(grid_x + n_fill), (unsigned long long)(kMaxGridItems / kThreads));
+    a.grid = (uint32_t)grid_x;
     hipLaunchKernelGGL(fn, dim3(a.grid + n_fill), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), a);
     return hip_check("score kernel launch");

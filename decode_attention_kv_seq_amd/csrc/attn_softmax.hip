@@ -249,6 +249,14 @@ attn_status_t attn_softmax_f32(const float *x, float *out, uint32_t rows, uint32
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                     workspace_bytes, need);
     const SmPath path = softmax_path(rows, cols);
+    // a dispatch holds its grid size in work-items, 32 bits per dimension
+    const uint64_t items = path == SmPath::wave     ? (uint64_t)rows * 64
+                         : path == SmPath::row256   ? (uint64_t)rows * 256
+                         : path == SmPath::row512   ? (uint64_t)rows * 512
+                         : path == SmPath::row1024  ? (uint64_t)rows * 1024
+                                                    : (uint64_t)rows * cdiv(cols, kSmChunk) * 256;
+    if (items > 0xFFFFFFFFull)
+        return fail(ATTN_ERR_DIM, "rows=%u x cols=%u exceeds the dispatch limit", rows, cols);
     const bool v4 = cols % 4 == 0 && aligned(x, 16) && aligned(out, 16);
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *stats = static_cast<float *>(workspace);

@@ -56,8 +56,10 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
     ATTN_ERR_DIM = 2,         /* a size is 0, head_dim > ATTN_MAX_HEAD_DIM,
-                                 seq_len > 2^31, batch > 65535, or the cache
-                                 is too large to index                         */
+                                 seq_len > 2^31, batch > 65535,
+                                 batch*n_heads > 67108860, the cache is too
+                                 large to index, or a launch would exceed the
+                                 GPU's dispatch limit (2^32 - 1 work-items)   */
     ATTN_ERR_ALIGN = 3,       /* fp16 pointer not 2-byte aligned, fp32/uint32
                                  pointer not 4-byte aligned, workspace not
                                  16-byte aligned                                */
@@ -110,7 +112,7 @@ typedef struct attn_plan_info {
     uint32_t balanced;             /* 1: balanced grid (equal positions per
                                       workgroup across the batch); 0: chunked */
     uint32_t heads_per_workgroup;  /* heads one split workgroup reads together */
-    uint32_t workgroups;           /* workgroups of the split launch          */
+    uint64_t workgroups;           /* workgroups of the split launch          */
     uint32_t chunk;                /* chunked grid: positions per chunk (0 if
                                       balanced)                                */
     uint32_t chunks;               /* chunked grid: chunks per (sequence, head

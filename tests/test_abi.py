@@ -225,6 +225,39 @@ def test_softmax_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, 1 << 20, 1 << 31, FAKE, 1 << 40, None) == DIM
 
 
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="stand-in pointers pass every check but the dispatch limit: host-only")
+def test_dispatch_limits(lib):
+    """Calls whose launch would exceed the GPU's dispatch limit (2^32 - 1
+    work-items per grid dimension) are refused with ATTN_ERR_DIM before any
+    HIP call, though every other check passes: a paged batch that declares a
+    2^31-position capacity over a small pool, more than 67108860 sequences x
+    heads (the merge's grid), a softmax of 70 million one-column rows (one
+    wave per row), the scores pass over 65536 heads x 2^31 positions; the
+    plan query refuses the same sizes."""
+    big = 1 << 62
+    # paged, 1100 sequences (chunked grid) x 512 heads, capacity 65536 x 32768
+    assert lib.attn_decode_f16_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1100, 512, 128, 65536, 32768,
+                                     1, None, FAKE, big, None) == DIM
+    assert b"dispatch limit" in lib.attn_last_error()
+    # 128 heads stay within the limit per sequence, 9.2e9 workgroups in all
+    assert ad.plan(1100, 128, 128, 1 << 31, 0, ad.PLAN_PAGED)["workgroups"] > 1 << 32
+    with pytest.raises(ad.AttnError):
+        ad.plan(1100, 512, 128, 1 << 31, 0, ad.PLAN_PAGED)
+    # sequences x heads
+    assert lib.attn_decode_workspace_bytes(65535, 1025, 8, 1) == 0
+    assert lib.attn_decode_workspace_bytes(65535, 1024, 8, 1) > 0
+    assert lib.attn_decode_f16_batched(FAKE, FAKE, FAKE, FAKE, FAKE, 65535, 1025, 8, 1, None,
+                                       FAKE, big, None) == DIM
+    # softmax: 70M rows of one column take a wave each
+    assert lib.attn_softmax_f32(FAKE, FAKE, 70000000, 1, FAKE, big, None) == DIM
+    assert b"dispatch limit" in lib.attn_last_error()
+    # the scores pass and a single-sequence plan over 65536 heads x 2^31 positions
+    assert lib.attn_qk_f16(FAKE, FAKE, FAKE, 65536, 1, 1 << 31, (1 << 31) - 1, None) == DIM
+    with pytest.raises(ad.AttnError):
+        ad.plan(1, 65536, 1, 1 << 31, (1 << 31) - 1, 0)
+
+
 def test_paged_step_rejects_bad_arguments(lib):
     f = lib.attn_decode_step_f16_paged
 
