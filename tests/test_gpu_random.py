@@ -11,7 +11,8 @@ import torch
 
 import decode_attention_kv_seq_amd as ad
 import oracle
-from test_gpu_decode_step import assert_rotation, check_step, run_step_batched
+from test_gpu_decode_step import (assert_rotation, batched_inputs, check_step, run_step_batched,
+                                  scatter_pages)
 from test_gpu_softmax import check as softmax_check
 
 pytestmark = pytest.mark.gpu
@@ -291,4 +292,44 @@ def test_random_large_batch_steps(case):
     out, kg, vg = run_step_batched(q, kn, vn, kc, vc, cps, D)
     for b in sorted({0, B - 1, *rng.choice(B, 4, replace=False).tolist()}):
         check_step(out[b], kg[b], vg[b], kc[b], vc[b], q[b], kn[b], vn[b], int(cps[b]), D, False,
+                   what="case %d sequence %d" % (case, b))
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_paged_step(case):
+    """The decode step on shuffled page pools (pages of 1-64 positions),
+    random batches: the dense step's output bits where both take the same
+    plan, the new rows in the right pages and nothing else written, and
+    three sequences against the oracle's step."""
+    rng = np.random.default_rng(11000 + case)
+    P = int(rng.choice([1, 2, 4, 16, 64]))
+    MB = int(rng.choice([1, 2, 5, 16, 64]))
+    S = P * MB
+    D = int(rng.choice([8, 16, 48, 64, 96, 128]))
+    H = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.choice([1, 3, 8, 40, 300]))
+    while B * S * H * D > 8 << 20:
+        B = max(1, B // 2)
+    trad = bool(rng.integers(0, 2))
+    cps = rng.integers(0, S + 2, B)
+    print("case", case, dict(B=B, S=S, H=H, D=D, P=P, trad=trad), flush=True)
+    q, kn, vn, kc, vc, cps = batched_inputs(rng, B, S, H, D, cps)
+    dense_out, dense_k, dense_v = run_step_batched(q, kn, vn, kc, vc, cps, D, trad)
+    kp, vp, bt = scatter_pages(kc, vc, P, rng)
+    kp_d, vp_d = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    out = ad.decode_step_paged(torch.from_numpy(q).to(DEV), torch.from_numpy(kn).to(DEV),
+                               torch.from_numpy(vn).to(DEV), kp_d, vp_d, torch.from_numpy(bt).to(DEV),
+                               torch.from_numpy(cps.astype(np.int32)).to(DEV), traditional=trad).cpu()
+    torch.cuda.synchronize()
+    if ad.plan(B, H, D, S, 0, ad.PLAN_PAGED | ad.PLAN_STEP) == ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS | ad.PLAN_STEP):
+        assert torch.equal(out, dense_out)
+    want_k, want_v = kp.copy(), vp.copy()
+    for b in range(B):
+        pos = min(int(cps[b]), S - 1)
+        want_k[bt[b, pos // P], pos % P] = dense_k[b, pos]
+        want_v[bt[b, pos // P], pos % P] = dense_v[b, pos]
+    assert np.array_equal(kp_d.cpu().numpy().view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(vp_d.cpu().numpy().view(np.uint16), want_v.view(np.uint16))
+    for b in sorted({0, B - 1, B // 2}):
+        check_step(out[b], dense_k[b], dense_v[b], kc[b], vc[b], q[b], kn[b], vn[b], int(cps[b]), D, trad,
                    what="case %d sequence %d" % (case, b))
