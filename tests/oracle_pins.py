@@ -744,6 +744,83 @@ def pin_softmax_equals_decode_weights(orc):
     assert np.all(np.abs(out[:, : cp + 1] - w[:, : cp + 1]) <= bound[:, : cp + 1] + 1e-300)
 
 
+# ---------------------------------------------------------------- batch and host threads
+# The pages define one sequence; a batch is read as independent sequences of
+# one cache capacity, each with its own current_pos (the oracle's batched form
+# loops over single-sequence calls).  Host threads only split heads or rows.
+
+
+def _sdpa_f64(q, k, v, L):
+    """torch float64 attention of one sequence: q [H, D], k/v [S, H, D], the
+    first L positions visible (boolean mask)."""
+    S, H, D = k.shape
+    qt = torch.from_numpy(q.astype(np.float64)).view(H, 1, D)
+    kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2).contiguous()
+    vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2).contiguous()
+    mask = (torch.arange(S) < L).view(1, 1, S).expand(H, 1, S)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    return ref.view(H, D).numpy()
+
+
+def pin_batched_is_independent_sequences(orc):
+    """Five sequences with distinct queries, caches and lengths (current_pos
+    0, the last slot, past the cache, two in between): each output equals
+    torch's float64 attention under that sequence's own mask, and the
+    single-sequence oracle on that sequence bitwise; each score row is -inf
+    exactly after that sequence's current_pos."""
+    rng = _rng(40)
+    B, S, H, D = 5, 23, 3, 16
+    cps = [0, S - 1, S + 4, 7, 12]
+    q = _randn_f16(rng, (B, H, D), 1.5)
+    k = _randn_f16(rng, (B, S, H, D))
+    v = _randn_f16(rng, (B, S, H, D))
+    for threads in (1, 2):
+        out, sc = orc.decode_batched(q, k, v, np.array(cps, dtype=np.int64), want_scores=True,
+                                     threads=threads)
+        assert out.shape == (B, H, D) and sc.shape == (B, H, S)
+        for b, cp in enumerate(cps):
+            L = min(cp, S - 1) + 1
+            assert np.allclose(out[b], _sdpa_f64(q[b], k[b], v[b], L), rtol=1e-12, atol=1e-13), b
+            one, s1, _ = orc.decode(q[b], k[b], v[b], cp, want_scores=True)
+            assert np.array_equal(out[b], one), b
+            assert np.array_equal(sc[b], s1), b
+            assert np.all(sc[b][:, L:] == -np.inf), b
+            assert np.all(np.isfinite(sc[b][:, :L])), b
+
+
+def pin_host_threads_split_heads_exactly(orc):
+    """Heads split over host threads, thread counts that do not divide the
+    head count among them: every head is computed once, by the same routine,
+    so outputs, scores and weights are bitwise those of one thread, and match
+    torch's float64 attention."""
+    rng = _rng(41)
+    S, H, D, cp = 19, 7, 24, 15
+    q = _randn_f16(rng, (H, D), 1.5)
+    k = _randn_f16(rng, (S, H, D))
+    v = _randn_f16(rng, (S, H, D))
+    base, s1, w1 = orc.decode(q, k, v, cp, want_scores=True, want_weights=True)
+    ref = _sdpa_f64(q, k, v, cp + 1)
+    for t in (2, 3, 5, 6, 7, 9):
+        out, s, w = orc.decode(q, k, v, cp, want_scores=True, want_weights=True, threads=t)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-13), t
+        assert np.array_equal(out, base), t
+        assert np.array_equal(s, s1), t
+        assert np.array_equal(w, w1), t
+
+
+def pin_softmax_host_threads_split_rows_exactly(orc):
+    """Rows split over host threads (counts that do not divide the row count):
+    bitwise the one-thread result, and torch's float64 softmax."""
+    rng = _rng(42)
+    x = (rng.standard_normal((11, 37)) * 3).astype(np.float32)
+    base = orc.softmax_rows(x)
+    ref = torch.softmax(torch.from_numpy(x.astype(np.float64)), dim=1).numpy()
+    for t in (2, 3, 4, 10, 11, 16):
+        out = orc.softmax_rows(x, threads=t)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-15), t
+        assert np.array_equal(out, base), t
+
+
 ALL_PINS = [
     pin_half_decoder_all_patterns,
     pin_one_hot_query_scores,
@@ -785,4 +862,7 @@ ALL_PINS = [
     pin_softmax_masked_entries,
     pin_softmax_rows_are_independent_and_row_major,
     pin_softmax_equals_decode_weights,
+    pin_batched_is_independent_sequences,
+    pin_host_threads_split_heads_exactly,
+    pin_softmax_host_threads_split_rows_exactly,
 ]

@@ -4,7 +4,13 @@ Each mutant is a one-line edit of ``oracle/attn_oracle.c`` of the kind that
 slips into a hand-written attention routine (a dropped term, a wrong sign,
 index or operand).  The copy is built in a temporary directory on the CPU;
 every mutant must fail at least one pin.  No GPU is involved.
+
+``PY_MUTANTS`` do the same to the oracle's Python wrapper
+(``oracle/__init__.py``), whose batch loop and host-thread split of heads and
+rows carry no arithmetic but choose which inputs each call sees: the patched
+copy is loaded as a module of its own over the real oracle library.
 """
+import importlib.util
 import os
 
 import pytest
@@ -49,6 +55,49 @@ MUTANTS = {
     "softmax_last_column_dropped": ("        for (size_t c = 0; c < C; ++c) {\n            o[c] = exp(", "        for (size_t c = 0; c + 1 < C; ++c) {\n            o[c] = exp("),
 }
 
+PY_MUTANTS = {
+    "batched_shared_current_pos": ("int(current_pos[b])", "int(current_pos[0])"),
+    "batched_query_of_first_sequence": ("self.decode(q[b], k[b], v[b]", "self.decode(q[0], k[b], v[b]"),
+    "batched_cache_of_first_sequence": ("self.decode(q[b], k[b], v[b]", "self.decode(q[b], k[0], v[0]"),
+    "threads_head_range_short_by_one": (
+        "bounds = [(H * i // threads, H * (i + 1) // threads) for i in range(threads)]",
+        "bounds = [(H * i // threads, H * (i + 1) // threads - 1) for i in range(threads)]"),
+    "threads_last_head_range_dropped": (
+        "bounds = [(H * i // threads, H * (i + 1) // threads) for i in range(threads)]",
+        "bounds = [(H * i // threads, H * (i + 1) // threads) for i in range(threads - 1)]"),
+    "softmax_threads_row_skipped": ("(rows * i // threads, rows * (i + 1) // threads)",
+                                    "(rows * i // threads + (i > 0), rows * (i + 1) // threads)"),
+}
+
+
+def _failed_pins(orc):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, RuntimeError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_wrapper_mutant_fails_a_pin(name, tmp_path):
+    old, new = PY_MUTANTS[name]
+    src_path = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+    with open(src_path) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation site missing or ambiguous: %r" % old
+    path = os.path.join(tmp_path, "mutant_wrapper.py")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    # a module inside the oracle package, so its relative import resolves
+    spec = importlib.util.spec_from_file_location("oracle._mutant_" + name, path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    oracle.load()   # the real C library, built if missing
+    failed = _failed_pins(mod.OracleLib(_build.LIB))
+    assert failed, "no pin caught wrapper mutant %s" % name
+
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_fails_a_pin(name, tmp_path):
@@ -61,11 +110,5 @@ def test_mutant_fails_a_pin(name, tmp_path):
     with open(c_path, "w") as f:
         f.write(mutated)
     lib = _build.build(src=c_path, lib=os.path.join(tmp_path, "libmutant.so"))
-    orc = oracle.OracleLib(lib)
-    failed = []
-    for pin in oracle_pins.ALL_PINS:
-        try:
-            pin(orc)
-        except (AssertionError, RuntimeError, ValueError, FloatingPointError):
-            failed.append(pin.__name__)
+    failed = _failed_pins(oracle.OracleLib(lib))
     assert failed, "no pin caught mutant %s" % name
