@@ -173,7 +173,7 @@ def alloc_workspace(batch, n_heads, head_dim, seq_len, device) -> torch.Tensor:
     n = workspace_bytes(batch, n_heads, head_dim, seq_len)
     if n == 0:
         raise ValueError("invalid sizes")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def _cp_tensor(cp: torch.Tensor, batch: int, device) -> torch.Tensor:

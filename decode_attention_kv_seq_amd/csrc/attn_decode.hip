@@ -278,24 +278,8 @@ struct SplitArgs {
     uint32_t max_blocks;      // block-table row length
     uint32_t num_blocks;      // pages in the pool
     uint32_t page_shift;      // log2(positions per page)
-    uint32_t grid_flags;      // chunked grid: kGridRotate, kGridEven, ...
-    uint32_t n_cu;            // compute units (dispatch rounds of the grid)
-    float rank_step;          // kGridRankWeight: weight lost per dispatch round
-    uint32_t *merge_cnt;      // in-launch merge: arrivals per (sequence, head block), or null
-    uint32_t merge_groups;    // ... summed in the merge launch's chunk-group order
     RopeArgs rope;            // decode step: q is rotated, the new token's slot is skipped
 };
-
-// Chunked-grid variants: head blocks rotated by chunk index (each head block's
-// chunks spread over the XCDs); chunk boundaries spread evenly over the
-// valid positions (the chunk count unchanged).
-constexpr uint32_t kGridRotate = 1, kGridEven = 2, kGridReverse = 4, kGridRankPrio = 8, kGridRankWeight = 16;
-
-// Sum over i < x of floor(i / q).
-__device__ __forceinline__ uint64_t floor_prefix(uint64_t x, uint64_t q) {
-    const uint64_t t = x / q;
-    return t == 0 ? 0 : q * t * (t - 1) / 2 + t * (x - q * t);
-}
 
 // Workspace header written by the split launch and read by the combine.
 enum : uint32_t { kHdrBalanced = 0, kHdrChunk, kHdrNcStride, kHdrNHb, kHdrHpb, kHdrGrid, kHdrWords };
@@ -324,12 +308,11 @@ struct PieceDst {
     uint16_t *out;
 };
 
-// What a split launch computes: the one-pass decode (kModeDecodeMerge: with
-// the partials merged in the same launch, chunked grid); softmax.V from stored
+// What a split launch computes: the one-pass decode; softmax.V from stored
 // fp16 scores (the page's second dispatch); the decode step (q rotated, the
 // new token's slot left to the combine); or only the scores, written as fp16
 // (the page's first dispatch).
-enum : int { kModeDecode = 0, kModePv = 1, kModeStep = 2, kModeQk = 3, kModeDecodeMerge = 4 };
+enum : int { kModeDecode = 0, kModePv = 1, kModeStep = 2, kModeQk = 3 };
 
 // Stream positions [c0, c_end) of head block hb of sequence b through the
 // online softmax and leave one merged state per head at `dst` (kModeQk: write
@@ -630,15 +613,6 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         }
         if (dst.out) {
             dst.out[ho * a.D + d] = f2h_rne(o / lsum);
-        } else if constexpr (MODE == kModeDecodeMerge) {
-            // merged in this launch: agent-scope stores, written through to
-            // where every workgroup of the device reads them
-            __hip_atomic_store(dst.po + ho * dst.po_hs + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d == 0) {
-                __hip_atomic_store(dst.pml + ho * dst.pml_hs, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst.pml + ho * dst.pml_hs + 1, lsum, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
         } else {
             dst.po[ho * dst.po_hs + d] = o;
             if (d == 0) {
@@ -648,155 +622,6 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         }
     }
     __syncthreads();   // LDS may be reused by the caller's next piece
-}
-
-// In-launch merge of one (sequence, head block).  Every chunk workgroup
-// leaves its partial states with agent-scope stores (written through to the
-// device's point of coherence, so no cache write-back is needed), waits for
-// them to complete, and one thread counts the workgroup's arrival with an
-// agent-scope atomic.  The workgroup that arrives last resets the counter to
-// zero for the next call, copies every partial of its head block into LDS
-// with agent-scope loads that write LDS directly (one round, no registers),
-// and merges them exactly as the merge launch does (attn_combine_kernel<NT>
-// with G = NT / D chunk groups: "virtual thread" (r, d) chains chunks r,
-// r + G, ... of element d, then the groups are summed in order; or, for
-// attn_combine_wave_kernel, one chain per element), so the output is bitwise
-// that of the two-launch form.  No workgroup waits on another.  The counters
-// must be zero before the first call; every call leaves them so.
-// LDS: `sm` (>= kMergeSmall floats) takes the groups' o sums; the dynamic LDS
-// the launch adds holds the partials, merge_lds_bytes() of it.
-constexpr uint32_t kMergeSmall = 2048;     // floats of group sums (hpb * G * D)
-constexpr uint32_t kSplitStaticLds = 9u << 10;   // a split workgroup's own LDS, at most (16-byte rows)
-constexpr uint32_t kMergeMaxLSums = 64;    // hpb * G: the groups' l sums
-constexpr uint32_t kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0): vector memory ops complete
-constexpr int kBufCohLoad = 16;            // buffer cache policy sc1: agent-scope (coherent) load
-constexpr int kBufRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data
-
-// Bytes of one head's partials in LDS: o [nc][D] padded to 1 KiB (a wave
-// copies 1 KiB per instruction), then (m, l) [nc] padded to 256 bytes.
-__host__ __device__ constexpr uint32_t merge_o_bytes(uint32_t nc, uint32_t D) {
-    return (nc * D * 4 + 1023) / 1024 * 1024;
-}
-__host__ __device__ constexpr uint32_t merge_ml_bytes(uint32_t nc) { return (nc * 8 + 255) / 256 * 256; }
-__host__ __device__ constexpr uint32_t merge_lds_bytes(uint32_t hpb, uint32_t nc, uint32_t D) {
-    return hpb * (merge_o_bytes(nc, D) + merge_ml_bytes(nc));
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Copy `bytes` (a multiple of 4) from global `src` to LDS `dst` with
-// agent-scope loads; `span` (a multiple of 64 * width) bytes of LDS are
-// written, the part past `bytes` with zeros.  Each wave takes every fourth
-// slice of 64 lanes x width bytes.
-template <int WIDTH>
-__device__ __forceinline__ void merge_copy(const float *src, uint32_t bytes, char *dst, uint32_t span) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, (int)bytes, kBufRsrcWord3);
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    constexpr uint32_t kSlice = 64 * WIDTH;
-    static_assert(WIDTH == 16 || WIDTH == 4, "LDS copies of 4 or 16 bytes per lane");
-    for (uint32_t off = wave * kSlice; off < span; off += kWaves * kSlice) {
-        if constexpr (WIDTH == 16)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + off), 16, off + lane * 16, 0, 0,
-                                                     kBufCohLoad);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + off), 4, off + lane * 4, 0, 0,
-                                                     kBufCohLoad);
-    }
-}
-
-// The merge of one head block's partials, once they are all in LDS (see
-// merge_if_last): head_dim D and G chunk groups are compile-time constants;
-// WAVE: the one-chain form of attn_combine_wave_kernel.
-template <int D, int G, bool WAVE>
-__device__ __forceinline__ void merge_heads(const SplitArgs &a, uint32_t nc, size_t bh0, float *sm,
-                                            float *sm_ls) {
-    extern __shared__ __align__(16) char sm_dyn[];
-    constexpr uint32_t GD = G * D;
-    const uint32_t tid = threadIdx.x, lane = tid & 63, hpb = a.hpb;
-    const uint32_t ob = merge_o_bytes(nc, D), mb = merge_ml_bytes(nc);
-    char *o_lds = sm_dyn, *ml_lds = sm_dyn + hpb * ob;
-
-    // 1. every partial of the head block into LDS, in one round
-    for (uint32_t ho = 0; ho < hpb; ++ho) {
-        merge_copy<16>(a.part_o + (bh0 + ho) * a.nc_stride * D, nc * D * 4, o_lds + ho * ob, ob);
-        merge_copy<4>(a.part_ml + (bh0 + ho) * a.nc_stride * 2, nc * 8, ml_lds + ho * mb, mb);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-
-    // 2. per head (one wave each): M = max m_c, then m_c -> 2^(m_c - M) in place
-    for (uint32_t ho = tid >> 6; ho < hpb; ho += kWaves) {
-        float *ml = reinterpret_cast<float *>(ml_lds + ho * mb);
-        float M = -INFINITY;
-        for (uint32_t c = lane; c < nc; c += 64) M = fmaxf(M, ml[2 * c]);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-        for (uint32_t c = lane; c < nc; c += 64) ml[2 * c] = __builtin_amdgcn_exp2f(ml[2 * c] - M);
-    }
-    __syncthreads();
-
-    // 3. the group chains: virtual thread (ho, r, d) chains chunks r, r + G, ...
-    for (uint32_t vt = tid; vt < hpb * GD; vt += kThreads) {
-        const uint32_t ho = vt / GD, r = vt % GD / D, d = vt % D;
-        const float *o = reinterpret_cast<const float *>(o_lds + ho * ob) + d;
-        const float *ml = reinterpret_cast<const float *>(ml_lds + ho * mb);
-        float os = 0.f, ls = 0.f;
-#pragma unroll 4
-        for (uint32_t c = r; c < nc; c += G) {
-            const float w = ml[2 * c];
-            os = fmaf(o[c * D], w, os);
-            ls = fmaf(ml[2 * c + 1], w, ls);
-        }
-        sm[vt] = os;
-        if (d == 0) sm_ls[ho * G + r] = ls;
-    }
-    __syncthreads();
-
-    // 4. groups summed in order, rounded to fp16
-    for (uint32_t idx = tid; idx < hpb * D; idx += kThreads) {
-        const uint32_t ho = idx / D, d = idx % D;
-        float os, ls;
-        if constexpr (WAVE) {
-            os = sm[ho * GD + d];
-            ls = sm_ls[ho];
-        } else {
-            os = 0.f;
-            ls = 0.f;
-#pragma unroll
-            for (int r = 0; r < G; ++r) {
-                os += sm[ho * GD + r * D + d];
-                ls += sm_ls[ho * G + r];
-            }
-        }
-        a.out[(bh0 + ho) * D + d] = f2h_rne(os / ls);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void merge_if_last(const SplitArgs &a, uint32_t b, uint32_t hb,
-                                              uint32_t nc, size_t bh0, float *sm) {
-    __shared__ uint32_t sm_last;
-    __shared__ float sm_ls[kMergeMaxLSums];
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's partial stores are done
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t *cnt = a.merge_cnt + (size_t)b * a.n_hb + hb;
-        const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t last = prev == nc - 1 ? 1u : 0u;
-        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = last;
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    switch (a.merge_groups) {   // 0: the one-wave-per-pair form
-    case 0: merge_heads<D, 1, true>(a, nc, bh0, sm, sm_ls); break;
-    case 1: merge_heads<D, 1, false>(a, nc, bh0, sm, sm_ls); break;
-    case 2: merge_heads<D, 2, false>(a, nc, bh0, sm, sm_ls); break;
-    case 4: merge_heads<D, 4, false>(a, nc, bh0, sm, sm_ls); break;
-    case 8: merge_heads<D, 8, false>(a, nc, bh0, sm, sm_ls); break;
-    default: merge_heads<D, 16, false>(a, nc, bh0, sm, sm_ls); break;   // G = 16 (the planner allows no more)
-    }
 }
 
 // VEC: fp16 values per lane load; GL: lanes per row (power of two);
@@ -835,39 +660,14 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
         write_header(a, 0);
     }
     const uint32_t b = blockIdx.y;
-    if (a.grid_flags & kGridRankPrio) {   // later dispatch rounds issue first
-        const uint32_t round = (blockIdx.y * gridDim.x + blockIdx.x) / a.n_cu;
-        if (round == 1) __builtin_amdgcn_s_setprio(1);
-        else if (round == 2) __builtin_amdgcn_s_setprio(2);
-        else if (round >= 3) __builtin_amdgcn_s_setprio(3);
-    }
-    const uint32_t chunk_id = blockIdx.x / a.n_hb;
-    const uint32_t chunk = (a.grid_flags & kGridReverse) ? gridDim.x / a.n_hb - 1 - chunk_id : chunk_id;
-    const uint32_t hb = (a.grid_flags & kGridRotate) ? (blockIdx.x + chunk) % a.n_hb : blockIdx.x % a.n_hb;
+    const uint32_t hb = blockIdx.x % a.n_hb;
+    const uint32_t chunk = blockIdx.x / a.n_hb;
     const uint32_t cp = a.cp_dev ? a.cp_dev[b] : a.cp_host;
     // a decode step streams the positions before the new token's slot
     const uint32_t L = valid_len(cp, a.S) - (ROPE ? 1u : 0u);
-    uint32_t c0 = chunk * a.chunk;
+    const uint32_t c0 = chunk * a.chunk;
     if (c0 >= L) return;                     // whole workgroup: nothing to read
-    uint32_t c_end = min(c0 + a.chunk, L);
-    if (MODE != kModeQk && (a.grid_flags & kGridEven)) {
-        // n chunks of q or q + 1 positions, the longer ones first
-        const uint32_t n = (L + a.chunk - 1) / a.chunk;
-        const uint32_t q = L / n, rem = L - q * n;
-        c0 = chunk * q + min(chunk, rem);
-        c_end = c0 + q + (chunk < rem ? 1u : 0u);
-    } else if (MODE != kModeQk && (a.grid_flags & kGridRankWeight)) {
-        // chunk c' is streamed by the workgroup dispatched in round
-        // floor((j0 + c') / qr) (n_cu divisible by n_hb); later rounds get
-        // less: weight 1 - rank_step * round
-        const uint32_t n = (L + a.chunk - 1) / a.chunk;
-        const uint64_t qr = a.n_cu / a.n_hb, j0 = (uint64_t)b * (gridDim.x / a.n_hb);
-        const double f0 = (double)floor_prefix(j0, qr);
-        auto W = [&](uint32_t c) { return (double)c - a.rank_step * ((double)floor_prefix(j0 + c, qr) - f0); };
-        const double tot = W(n);
-        c0 = (uint32_t)((double)L * W(chunk) / tot);
-        c_end = chunk + 1 == n ? L : (uint32_t)((double)L * W(chunk + 1) / tot);
-    }
+    const uint32_t c_end = min(c0 + a.chunk, L);
     const size_t bh0 = (size_t)b * a.H + (size_t)hb * a.hpb;
     PieceDst dst;
     dst.po = a.part_o + (bh0 * a.nc_stride + chunk) * a.D;
@@ -878,8 +678,6 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     __shared__ __align__(16) uint16_t sm_sc[MODE == kModeQk ? kScoreWindow : 8];
     split_piece<VEC, GL, NV, FULL, U, PF, DUMP, PAGED, MODE>(a, b, hb, c0, c_end, dst, sm_o, sm_m,
                                                                  sm_l, sm_sc);
-    if constexpr (MODE == kModeDecodeMerge)
-        merge_if_last<VEC * GL * NV>(a, b, hb, (L + a.chunk - 1) / a.chunk, bh0, sm_o);
 }
 
 // Inclusive prefix of the streamed lengths (valid length minus `excl`):
@@ -1349,16 +1147,13 @@ struct Knobs {
     uint32_t unroll;   // positions per row group per block (2, 4, 8)
     uint32_t pf;       // double-buffered blocks
     uint32_t bal;      // per-sequence lengths: balanced grid (equal work per workgroup)
-    uint32_t merge = 0;   // chunked grid: merge the partials in the split launch
-    uint32_t gridf = 0;   // chunked grid: kGridRotate | kGridEven | ...
-    uint32_t rankpm = 0;  // kGridRankWeight: total weight spread over the rounds, per mille
 };
 constexpr uint32_t kChunkGranule = 16;
 constexpr uint32_t kMaxHeadsPerWG = kWaves * 64 / 8;   // row groups at 8 lanes per row
 
 const Knobs &env_knobs() {
     static const Knobs t = [] {
-        Knobs r{0, 0, 0, 0, 2, 2, 2, 99, 999};
+        Knobs r{0, 0, 0, 0, 2, 2};
         const char *env = getenv("ATTN_DECODE_TUNE");
         if (env) {
             char buf[256];
@@ -1373,9 +1168,6 @@ const Knobs &env_knobs() {
                     r.unroll = v;
                 else if (sscanf(tok, "pf=%u", &v) == 1) r.pf = v ? 1 : 0;
                 else if (sscanf(tok, "bal=%u", &v) == 1) r.bal = v ? 1 : 0;
-                else if (sscanf(tok, "merge=%u", &v) == 1) r.merge = v ? 1 : 0;
-                else if (sscanf(tok, "gridf=%u", &v) == 1) r.gridf = v & 31u;
-                else if (sscanf(tok, "rankpm=%u", &v) == 1) r.rankpm = v;
             }
         }
         return r;
@@ -1469,9 +1261,6 @@ Knobs knobs(uint32_t D, Kind kind) {
     if (e.unroll) k.unroll = e.unroll;
     if (e.pf != 2) k.pf = e.pf;
     if (e.bal != 2) k.bal = e.bal;
-    if (e.merge != 2) k.merge = e.merge;
-    if (e.gridf != 99) k.gridf = e.gridf;
-    if (e.rankpm != 999) k.rankpm = e.rankpm;
     return k;
 }
 
@@ -1571,8 +1360,7 @@ Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span
 // (per-sequence lengths, batch <= kBalancedMaxBatch).
 struct WsLayout {
     size_t o_off, ml_off, total;
-    size_t slots;     // partial states the workspace holds
-    size_t cnt_off;   // in-launch merge counters, uint32 [batch, n_heads]
+    size_t slots;   // partial states the workspace holds
 };
 
 size_t balanced_slots(uint32_t batch, uint32_t H, uint32_t D) {
@@ -1596,9 +1384,7 @@ WsLayout workspace_layout(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
     const size_t hdr = kHeaderBytes;
     const size_t o_bytes = (slots * D * sizeof(float) + 255) / 256 * 256;
     const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
-    const size_t cnt_bytes = ((size_t)batch * H * sizeof(uint32_t) + 255) / 256 * 256;
-    const size_t cnt_off = hdr + o_bytes + ml_bytes;
-    return WsLayout{hdr, hdr + o_bytes, cnt_off + cnt_bytes, slots, cnt_off};
+    return WsLayout{hdr, hdr + o_bytes, hdr + o_bytes + ml_bytes, slots};
 }
 
 attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
@@ -1627,7 +1413,7 @@ using SplitFn = void (*)(SplitArgs);
 
 template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED, int MODE>
 SplitFn kernel_for(bool bal) {
-    if constexpr (MODE == kModeQk || MODE == kModePv || MODE == kModeDecodeMerge)   // chunked grid only
+    if constexpr (MODE == kModeQk || MODE == kModePv)   // single sequence: chunked grid
         return attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>;
     else
         return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>
@@ -1680,16 +1466,6 @@ SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     ATTN_CASE(1, 64, 3, false)
     ATTN_CASE(1, 64, 4, false)
 #undef ATTN_CASE
-    return nullptr;
-}
-
-// The chunked grid with the in-launch merge: the 16-byte layouts of head_dim
-// 64 and 128, no score dump, dense caches.
-SplitFn pick_merge(const Layout &ly, const Knobs &k) {
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 8)
-        return pick_unroll<8, 8, 1, true, false, false, kModeDecodeMerge>(k, false);
-    if (ly.vec == 8 && ly.nv == 1 && ly.full && ly.gl == 16)
-        return pick_unroll<8, 16, 1, true, false, false, kModeDecodeMerge>(k, false);
     return nullptr;
 }
 
@@ -1801,7 +1577,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     if (grid_x * kThreads > kMaxGridItems)
         return fail(ATTN_ERR_DIM, "%llu workgroups per sequence exceed the dispatch limit of %llu",
                     (unsigned long long)grid_x, (unsigned long long)(kMaxGridItems / kThreads));
-    SplitFn fn =
+    const SplitFn fn =
         scores_in ? pick_split<false, false, kModePv>(ly, kn, false)
         : rope    ? (pg ? pick_split<false, true, kModeStep>(ly, kn, bal)
                         : pick_split<false, false, kModeStep>(ly, kn, bal))
@@ -1842,40 +1618,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.num_blocks = pg ? pg->num_blocks : 0;
     a.page_shift = pg ? pg->page_shift : 0;
     a.rope = rope ? *rope : RopeArgs{};
-    a.grid_flags = bal ? 0u : kn.gridf;
-    a.n_cu = 256;
-    {
-        const uint64_t rounds = cdiv(grid_x * batch, a.n_cu);
-        a.rank_step = rounds > 1 ? kn.rankpm * 1e-3f / (float)(rounds - 1) : 0.f;
-        if ((a.grid_flags & kGridRankWeight) && (a.n_cu % (H / hpb) != 0 || rounds <= 1))
-            a.grid_flags &= ~kGridRankWeight;
-    }
-    a.merge_cnt = nullptr;
-    a.merge_groups = 0;
-    // In-launch merge: the chunked grid's last workgroup per (sequence, head
-    // block) merges its partials.  It follows the merge launch's summation
-    // order, which is expressible here while a head's chunks fit that
-    // launch's one round of loads (or it takes one wave per pair: a single
-    // chain); the partials must fit LDS next to the workgroups a CU holds.
-    const uint64_t pairs = (uint64_t)batch * H;
-    const uint32_t comb_nt = pairs < kCombineWide ? 1024u : pairs < kCombineWave ? 256u : 0u;
-    const uint32_t groups = comb_nt ? comb_nt / D : 1u;
-    uint32_t merge_lds = 0;
-    const SplitFn merge_fn = pick_merge(ly, kn);
-    if (kn.merge && merge_fn && !bal && !rope && !scores_in && !dump && !pg && out && !a.direct &&
-        plan.n_chunks > 1 && plan.n_chunks <= (uint64_t)kCombineRegs * groups &&
-        (comb_nt == 0 || plan.n_chunks <= comb_nt) && (groups & (groups - 1)) == 0 && groups <= 16 &&
-        (uint64_t)hpb * groups * D <= kMergeSmall && hpb * groups <= kMergeMaxLSums) {
-        const uint64_t lds = merge_lds_bytes(hpb, plan.n_chunks, D);
-        const uint64_t per_cu = cdiv(grid_x * batch, 256);   // workgroups a CU holds at once
-        if (lds <= (48u << 10) && (lds + kSplitStaticLds) * per_cu <= (160u << 10)) {
-            a.merge_cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + wl.cnt_off);
-            a.merge_groups = comb_nt ? groups : 0u;
-            merge_lds = (uint32_t)lds;
-            fn = merge_fn;
-        }
-    }
-    *wrote_out = a.direct != 0 || a.merge_cnt != nullptr;
+    *wrote_out = a.direct != 0;
 
     if (dump) {
         const uint64_t total = (uint64_t)batch * H * S;
@@ -1886,7 +1629,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
         if (s != ATTN_OK) return s;
     }
     const dim3 grid = bal ? dim3(a.grid) : dim3(a.n_hb * plan.n_chunks, batch);
-    hipLaunchKernelGGL(fn, grid, dim3(kThreads), merge_lds, stream, a);
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, a);
     return hip_check("split kernel launch");
 }
 
