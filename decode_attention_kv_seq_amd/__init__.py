@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_f16.restype = ctypes.c_int
     lib.attn_decode_f16_batched.argtypes = [vp, vp, vp, vp, vp, u32, u32, u32, u32, vp, vp, sz, vp]
     lib.attn_decode_f16_batched.restype = ctypes.c_int
+    lib.attn_decode_f16_batched_noalloc.argtypes = [vp, vp, vp, vp, vp, u32, u32, u32, u32, vp, vp]
+    lib.attn_decode_f16_batched_noalloc.restype = ctypes.c_int
     lib.attn_decode_f16_split.argtypes = [vp, vp, vp, vp, u32, u32, u32, u32, u32, vp, vp, sz, vp]
     lib.attn_decode_f16_split.restype = ctypes.c_int
     lib.attn_decode_f16_combine.argtypes = [vp, vp, u32, u32, u32, u32, u32, vp, sz, vp]
@@ -249,6 +251,34 @@ def decode_batched(q, k, v, current_pos, *, out=None, dump: bool = False, worksp
                                            workspace.numel() * workspace.element_size(),
                                            _stream_handle(stream)))
     return (out, sc) if dump else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def decode_batched_noalloc(q, k, v, current_pos, *, out, dump=None, stream=None):
+    """decode_batched through attn_decode_f16_batched_noalloc: the library's
+    own per-GPU workspace, so nothing is allocated by the call (``out`` and
+    ``dump`` are the caller's).  Calls that overlap on one GPU race."""
+    lib = load_library()
+    _req(k, "k", torch.float16)
+    dev = k.device
+    _req(q, "q", torch.float16, dev)
+    _req(v, "v", torch.float16, dev)
+    if k.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [batch, capacity, n_heads, head_dim]")
+    B, S, H, D = k.shape
+    if tuple(q.shape) != (B, H, D):
+        raise ValueError("q must be [batch, n_heads, head_dim]")
+    cp = _cp_tensor(current_pos, B, dev)
+    _req(out, "out", torch.float16, dev)
+    if tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be [batch, n_heads, head_dim]")
+    _req_dump(dump, (B, H, S), dev)
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_decode_f16_batched_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cp), B, H,
+                                                   D, S, _ptr(dump), _stream_handle(stream)))
+    return out
 
 
 def _batch_view(q, k, v):

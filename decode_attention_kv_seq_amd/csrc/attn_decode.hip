@@ -40,6 +40,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "attn_internal.h"
 
 namespace {
@@ -1757,6 +1759,43 @@ attn_status_t check_paging(const uint32_t *block_table, const uint32_t *cp_dev, 
 
 }  // namespace
 
+// ------------------------------------------------- allocation-free calls
+// The workspace of attn_decode_f16_batched_noalloc: a fixed array on every
+// GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel (in host code it stands in for the
+// symbol, not for a device address): it looks up the device address once per
+// device with hipGetSymbolAddress and passes that.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];   // device address of `scratch`, per device
+
+// The current device's `scratch`, looked up on its first use there.
+attn_status_t scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(ATTN_ERR_HIP, "device %d is past the %d the library keeps scratch for", dev,
+                    kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ok();
+}
+
+}  // namespace
+
 // ============================================================== C ABI
 
 extern "C" {
@@ -1827,6 +1866,31 @@ attn_status_t attn_decode_f16_batched(const uint16_t *q, const uint16_t *k_cache
     if (!current_pos) return fail(ATTN_ERR_NULL, "current_pos must be non-NULL");
     return decode_full(q, k_cache, v_cache, out, current_pos, 0, batch, n_heads, head_dim,
                        capacity, scores_dump, workspace, workspace_bytes, nullptr, stream);
+}
+
+attn_status_t attn_decode_f16_batched_noalloc(const uint16_t *q, const uint16_t *k_cache,
+                                              const uint16_t *v_cache, uint16_t *out,
+                                              const uint32_t *current_pos, uint32_t batch,
+                                              uint32_t n_heads, uint32_t head_dim,
+                                              uint32_t capacity, float *scores_dump,
+                                              void *stream) {
+    // every argument check before the first HIP call, as elsewhere
+    if (!current_pos) return fail(ATTN_ERR_NULL, "current_pos must be non-NULL");
+    attn_status_t s = check_split(q, k_cache, v_cache, current_pos, batch, n_heads, head_dim,
+                                  capacity, scores_dump);
+    if (s != ATTN_OK) return s;
+    if (!out) return fail(ATTN_ERR_NULL, "out must be non-NULL");
+    if (!aligned(out, 2)) return fail(ATTN_ERR_ALIGN, "out must be 2-byte aligned");
+    const size_t need = workspace_layout(batch, n_heads, head_dim, capacity).total;
+    if (need > ATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of workspace; the allocation-free call holds %zu",
+                    need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    s = scratch_of_current_device(&ws);
+    if (s != ATTN_OK) return s;
+    return decode_full(q, k_cache, v_cache, out, current_pos, 0, batch, n_heads, head_dim,
+                       capacity, scores_dump, ws, ATTN_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }
 
 attn_status_t attn_decode_f16_split(const uint16_t *q, const uint16_t *k_cache,

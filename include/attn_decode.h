@@ -172,6 +172,32 @@ attn_status_t attn_decode_f16_batched(const uint16_t *q, const uint16_t *k_cache
                                       size_t workspace_bytes, void *stream);
 
 /*
+ * attn_decode_f16_batched with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * and harnesses that forbid allocation.  The workspace is instead a fixed
+ * array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on, from the first call there until the process ends; the call
+ * itself allocates nothing.  The caller still passes inputs and outputs.
+ *   Errors: as attn_decode_f16_batched; ATTN_ERR_WORKSPACE when
+ *   attn_decode_workspace_bytes(batch, n_heads, head_dim, capacity) exceeds
+ *   ATTN_NOALLOC_SCRATCH_BYTES (checked on the host, nothing enqueued);
+ *   ATTN_ERR_HIP when the array cannot be located on the current device.
+ *   Nothing in the array needs to start at zero.
+ * The array is per GPU and shared by every call on that GPU: calls that can
+ * run at the same time on one GPU (enqueued on different streams, or graphs
+ * replayed concurrently) race on it and give wrong results.  Keep such calls
+ * on one stream.  `stream` must belong to the current device.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+attn_status_t attn_decode_f16_batched_noalloc(const uint16_t *q, const uint16_t *k_cache,
+                                              const uint16_t *v_cache, uint16_t *out,
+                                              const uint32_t *current_pos, uint32_t batch,
+                                              uint32_t n_heads, uint32_t head_dim,
+                                              uint32_t capacity, float *scores_dump,
+                                              void *stream);
+
+/*
  * The same computation as the two calls above, split at its one internal
  * boundary, for callers that need to place work between the two launches
  * (timing the streaming kernel alone, or moving the partial states between

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -136,6 +136,29 @@ def test_paged_rejects_bad_arguments(lib):
     assert call(P=65536, MB=1 << 16) == DIM        # capacity 2^32
     assert call(wsb=16) == WS
     assert call(D=300) == DIM
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="stand-in device addresses: host-only")
+def test_noalloc_rejects_bad_arguments(lib):
+    """The allocation-free call: the usual checks, and sizes whose workspace
+    exceeds the library's per-GPU array (ATTN_NOALLOC_SCRATCH_BYTES) refused
+    with ATTN_ERR_WORKSPACE before any HIP call."""
+    f = lib.attn_decode_f16_batched_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 64, 128, None, None) == NULL
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 128, None, None) == NULL
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 2, 4, 64, 128, None, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE + 1, FAKE, 2, 4, 64, 128, None, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 2, 4, 64, 128, None, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 64, 128, None, None) == DIM
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 300, 128, None, None) == DIM
+    assert ad.workspace_bytes(1024, 64, 128, 131072) > ad.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1024, 64, 128, 131072, None, None) == WS
+    assert b"allocation-free" in lib.attn_last_error()
+    # the workloads here fit
+    for (B, H, D, S) in [(64, 32, 128, 8192), (1, 32, 128, 32768), (1, 64, 64, 131072),
+                         (1024, 32, 128, 8192)]:
+        assert 0 < ad.workspace_bytes(B, H, D, S) <= ad.NOALLOC_SCRATCH_BYTES
 
 
 def test_paged_generator_gathers_the_pool():
