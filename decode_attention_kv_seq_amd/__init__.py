@@ -16,6 +16,7 @@ q and the output ``[n_heads, head_dim]``.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -125,6 +126,22 @@ def _stream_handle(stream) -> Optional[int]:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with ``stream=`` (when given) as the current stream.
+    torch's caching allocator ties each block to the stream that is current
+    when it is allocated, and reuses a freed block on that stream without
+    waiting for other streams: so the workspace, ``out`` and dump that a
+    wrapper allocates for work it enqueues on ``stream`` must come from
+    ``stream``'s own blocks, not the current stream's."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return run
+
+
 def _req(t: torch.Tensor, name: str, dtype, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -187,6 +204,7 @@ def _cp_tensor(cp: torch.Tensor, batch: int, device) -> torch.Tensor:
     return cp
 
 
+@_on_stream
 def decode(q, k, v, current_pos: int, *, out=None, dump: bool = False, workspace=None,
            stream=None):
     """One sequence: q [H, D], k/v [S, H, D] fp16 -> out [H, D] fp16.
@@ -221,6 +239,7 @@ def decode(q, k, v, current_pos: int, *, out=None, dump: bool = False, workspace
     return (out, sc) if dump else out
 
 
+@_on_stream
 def decode_batched(q, k, v, current_pos, *, out=None, dump: bool = False, workspace=None,
                    stream=None):
     """Ragged batch: q [B, H, D], k/v [B, S, H, D] fp16, current_pos int32 [B]
@@ -256,6 +275,7 @@ def decode_batched(q, k, v, current_pos, *, out=None, dump: bool = False, worksp
 NOALLOC_SCRATCH_BYTES = 32 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 
 
+@_on_stream
 def decode_batched_noalloc(q, k, v, current_pos, *, out, dump=None, stream=None):
     """decode_batched through attn_decode_f16_batched_noalloc: the library's
     own per-GPU workspace, so nothing is allocated by the call (``out`` and
@@ -288,6 +308,7 @@ def _batch_view(q, k, v):
     return q, k, v
 
 
+@_on_stream
 def split(q, k, v, current_pos, workspace, *, dump=None, stream=None):
     """First launch of a decode: stream the cache into the workspace.
 
@@ -310,6 +331,7 @@ def split(q, k, v, current_pos, workspace, *, dump=None, stream=None):
                                          _stream_handle(stream)))
 
 
+@_on_stream
 def combine(out, current_pos, batch, n_heads, head_dim, seq_len, workspace, *, stream=None):
     """Second launch: merge the workspace partials into ``out``."""
     lib = load_library()
@@ -345,6 +367,7 @@ def _paged_args(q, k_pool, v_pool, block_table, current_pos):
     return B, H, D, P, block_table.shape[1], NB, cp
 
 
+@_on_stream
 def decode_paged(q, k_pool, v_pool, block_table, current_pos, *, out=None, dump=False,
                  workspace=None, stream=None):
     """Paged cache: q [B, H, D]; k/v pools [num_blocks, page_size, H, D];
@@ -370,6 +393,7 @@ def decode_paged(q, k_pool, v_pool, block_table, current_pos, *, out=None, dump=
     return (out, sc) if dump else out
 
 
+@_on_stream
 def split_paged(q, k_pool, v_pool, block_table, current_pos, workspace, *, dump=None, stream=None):
     """First launch of a paged decode; `combine(out, current_pos, B, H, D,
     max_blocks * page_size, workspace)` is the second."""
@@ -385,6 +409,7 @@ def split_paged(q, k_pool, v_pool, block_table, current_pos, workspace, *, dump=
                                                _stream_handle(stream)))
 
 
+@_on_stream
 def qk(q, k, current_pos: int, *, scores=None, stream=None):
     """First dispatch: q [H, D], k [S, H, D] -> fp16 scores [H, S]
     (scaled, -inf after current_pos)."""
@@ -408,6 +433,7 @@ def qk(q, k, current_pos: int, *, scores=None, stream=None):
     return scores
 
 
+@_on_stream
 def pv(scores, v, current_pos: int, *, out=None, workspace=None, stream=None):
     """Second dispatch: fp16 scores [H, S], v [S, H, D] -> out [H, D]."""
     lib = load_library()
@@ -441,6 +467,7 @@ def _rope_params(rope_dims, head_dim, base):
     return dims, float(base)
 
 
+@_on_stream
 def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, *, rope_dims=None,
                 rope_base: float = 10000.0, traditional: bool = False, out=None, workspace=None,
                 stream=None):
@@ -496,6 +523,7 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, current_pos, *, rope_dims=Non
     return out
 
 
+@_on_stream
 def decode_step_paged(q, k_new, v_new, k_pool, v_pool, block_table, current_pos, *,
                       rope_dims=None, rope_base: float = 10000.0, traditional: bool = False,
                       out=None, workspace=None, stream=None):
@@ -526,6 +554,7 @@ def decode_step_paged(q, k_new, v_new, k_pool, v_pool, block_table, current_pos,
     return out
 
 
+@_on_stream
 def rope(x, positions, *, rope_dims=None, rope_base: float = 10000.0, traditional: bool = False,
          out=None, stream=None):
     """Rotary embedding: x [B, H, D] fp16, positions int32/uint32 GPU tensor
@@ -553,6 +582,7 @@ def softmax_workspace_bytes(rows: int, cols: int) -> int:
     return int(load_library().attn_softmax_workspace_bytes(rows, cols))
 
 
+@_on_stream
 def softmax(x, *, out=None, workspace=None, stream=None):
     """Row softmax of an fp32 GPU tensor [rows, cols] (last dimension).
     ``out`` may be ``x`` itself."""

@@ -1,14 +1,24 @@
 """The C-ABI library on a host without a GPU: it loads, exports every
 function include/attn_decode.h declares, and rejects bad arguments on the
-host before any HIP call (no kernel is launched by these tests)."""
+host before any HIP call (no kernel is launched by these tests).
+
+The argument checks are called with a stand-in device address (FAKE) that
+is never dereferenced while a check refuses the call.  Should a check ever
+let such a call through, it would launch on an unmapped address, so those
+tests are host-only: they are skipped where a GPU is visible."""
 import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
+import torch
 
 import decode_attention_kv_seq_amd as ad
+
+host_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                               reason="stand-in device addresses: host-only")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_decode.h")
@@ -64,6 +74,7 @@ def call_single(lib, q=FAKE, k=FAKE, v=FAKE, out=FAKE, H=4, D=64, S=128, cp=100,
     return lib.attn_decode_f16(q, k, v, out, H, D, S, cp, dump, ws, ws_bytes, None)
 
 
+@host_only
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(out=None), NULL),
     (dict(H=0), DIM), (dict(D=0), DIM), (dict(S=0), DIM), (dict(D=257), DIM),
@@ -76,6 +87,7 @@ def test_single_rejects_bad_arguments(lib, kw, code):
     assert lib.attn_last_error().decode()
 
 
+@host_only
 def test_batched_rejects_bad_arguments(lib):
     f = lib.attn_decode_f16_batched
     assert f(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 64, 128, None, FAKE, 1 << 30, None) == NULL
@@ -87,6 +99,7 @@ def test_batched_rejects_bad_arguments(lib):
     assert b"smaller" in lib.attn_last_error()
 
 
+@host_only
 def test_split_and_combine_reject_bad_arguments(lib):
     assert lib.attn_decode_f16_split(None, FAKE, FAKE, None, 5, 1, 4, 64, 128, None, FAKE,
                                      1 << 30, None) == NULL
@@ -98,6 +111,7 @@ def test_split_and_combine_reject_bad_arguments(lib):
                                        None) == ALIGN
 
 
+@host_only
 def test_error_text_is_per_call(lib):
     call_single(lib, D=0)
     a = lib.attn_last_error().decode()
@@ -116,6 +130,7 @@ def test_binding_rejects_cpu_tensors():
         ad.decode(q, k.float(), k, 100)
 
 
+@host_only
 def test_paged_rejects_bad_arguments(lib):
     f = lib.attn_decode_f16_paged
     ok_args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, bt=FAKE, cp=FAKE, B=2, H=4, D=64, P=16,
@@ -138,8 +153,7 @@ def test_paged_rejects_bad_arguments(lib):
     assert call(D=300) == DIM
 
 
-@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
-                    reason="stand-in device addresses: host-only")
+@host_only
 def test_noalloc_rejects_bad_arguments(lib):
     """The allocation-free call: the usual checks, and sizes whose workspace
     exceeds the library's per-GPU array (ATTN_NOALLOC_SCRATCH_BYTES) refused
@@ -178,6 +192,7 @@ def test_paged_generator_gathers_the_pool():
             assert torch.equal(dk, k.view(L, 8)) and torch.equal(dv, v.view(L, 8))
 
 
+@host_only
 def test_two_dispatch_rejects_bad_arguments(lib):
     assert lib.attn_qk_f16(None, FAKE, FAKE, 4, 64, 128, 5, None) == NULL
     assert lib.attn_qk_f16(FAKE, FAKE, FAKE + 1, 4, 64, 128, 5, None) == ALIGN
@@ -187,6 +202,7 @@ def test_two_dispatch_rejects_bad_arguments(lib):
     assert lib.attn_pv_f16(FAKE, FAKE + 1, FAKE, 4, 64, 128, 5, FAKE, 1 << 30, None) == ALIGN
 
 
+@host_only
 def test_decode_step_rejects_bad_arguments(lib):
     f = lib.attn_decode_step_f16
     ok = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, out=FAKE, H=4, D=64, S=128, cp=100,
@@ -220,6 +236,7 @@ def test_decode_step_rejects_bad_arguments(lib):
              None) == DIM
 
 
+@host_only
 def test_rope_rejects_bad_arguments(lib):
     f = lib.attn_rope_f16
     assert f(None, FAKE, FAKE, 2, 4, 64, 64, 1e4, 0, None) == NULL
@@ -231,6 +248,7 @@ def test_rope_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, FAKE, 0, 4, 64, 64, 1e4, 0, None) == DIM
 
 
+@host_only
 def test_softmax_rejects_bad_arguments(lib):
     f = lib.attn_softmax_f32
     need = ad.softmax_workspace_bytes(8, 5000)
@@ -248,8 +266,7 @@ def test_softmax_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, 1 << 20, 1 << 31, FAKE, 1 << 40, None) == DIM
 
 
-@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
-                    reason="stand-in pointers pass every check but the dispatch limit: host-only")
+@host_only
 def test_dispatch_limits(lib):
     """Calls whose launch would exceed the GPU's dispatch limit (2^32 - 1
     work-items per grid dimension) are refused with ATTN_ERR_DIM before any
@@ -281,6 +298,7 @@ def test_dispatch_limits(lib):
         ad.plan(1, 65536, 1, 1 << 31, (1 << 31) - 1, 0)
 
 
+@host_only
 def test_paged_step_rejects_bad_arguments(lib):
     f = lib.attn_decode_step_f16_paged
 
@@ -302,6 +320,7 @@ def test_paged_step_rejects_bad_arguments(lib):
     assert call(wsb=16) == WS
 
 
+@host_only
 def test_header_and_library_from_c(tmp_path):
     """tests/c/abi_from_c.c, a strict C99 program (gcc -std=c99 -pedantic
     -Werror) that includes the header, links the library and checks its

@@ -442,6 +442,41 @@ def test_side_stream():
     assert torch.equal(out, ref)
 
 
+def test_stream_argument_not_current():
+    """stream= a side stream that is not the current one, while the current
+    stream still has work queued: the wrappers' own allocations (workspace,
+    out, dump) are recorded on the side stream, so the caching allocator
+    does not hand their memory to the current stream's next allocations
+    while the side stream's kernels still use it.  Every output equals the
+    plain call's bitwise."""
+    rng = np.random.default_rng(15)
+    S, H, D = 30000, 16, 128
+    q, k, v = to_dev(randn16(rng, (H, D))), to_dev(randn16(rng, (S, H, D))), to_dev(randn16(rng, (S, H, D)))
+    ref = ad.decode(q, k, v, S - 1)
+    ref_d = ad.decode(q, k, v, 20000, dump=True)
+    x = torch.randn(4096, 4096, device=DEV)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(6):
+        for _ in range(3):
+            x = x @ x * 1e-3          # keeps the current stream busy
+        outs.append(ad.decode(q, k, v, S - 1, stream=side))
+        outs.append(ad.decode(q, k, v, 20000, dump=True, stream=side))
+        # the current stream's allocations of the same sizes, written at once
+        junk = [torch.full((ad.workspace_bytes(1, H, D, S),), 255, dtype=torch.uint8, device=DEV)
+                for _ in range(2)]
+        junk += [torch.full((H, D), -7.0, dtype=torch.float16, device=DEV),
+                 torch.full((H, S), 3.0, dtype=torch.float32, device=DEV)]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for i in range(0, len(outs), 2):
+        assert torch.equal(outs[i], ref), i
+        assert torch.equal(outs[i + 1][0], ref_d[0]) and torch.equal(outs[i + 1][1], ref_d[1]), i
+
+
 def test_binding_rejects_host_and_misshaped_buffers():
     """The library takes raw device pointers, so the binding refuses, before
     any launch, caller buffers that are on the host, of the wrong dtype or
