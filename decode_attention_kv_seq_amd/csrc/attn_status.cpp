@@ -4,6 +4,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "attn_internal.h"
 
@@ -33,7 +34,13 @@ attn_status_t hip_check(const char *what) {
 extern "C" {
 
 const char *attn_status_string(attn_status_t status) {
-    switch (status) {
+    // A C caller may pass any int.  In C++ an enum value outside its
+    // enumerators' range may not be read as the enum, so read its bytes as
+    // an int instead.
+    int code;
+    static_assert(sizeof code == sizeof status, "attn_status_t is int-sized");
+    memcpy(&code, &status, sizeof code);
+    switch (code) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_DIM: return "invalid size";
