@@ -17,6 +17,12 @@ Prints ONE JSON line on stdout:
                  rocprofv3 FETCH_SIZE/WRITE_SIZE bytes per launch when a
                  counter summary for the current kernel source is committed
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
+  config.gates   (default run) the same whole-step and split-kernel figures
+                 for the 32768-position cache and the ragged 64-sequence
+                 batch, timed in the same process, each against 80% of the
+                 HBM peak
+Inputs are normal draws (torch.randn, seeded) of each workload's shape and
+structure, made on the GPU.
 Everything else goes to stderr.
 """
 from __future__ import annotations
@@ -36,6 +42,8 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attention HBM GB/s (K+V bytes/s) and % of MI355X HBM peak; µs/step"
 HBM_PEAK_GBS = 8000.0
+CPU_SHARE = 16            # host CPUs a GPU machine gives each GPU
+GATE_FRAC = 0.80          # the target: K+V bytes at >= 80% of the HBM peak
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_seq_amd", "csrc", "attn_decode.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -60,6 +68,9 @@ def parse():
     p.add_argument("--rotate", type=int, default=0,
                    help="K/V copies to cycle through (0: enough for >= 2 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-gates", action="store_true",
+                   help="skip timing the gated workloads (seq-32768 cache, ragged batch) after "
+                        "the default one")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
@@ -82,15 +93,35 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(w, seconds: float, path: str = "fused"):
+def host_cpus():
+    """Host CPUs the process may use, and how many the machine has."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return usable, os.cpu_count() or usable
+
+
+def baseline_threads():
+    """Threads for the CPU oracle: the host CPUs this process may use, at
+    most CPU_SHARE.  A GPU machine gives each GPU a share of 16 of its host
+    CPUs (worker pools are to be sized to it, whatever os.cpu_count()
+    reports), so the baseline stays within that share."""
+    usable, _ = host_cpus()
+    return max(1, min(usable, CPU_SHARE))
+
+
+def cpu_baseline(w, seconds: float, path: str = "fused", inputs=None):
     """Time the oracle (as it is) on whole (sequence, head) units of the
-    workload: its decode, or for the decode step its rotate-append-attend."""
+    workload: its decode, or for the decode step its rotate-append-attend.
+    ``inputs`` = (q, k, v) device tensors of the run (dense caches): the
+    units are host copies of them; paged workloads regenerate their units."""
     import numpy as np
     from decode_attention_kv_seq_amd import workloads as wl
     import oracle
 
     orc = oracle.load()
-    cores = min(os.cpu_count() or 1, 16)
+    cores = baseline_threads()
     pos = w.positions()
     rng = np.random.default_rng(0)
     units = [(int(b), int(h)) for b in range(w.batch) for h in range(w.n_heads)]
@@ -100,7 +131,15 @@ def cpu_baseline(w, seconds: float, path: str = "fused"):
     bt = w.block_table() if w.paged else None
 
     def one(b, h):
-        q, k, v = wl.head_slice_paged(w, b, h, bt) if w.paged else wl.head_slice(w, b, h)
+        if w.paged:
+            q, k, v = wl.head_slice_paged(w, b, h, bt)
+        elif inputs is not None:
+            L = w.valid_len(b)
+            q = inputs[0][b, h].reshape(1, 1, -1).cpu()
+            k = inputs[1][b, :L, h].reshape(L, 1, -1).cpu()
+            v = inputs[2][b, :L, h].reshape(L, 1, -1).cpu()
+        else:
+            q, k, v = wl.head_slice(w, b, h)
         return q[0], k, v, int(pos[b]), k.shape[0] * w.head_dim * 2 * 2
 
     step_rng = np.random.default_rng(1)
@@ -149,16 +188,21 @@ def cpu_baseline(w, seconds: float, path: str = "fused"):
         reps1 += 1
         dt1 = time.perf_counter() - t0
     bytes1 = sum(s1[4] for s1 in sample[:n1]) * reps1
+    usable, total = host_cpus()
     return {
         "value": round(total_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
+        "host_cpus": total,
+        "host_cpus_usable": usable,
+        "cpu_model": cpu_model(),
         "value_1thread": round(bytes1 / dt1 / 1e9, 4),
-        "sample": "%d of %d (sequence, head) units%s, %.1f MB of K+V, %.2f s on %d threads of "
-                  "%s (fp64 scalar C oracle%s); one thread: %d unit%s%s, %.1f MB in %.2f s" % (
+        "sample": "%d of %d (sequence, head) units%s, %.1f MB of K+V, %.2f s on %d threads "
+                  "(host: %d CPUs, %d usable by this process; %s) (fp64 scalar C oracle%s); "
+                  "one thread: %d unit%s%s, %.1f MB in %.2f s" % (
                       n_units, len(units), "" if reps == 1 else " x %d passes" % reps,
-                      total_bytes / 1e6, dt, cores, cpu_model(),
+                      total_bytes / 1e6, dt, cores, total, usable, cpu_model(),
                       ": rotate, append, attend" if path == "step" else "",
                       n1, "" if n1 == 1 else "s", "" if reps1 == 1 else " x %d passes" % reps1,
                       bytes1 / 1e6, dt1),
@@ -256,7 +300,7 @@ def run_softmax(args, name):
     cpu = None
     if not args.no_cpu_baseline:
         orc = oracle.load()
-        cores = min(os.cpu_count() or 1, 16)
+        cores = baseline_threads()
         xh = x0.cpu().numpy()
         t0 = time.perf_counter()
         orc.softmax_rows(xh[: max(1, w.rows // 8)])
@@ -266,8 +310,10 @@ def run_softmax(args, name):
         for _ in range(reps):
             orc.softmax_rows(xh, threads=cores)
         dt = time.perf_counter() - t0
+        usable, total = host_cpus()
         cpu = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-               "kind": "oracle",
+               "kind": "oracle", "host_cpus": total, "host_cpus_usable": usable,
+               "cpu_model": cpu_model(),
                "sample": "the whole [%d, %d] input, %d time%s, %.2f s on %d threads of %s "
                          "(fp64 C oracle)" % (w.rows, w.cols, reps, "" if reps == 1 else "s", dt,
                                               cores, cpu_model())}
@@ -298,31 +344,25 @@ def run_softmax(args, name):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-
+def measure_decode(w, args, dev, lib, path="fused", steps=None, warmup=None):
+    """Time whole steps of one decode workload (rotated K/V copies, HIP
+    events on the stream the kernels run on), the same steps with one copy
+    repeated, and the split kernel alone inside otherwise unchanged steps.
+    Returns the figures and the inputs (for the CPU baseline)."""
     import torch
     import decode_attention_kv_seq_amd as ad
     from decode_attention_kv_seq_amd import workloads as wl
 
-    name = args.workload or wl.BENCH_WORKLOAD
-    if name in wl.SOFTMAX_WORKLOADS:
-        return run_softmax(args, name)
-    w = wl.WORKLOADS[name]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    lib = ad.load_library()
-    props = torch.cuda.get_device_properties(dev)
-    log("device: %s, %d CUs, %.0f GiB" % (props.name, props.multi_processor_count,
-                                          props.total_memory / 2 ** 30))
-
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     t0 = time.perf_counter()
-    q = wl.make_q(w, dev)
-    k0, v0 = wl.make_kv_paged(w, dev) if w.paged else wl.make_kv(w, dev)
+    if w.paged:
+        q = wl.make_q(w, dev)
+        k0, v0 = wl.make_kv_paged(w, dev)
+        source = "counter-based generator (Irwin-Hall(4), +-3.46 sigma)"
+    else:
+        q, k0, v0 = wl.make_normal(w, dev)
+        source = "torch.randn (normal)"
     kv_alloc = 2 * k0.numel() * 2
     copies = args.rotate or max(1, math.ceil((2 << 30) / kv_alloc))
     ks, vs = [k0], [v0]
@@ -330,8 +370,9 @@ def main():
         ks.append(k0.clone())
         vs.append(v0.clone())
     torch.cuda.synchronize()
-    log("inputs: %s, %d cop%s of %.1f MiB K+V, generated in %.1f s"
-        % (name, copies, "y" if copies == 1 else "ies", kv_alloc / 2 ** 20, time.perf_counter() - t0))
+    log("inputs: %s, %d cop%s of %.1f MiB K+V (%s), generated in %.1f s"
+        % (w.name, copies, "y" if copies == 1 else "ies", kv_alloc / 2 ** 20, source,
+           time.perf_counter() - t0))
 
     B, S, H, D = w.kv_shape   # S: capacity per sequence (max_blocks * page_size when paged)
     if w.paged:
@@ -376,7 +417,7 @@ def main():
                     cp_host, B, H, D, S, vp(ws.data_ptr()), ws_bytes, sh)
     full = (lib.attn_decode_f16_paged if w.paged else
             lib.attn_decode_f16_batched if w.batched else lib.attn_decode_f16)
-    if args.path == "two_dispatch":
+    if path == "two_dispatch":
         if w.batched:
             raise SystemExit("--path two_dispatch needs a single-sequence workload")
         scores = torch.empty((H, S), dtype=torch.float16, device=dev)
@@ -389,7 +430,7 @@ def main():
             rc = lib.attn_qk_f16(*qk_args[r])
             return rc if rc else lib.attn_pv_f16(*pv_args[r])
         step_fns = [lambda r=r: two_dispatch(r) for r in range(copies)]
-    elif args.path == "step":
+    elif path == "step":
         gen = torch.Generator(device=dev)
         gen.manual_seed(w.seed + 1000)
         k_new = torch.randn(w.q_shape, generator=gen, device=dev).half()
@@ -432,20 +473,20 @@ def main():
         del a, b
 
     # ---- whole steps
-    for i in range(args.warmup):
+    for i in range(warmup):
         check(step_fns[i % copies]())
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         check(step_fns[i % copies]())
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    ms_hot = hot_ms(step_fns[0], check, args.steps, stream, torch) if copies > 1 else ms
+    ms = e0.elapsed_time(e1) / steps
+    ms_hot = hot_ms(step_fns[0], check, steps, stream, torch) if copies > 1 else ms
 
     # ---- the split kernel alone, inside otherwise unchanged steps
-    n_split = max(20, min(args.steps, 500)) if args.path == "fused" else 0
+    n_split = max(20, min(steps, 500)) if path == "fused" else 0
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_split)]
     for i in range(n_split):
@@ -459,9 +500,64 @@ def main():
 
     value = nbytes / (ms * 1e-3) / 1e9
     achieved = nbytes / (split_avg * 1e-3) / 1e9
-    log("step %.2f us -> %.1f GB/s (%.1f%% of 8 TB/s); split kernel %.2f us (median %.2f) -> %.1f GB/s"
-        % (ms * 1e3, value, 100 * value / HBM_PEAK_GBS, split_avg * 1e3,
+    log("%s: step %.2f us -> %.1f GB/s (%.1f%% of 8 TB/s); split kernel %.2f us (median %.2f) -> %.1f GB/s"
+        % (w.name, ms * 1e3, value, 100 * value / HBM_PEAK_GBS, split_avg * 1e3,
            split_ms[len(split_ms) // 2] * 1e3, achieved))
+    return {
+        "ms": ms, "ms_hot": ms_hot, "split_avg": split_avg, "value": value, "achieved": achieved,
+        "nbytes": nbytes, "copies": copies, "shape": (B, S, H, D), "source": source,
+        "inputs": None if w.paged else (q, k0, v0),
+    }
+
+
+def gate_entry(w, r):
+    """One gated workload's figures for config.gates."""
+    target_us = r["nbytes"] / (GATE_FRAC * HBM_PEAK_GBS * 1e9) * 1e6
+    return {
+        "us_per_step": round(r["ms"] * 1e3, 3),
+        "GB/s": round(r["value"], 2),
+        "frac": round(r["value"] / HBM_PEAK_GBS, 4),
+        "split_kernel_us": round(r["split_avg"] * 1e3, 3),
+        "split_kernel_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": r["nbytes"],
+        "us_at_80pct": round(target_us, 2),
+        "meets_80pct": bool(r["ms"] * 1e3 <= target_us),
+        "inputs": r["source"],
+    }
+
+
+# Workloads whose whole step is also timed in the default run: the other
+# cache at seq_len >= 32768 (where the 80% target applies) and the largest
+# K+V footprint.
+GATE_WORKLOADS = ("h32_d128_s32768_cp20000_garbage", "b64_h32_d128_cap8192_ragged")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_kv_seq_amd as ad
+    from decode_attention_kv_seq_amd import workloads as wl
+
+    name = args.workload or wl.BENCH_WORKLOAD
+    if name in wl.SOFTMAX_WORKLOADS:
+        return run_softmax(args, name)
+    w = wl.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = ad.load_library()
+    props = torch.cuda.get_device_properties(dev)
+    log("device: %s, %d CUs, %.0f GiB" % (props.name, props.multi_processor_count,
+                                          props.total_memory / 2 ** 30))
+
+    r = measure_decode(w, args, dev, lib, args.path)
+    B, S, H, D = r["shape"]
+    ms, ms_hot, split_avg, value, achieved = r["ms"], r["ms_hot"], r["split_avg"], r["value"], r["achieved"]
+    nbytes, copies = r["nbytes"], r["copies"]
 
     traffic = load_traffic(name)
     roofline = {
@@ -475,8 +571,24 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds, args.path)
+        cpu = cpu_baseline(w, args.cpu_seconds, args.path, r["inputs"])
         log("cpu baseline: %s" % json.dumps(cpu))
+    r["inputs"] = None
+    del r
+    torch.cuda.empty_cache()
+
+    gates = None
+    if not args.no_gates and args.path == "fused" and args.workload is None:
+        gates = {}
+        for gname in GATE_WORKLOADS:
+            gr = measure_decode(wl.WORKLOADS[gname], args, dev, lib, "fused")
+            gates[gname] = gate_entry(wl.WORKLOADS[gname], gr)
+            del gr
+            torch.cuda.empty_cache()
+        gates[name] = gate_entry(w, {"ms": ms, "value": value, "split_avg": split_avg,
+                                     "achieved": achieved, "nbytes": nbytes,
+                                     "source": "torch.randn (normal)"})
+        log("gates: %s" % json.dumps(gates))
 
     config = {
         "workload": name,
@@ -490,7 +602,11 @@ def main():
         "split_kernel_us": round(split_avg * 1e3, 3),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "path": args.path,
+        "inputs": "torch.randn (normal)" if not w.paged else
+                  "counter-based generator (Irwin-Hall(4), +-3.46 sigma)",
     }
+    if gates is not None:
+        config["gates"] = gates
     if args.path == "step":
         config["kv_bytes_counted"] = "rows 0..pos-1 of K and V read, row pos of K and V written"
     line = {

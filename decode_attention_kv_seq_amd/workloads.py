@@ -331,6 +331,41 @@ def head_slice(w: Workload, b: int, h: int, n_rows: Optional[int] = None):
     return q, out[0], out[1]
 
 
+def make_normal(w: Workload, device, chunk_rows: int = 2048):
+    """True normal inputs of the workload's shape and structure: q
+    [B, H, D] ~ N(0, sigma_q^2); k, v [B, S, H, D] ~ N(0, sigma_kv^2), rows
+    after current_pos ~ N(0, garbage_sigma^2) where the workload has
+    garbage, the K rows of ``spike_rows()`` times ``spike_scale``; all fp16
+    (nearest even).  Drawn with torch.randn from a generator seeded by the
+    workload, on ``device``, so the values depend on the device type: a
+    check against the oracle takes host copies of these tensors.  (The
+    counter-based generator above is bounded at +-3.46 sigma; these draws
+    have the normal tails.)"""
+    assert not w.paged
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_003 * w.seed + 17)
+    q = (torch.randn(w.q_shape, generator=g, device=device) * w.sigma_q).half()
+    B, S, H, D = w.kv_shape
+    k = torch.empty(w.kv_shape, dtype=torch.float16, device=device)
+    v = torch.empty(w.kv_shape, dtype=torch.float16, device=device)
+    lo_garbage = S
+    if w.garbage_sigma is not None and not w.batched:
+        lo_garbage = min(w.cur_pos, S - 1) + 1
+    for t in (k, v):
+        for b in range(B):
+            for r0 in range(0, S, chunk_rows):
+                r1 = min(S, r0 + chunk_rows)
+                x = torch.randn((r1 - r0, H, D), generator=g, device=device)
+                sig = torch.full((r1 - r0, 1, 1), w.sigma_kv, device=device)
+                if r1 > lo_garbage:
+                    sig[max(0, lo_garbage - r0):] = w.garbage_sigma
+                t[b, r0:r1] = (x * sig).half()
+    if w.spike_fraction > 0:
+        rows = w.spike_rows().to(device)
+        k[:, rows] = k[:, rows] * w.spike_scale
+    return q, k, v
+
+
 # The five decode-attention workloads, named by shape.
 WORKLOADS = {
     wl.name: wl for wl in [

@@ -9,7 +9,8 @@ Metal Kernels in Rust - A Deep Dive Through Attention", section "Testing").
 
 Oracle inputs are generated on the host by the seeded generator; the GPU
 inputs come from the same generator on the device (bit-identical, checked
-in test_device_generator_matches_host).
+in test_device_generator_matches_host).  The full-size cases also run on
+normal draws made on the GPU (torch.randn), the oracle taking host copies.
 """
 import numpy as np
 import pytest
@@ -106,48 +107,98 @@ def test_workload_full_parity(name):
     assert_dump_close(dump, ref_s, q_h.numpy(), k_h[0].numpy(), w.cur_pos, name)
 
 
-def test_workload_ragged_batch_sampled():
-    """64 sequences x 32 heads, capacity 8192: 16 sampled (sequence, head)
-    pairs against the oracle, every sequence's masked dump slots -inf."""
+def _inputs(w, source):
+    """The workload's q, k, v on the GPU: the counter-based generator
+    (bounded at +-3.46 sigma) or normal draws (torch.randn)."""
+    if source == "generator":
+        q = wl.make_q(w, DEV)
+        k, v = wl.make_kv(w, DEV)
+        return q, k, v
+    return wl.make_normal(w, DEV)
+
+
+@pytest.mark.parametrize("source", ["normal"])
+@pytest.mark.parametrize("name", ["h4_d64_s128_cp100", "h32_d128_s4096_full",
+                                  "h32_d128_s32768_cp20000_garbage"])
+def test_workload_full_parity_normal(name, source):
+    """The same, with normal inputs drawn on the GPU (the peaked softmax of
+    q with sigma 2 and the garbage with sigma 10 have their normal tails);
+    the oracle takes host copies of the device tensors."""
+    w = wl.WORKLOADS[name]
+    print("case", name, source, flush=True)
+    q, k, v = _inputs(w, source)
+    out = ad.decode(q[0], k[0], v[0], w.cur_pos)
+    out_d, dump = ad.decode(q[0], k[0], v[0], w.cur_pos, dump=True)
+    torch.cuda.synchronize()
+    qh, kh, vh = q[0].cpu(), k[0].cpu(), v[0].cpu()
+    ref, ref_s, _ = oracle.decode(qh, kh, vh, w.cur_pos, want_scores=True, threads=16)
+    assert_close(out, ref, name)
+    assert torch.equal(out, out_d), "dump variant differs from the timed kernel"
+    assert_dump_close(dump, ref_s, qh.numpy(), kh.numpy(), w.cur_pos, name)
+
+
+@pytest.mark.parametrize("source", ["generator", "normal"])
+def test_workload_ragged_batch_full(source):
+    """64 sequences x 32 heads, capacity 8192 (the full-size launch the bench
+    times): every output element of every (sequence, head) and every dumped
+    score against the oracle, on host copies of the device caches; every
+    sequence's masked dump slots exactly -inf."""
     w = wl.WORKLOADS["b64_h32_d128_cap8192_ragged"]
-    q = wl.make_q(w, DEV)
-    k, v = wl.make_kv(w, DEV)
+    print("case", w.name, source, flush=True)
+    q, k, v = _inputs(w, source)
     cp = w.positions().to(torch.int32).to(DEV)
     out = ad.decode_batched(q, k, v, cp)
     out_d, dump = ad.decode_batched(q, k, v, cp, dump=True)
     torch.cuda.synchronize()
     assert torch.equal(out, out_d)
     pos = w.positions()
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    del k, v
+    ref, ref_s = oracle.decode_batched(qh, kh, vh, pos, want_scores=True, threads=16)
+    assert_close(out, ref, "ragged batch")
+    dump_h = dump.cpu()
     for b in range(w.batch):
         L = w.valid_len(b)
-        assert bool(torch.all(dump[b, :, L:] == -torch.inf))
-    rng = np.random.default_rng(0)
-    picks = [(int(b), int(rng.integers(0, w.n_heads))) for b in rng.choice(w.batch, 16, replace=False)]
-    picks[0] = (int(torch.argmax(pos)), 0)    # longest sequence
-    picks[1] = (int(torch.argmin(pos)), 31)   # shortest sequence
-    for b, h in picks:
-        qs, ks, vs = wl.head_slice(w, b, h)
-        ref, ref_s, _ = oracle.decode(qs[0], ks, vs, int(pos[b]), want_scores=True)
-        assert_close(out[b, h:h + 1], ref, "b=%d h=%d" % (b, h))
-        L = w.valid_len(b)
-        assert_dump_close(dump[b, h:h + 1, :L], ref_s, qs[0].numpy(), ks.numpy(), L - 1,
-                          "b=%d h=%d" % (b, h))
+        assert_dump_close(dump_h[b], ref_s[b], qh[b].numpy(), kh[b].numpy(), L - 1, "b=%d" % b)
 
 
-def test_workload_long_context_sampled():
-    """seq_len 131072, 64 heads, 1% of K rows x8: 8 sampled heads against the oracle."""
+@pytest.mark.parametrize("source", ["generator", "normal"])
+def test_workload_long_context_full(source):
+    """seq_len 131072, 64 heads, 1% of K rows x8 (the bench's workload):
+    every output element and every dumped score of all 64 heads against the
+    oracle, on host copies of the device caches."""
     w = wl.WORKLOADS["h64_d64_s131072_spikes"]
-    q = wl.make_q(w, DEV)[0]
-    k, v = wl.make_kv(w, DEV)
-    out = ad.decode(q, k[0], v[0], w.cur_pos)
-    out_d, dump = ad.decode(q, k[0], v[0], w.cur_pos, dump=True)
+    print("case", w.name, source, flush=True)
+    q, k, v = _inputs(w, source)
+    out = ad.decode(q[0], k[0], v[0], w.cur_pos)
+    out_d, dump = ad.decode(q[0], k[0], v[0], w.cur_pos, dump=True)
     torch.cuda.synchronize()
     assert torch.equal(out, out_d)
-    for h in (0, 9, 17, 30, 33, 46, 58, 63):
-        qs, ks, vs = wl.head_slice(w, 0, h)
-        ref, ref_s, _ = oracle.decode(qs[0], ks, vs, w.cur_pos, want_scores=True)
-        assert_close(out[h:h + 1], ref, "h=%d" % h)
-        assert_dump_close(dump[h:h + 1], ref_s, qs[0].numpy(), ks.numpy(), w.cur_pos, "h=%d" % h)
+    qh, kh, vh = q[0].cpu(), k[0].cpu(), v[0].cpu()
+    del k, v
+    ref, ref_s, _ = oracle.decode(qh, kh, vh, w.cur_pos, want_scores=True, threads=16)
+    assert_close(out, ref, "131072 positions")
+    assert_dump_close(dump, ref_s, qh.numpy(), kh.numpy(), w.cur_pos, "131072 positions")
+
+
+def test_long_context_values_near_one_relative():
+    """The 131072-position shape with V ~ N(1, 1), so outputs are mostly of
+    size 1 and the bar 1e-3 |ref| + 1e-4 (tighter than the 2e-3 floor of the
+    general bar) holds them to about two fp16 steps of the exact value.  (A
+    head whose softmax one x8 spike row dominates returns about that row's
+    V, which can be near 0: there the 1e-4 floor applies.)"""
+    w = wl.WORKLOADS["h64_d64_s131072_spikes"]
+    q, k, _ = wl.make_normal(w, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    v = (torch.randn(w.kv_shape, generator=g, device=DEV) + 1.0).half()
+    out = ad.decode(q[0], k[0], v[0], w.cur_pos)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.decode(q[0].cpu(), k[0].cpu(), v[0].cpu(), w.cur_pos, threads=16)
+    got = out.float().cpu().numpy()
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-3 * np.abs(ref) + 1e-4), float((err - 1e-3 * np.abs(ref)).max())
+    assert float(np.median(np.abs(ref))) > 0.5
 
 
 # ------------------------------------------------------------ page cases
