@@ -279,6 +279,12 @@ def run_softmax(args, name):
         if rc != 0:
             raise ad.AttnError(rc, lib.attn_last_error().decode())
 
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        del a, b
     torch.cuda.synchronize()
     log("inputs: %s [%d, %d] fp32, %d cop%s of %.1f MiB (x + out)" % (
         name, w.rows, w.cols, copies, "y" if copies == 1 else "ies", per_copy / 2 ** 20))

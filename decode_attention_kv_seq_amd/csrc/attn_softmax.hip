@@ -5,6 +5,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -143,12 +144,13 @@ __global__ __launch_bounds__(NT) void attn_softmax_stats_kernel(const float *x, 
 template <int NT, int VPT, bool V4>
 __global__ __launch_bounds__(NT) void attn_softmax_apply_kernel(const float *x, float *out,
                                                                 const float *stats, uint32_t cols,
-                                                                uint32_t n_chunks) {
+                                                                uint32_t n_chunks, uint32_t reverse) {
     __shared__ float sm_max[NT / 64];
     __shared__ float sm_sum[NT / 64];
     constexpr uint32_t CH = NT * VPT;
-    const size_t row = blockIdx.x / n_chunks;
-    const uint32_t chunk = blockIdx.x % n_chunks;
+    const uint32_t w = reverse ? gridDim.x - 1 - blockIdx.x : blockIdx.x;
+    const size_t row = w / n_chunks;
+    const uint32_t chunk = w % n_chunks;
     const uint32_t c0 = chunk * CH;
     const uint32_t c_end = cols - c0 < CH ? cols : c0 + CH;
     float v[VPT];
@@ -179,6 +181,32 @@ constexpr uint32_t kSmMinRows = 256;               // rows that fill the chip on
 constexpr uint64_t kSmSmallElems = 1u << 21;       // below this, one launch even with few rows
 
 enum class SmPath { wave, row256, row512, row1024, split };
+
+// Tuning sweeps only: ATTN_SOFTMAX_TUNE="ch=N,nt=N,rev=1" picks the split
+// path's chunk (4096, 8192 or 16384 columns: never more chunks than the
+// workspace holds), its threads, and the apply launch's chunk order.  Read
+// once per process.
+struct SmTune {
+    uint32_t ch = 0, nt = 0, rev = 0;
+};
+const SmTune &sm_tune() {
+    static const SmTune t = [] {
+        SmTune r;
+        const char *e = getenv("ATTN_SOFTMAX_TUNE");
+        if (e) {
+            char buf[128];
+            snprintf(buf, sizeof buf, "%s", e);
+            for (char *tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+                unsigned v = 0;
+                if (sscanf(tok, "ch=%u", &v) == 1 && (v == 4096 || v == 8192 || v == 16384)) r.ch = v;
+                else if (sscanf(tok, "nt=%u", &v) == 1) r.nt = v;
+                else if (sscanf(tok, "rev=%u", &v) == 1) r.rev = v ? 1u : 0u;
+            }
+        }
+        return r;
+    }();
+    return t;
+}
 
 SmPath softmax_path(uint32_t rows, uint32_t cols) {
     static const int forced = [] {
@@ -216,10 +244,26 @@ void launch_softmax(SmPath path, const float *x, float *out, uint32_t rows, uint
         hipLaunchKernelGGL((attn_softmax_row_kernel<1024, 32, V4>), dim3(rows), dim3(1024), 0, st, x, out, cols);
         break;
     case SmPath::split: {
-        const uint32_t n_chunks = (uint32_t)cdiv(cols, kSmChunk);
+        const SmTune &t = sm_tune();
+        const uint32_t ch = t.ch ? t.ch : kSmChunk;
+        const uint32_t n_chunks = (uint32_t)cdiv(cols, ch);
         const dim3 grid((unsigned)((uint64_t)rows * n_chunks));
-        hipLaunchKernelGGL((attn_softmax_stats_kernel<256, 16, V4>), grid, dim3(256), 0, st, x, stats, cols, n_chunks);
-        hipLaunchKernelGGL((attn_softmax_apply_kernel<256, 16, V4>), grid, dim3(256), 0, st, x, out, stats, cols, n_chunks);
+        if (ch == 8192 && t.nt == 512) {
+            hipLaunchKernelGGL((attn_softmax_stats_kernel<512, 16, V4>), grid, dim3(512), 0, st, x, stats, cols, n_chunks);
+            hipLaunchKernelGGL((attn_softmax_apply_kernel<512, 16, V4>), grid, dim3(512), 0, st, x, out, stats, cols, n_chunks, t.rev);
+        } else if (ch == 8192) {
+            hipLaunchKernelGGL((attn_softmax_stats_kernel<256, 32, V4>), grid, dim3(256), 0, st, x, stats, cols, n_chunks);
+            hipLaunchKernelGGL((attn_softmax_apply_kernel<256, 32, V4>), grid, dim3(256), 0, st, x, out, stats, cols, n_chunks, t.rev);
+        } else if (ch == 16384 && t.nt == 1024) {
+            hipLaunchKernelGGL((attn_softmax_stats_kernel<1024, 16, V4>), grid, dim3(1024), 0, st, x, stats, cols, n_chunks);
+            hipLaunchKernelGGL((attn_softmax_apply_kernel<1024, 16, V4>), grid, dim3(1024), 0, st, x, out, stats, cols, n_chunks, t.rev);
+        } else if (ch == 16384) {
+            hipLaunchKernelGGL((attn_softmax_stats_kernel<512, 32, V4>), grid, dim3(512), 0, st, x, stats, cols, n_chunks);
+            hipLaunchKernelGGL((attn_softmax_apply_kernel<512, 32, V4>), grid, dim3(512), 0, st, x, out, stats, cols, n_chunks, t.rev);
+        } else {
+            hipLaunchKernelGGL((attn_softmax_stats_kernel<256, 16, V4>), grid, dim3(256), 0, st, x, stats, cols, n_chunks);
+            hipLaunchKernelGGL((attn_softmax_apply_kernel<256, 16, V4>), grid, dim3(256), 0, st, x, out, stats, cols, n_chunks, t.rev);
+        }
         break;
     }
     }
