@@ -1149,13 +1149,15 @@ struct Knobs {
     uint32_t unroll;   // positions per row group per block (2, 4, 8)
     uint32_t pf;       // double-buffered blocks
     uint32_t bal;      // per-sequence lengths: balanced grid (equal work per workgroup)
+    uint32_t wfloor = 2;   // chunks per head block from wgs / head blocks: 0 rounded up,
+                           // 1 rounded down, 2 down for targets of <= 512 workgroups
 };
 constexpr uint32_t kChunkGranule = 16;
 constexpr uint32_t kMaxHeadsPerWG = kWaves * 64 / 8;   // row groups at 8 lanes per row
 
 const Knobs &env_knobs() {
     static const Knobs t = [] {
-        Knobs r{0, 0, 0, 0, 2, 2};
+        Knobs r{0, 0, 0, 0, 2, 2, 3};
         const char *env = getenv("ATTN_DECODE_TUNE");
         if (env) {
             char buf[256];
@@ -1170,6 +1172,7 @@ const Knobs &env_knobs() {
                     r.unroll = v;
                 else if (sscanf(tok, "pf=%u", &v) == 1) r.pf = v ? 1 : 0;
                 else if (sscanf(tok, "bal=%u", &v) == 1) r.bal = v ? 1 : 0;
+                else if (sscanf(tok, "wfloor=%u", &v) == 1 && v <= 2) r.wfloor = v;
             }
         }
         return r;
@@ -1263,6 +1266,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     if (e.unroll) k.unroll = e.unroll;
     if (e.pf != 2) k.pf = e.pf;
     if (e.bal != 2) k.bal = e.bal;
+    if (e.wfloor != 3) k.wfloor = e.wfloor;
     return k;
 }
 
@@ -1343,7 +1347,17 @@ Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span
     const Knobs k = knobs(D, kind);
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     const uint64_t n_hb = H / heads_per_wg(H, best, k.hpb);
-    const uint64_t nt = cdiv(k.wgs, (uint64_t)batch * n_hb);
+    // Chunks per (sequence, head block): about wgs workgroups in all.  With
+    // a target of at most two workgroups per CU (wgs <= 512), never more
+    // than the target: a few workgroups past a multiple of the CU count put
+    // a third chunk on some CUs, and the launch waits for them (40 heads x
+    // 32768 positions, head_dim 128: 520 workgroups 124.5 us, 500 103.8 us).
+    // With four per CU, one or two past the target cost less than the
+    // longer chunks of fewer workgroups (12 heads x 65536, head_dim 64: 1026
+    // workgroups 38.2 us, 948 42.1 us).
+    const uint64_t per = (uint64_t)batch * n_hb;
+    const bool at_most = k.wfloor == 1 || (k.wfloor == 2 && k.wgs <= 512);
+    const uint64_t nt = at_most ? (k.wgs / per > 0 ? k.wgs / per : 1) : cdiv(k.wgs, per);
     uint64_t c = cdiv(cdiv(span, nt), kChunkGranule) * kChunkGranule;
     if (kind == Kind::single_tiny || kind == Kind::batched_short)   // one chunk
         c = cdiv(span, kChunkGranule) * kChunkGranule;

@@ -191,6 +191,20 @@ def test_step_shapes(shape):
     check_step(out, kg, vg, kc, vc, q, kn, vn, cp, dims, trad, what=str(shape))
 
 
+@pytest.mark.parametrize("shape", [(8192, 40, 128, 8191), (32768, 24, 128, 30000)],
+                         ids=lambda s: "S%d_H%d_D%d_cp%d" % s)
+def test_step_head_counts_off_a_power_of_two(shape):
+    """Head counts that are not powers of two, on the plans that keep the
+    workgroup count within the target (two per CU)."""
+    S, H, D, cp = shape
+    print("step shape", shape, flush=True)
+    rng = np.random.default_rng(S + H)
+    q, kn, vn = randn16(rng, (H, D), 1.5), randn16(rng, (H, D)), randn16(rng, (H, D))
+    kc, vc = randn16(rng, (S, H, D)), randn16(rng, (S, H, D))
+    out, kg, vg = run_step_single(q, kn, vn, kc, vc, cp, D, False)
+    check_step(out, kg, vg, kc, vc, q, kn, vn, cp, D, False, threads=16, what=str(shape))
+
+
 def test_step_at_position_zero_returns_new_value_exactly():
     rng = np.random.default_rng(5)
     for D in (64, 128, 7):

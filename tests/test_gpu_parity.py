@@ -181,6 +181,29 @@ def test_workload_long_context_full(source):
     assert_dump_close(dump, ref_s, qh.numpy(), kh.numpy(), w.cur_pos, "131072 positions")
 
 
+@pytest.mark.parametrize("H,D,S,cp", [(40, 128, 32768, 32767), (20, 128, 65536, 40000),
+                                      (96, 128, 4096, 4095), (40, 192, 8192, 8191), (12, 64, 65536, 65535)])
+def test_head_counts_off_a_power_of_two(H, D, S, cp):
+    """Single sequences with head counts that are not powers of two (the
+    chunk count planned from the workgroup target rounds down for two
+    workgroups per CU, up for four): every output element and every dumped
+    score against the oracle, normal inputs."""
+    print("case", H, D, S, cp, flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(H * 1000 + D)
+    q = torch.randn((H, D), generator=g, device=DEV).half()
+    k = torch.randn((S, H, D), generator=g, device=DEV).half()
+    v = torch.randn((S, H, D), generator=g, device=DEV).half()
+    out = ad.decode(q, k, v, cp)
+    out_d, dump = ad.decode(q, k, v, cp, dump=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_d)
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    ref, ref_s, _ = oracle.decode(qh, kh, vh, cp, want_scores=True, threads=16)
+    assert_close(out, ref, "H=%d D=%d" % (H, D))
+    assert_dump_close(dump, ref_s, qh.numpy(), kh.numpy(), cp, "H=%d D=%d" % (H, D))
+
+
 def test_long_context_values_near_one_relative():
     """The 131072-position shape with V ~ N(1, 1), so outputs are mostly of
     size 1 and the bar 1e-3 |ref| + 1e-4 (tighter than the 2e-3 floor of the

@@ -35,6 +35,28 @@ def test_single_sequence_workload_plans(args, expect):
     assert {k: p[k] for k in expect} == expect, p
 
 
+@pytest.mark.parametrize("H,D,S,flags", [
+    (40, 128, 32768, 0), (40, 128, 8192, 0), (20, 128, 65536, 0), (96, 128, 4096, 0),
+    (24, 128, 65536, PLAN_STEP), (40, 128, 32768, PLAN_STEP), (40, 192, 32768, 0), (12, 128, 32768, 0),
+])
+def test_two_per_cu_plans_stay_within_their_target(H, D, S, flags):
+    """Single sequences whose target is at most 512 workgroups (two per CU,
+    head_dim > 64) never plan more than the target, and stay close to it: a
+    few past a multiple of the 256 CUs would give some CUs a third chunk."""
+    p = plan(1, H, D, S, S - 1, flags)
+    target = 256 if flags & PLAN_STEP and D <= 128 else 512
+    assert p["workgroups"] <= target, p
+    assert p["workgroups"] >= 0.85 * target, p
+
+
+@pytest.mark.parametrize("H,D,S,expect", [(12, 64, 65536, 1026), (20, 64, 65536, 1025)])
+def test_four_per_cu_plans_round_up(H, D, S, expect):
+    """With four workgroups per CU (head_dim 64, 1024 workgroups) the chunk
+    count rounds up: one or two workgroups past the target cost less than
+    the longer chunks of fewer workgroups."""
+    assert plan(1, H, D, S, S - 1)["workgroups"] == expect
+
+
 def test_ragged_batch_workload_takes_the_balanced_grid():
     p = plan(64, 32, 128, 8192, flags=PLAN_DEVICE_POS)
     assert (p["balanced"], p["workgroups"], p["heads_per_workgroup"], p["launches"]) == (1, 256, 8, 2)
