@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_f16_paged_split.argtypes = [vp, vp, vp, vp, vp, u32, u32, u32, u32, u32, u32,
                                                 vp, vp, sz, vp]
     lib.attn_decode_f16_paged_split.restype = ctypes.c_int
+    lib.attn_paged_table_check.argtypes = [vp, vp, u32, u32, u32, u32, vp, vp]
+    lib.attn_paged_table_check.restype = ctypes.c_int
     lib.attn_qk_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, vp]
     lib.attn_qk_f16.restype = ctypes.c_int
     lib.attn_pv_f16.argtypes = [vp, vp, vp, u32, u32, u32, u32, vp, sz, vp]
@@ -407,6 +409,30 @@ def split_paged(q, k_pool, v_pool, block_table, current_pos, workspace, *, dump=
                                                _ptr(workspace),
                                                workspace.numel() * workspace.element_size(),
                                                _stream_handle(stream)))
+
+
+@_on_stream
+def paged_table_check(block_table, current_pos, page_size: int, num_blocks: int, *, result=None,
+                      stream=None):
+    """attn_paged_table_check: -> uint32 GPU tensor [2] (entries a paged call
+    reads that are >= num_blocks; the first sequence holding one, or
+    0xFFFFFFFF).  Asynchronous, like every call."""
+    lib = load_library()
+    _req(block_table, "block_table", block_table.dtype)
+    if block_table.dtype not in (torch.int32, torch.uint32) or block_table.dim() != 2:
+        raise TypeError("block_table must be an int32/uint32 GPU tensor [batch, max_blocks]")
+    dev = block_table.device
+    B, MB = block_table.shape
+    cp = _cp_tensor(current_pos, B, dev)
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=dev)
+    _req_buf(result, "result", dev)
+    if result.numel() * result.element_size() < 8:
+        raise ValueError("result must hold two uint32 words")
+    with torch.cuda.device(dev):   # launch on the tensors' device
+        _check(lib.attn_paged_table_check(_ptr(block_table), _ptr(cp), B, int(page_size), MB,
+                                          int(num_blocks), _ptr(result), _stream_handle(stream)))
+    return result
 
 
 @_on_stream

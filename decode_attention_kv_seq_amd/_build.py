@@ -12,7 +12,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("attn_decode.hip", "attn_softmax.hip", "attn_status.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("attn_decode.hip", "attn_softmax.hip", "attn_table.hip",
+                                           "attn_status.cpp")]
 SRC = SOURCES[0]   # the decode kernels (their hash keys the committed counter profiles)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_decode.so")

@@ -238,7 +238,7 @@ attn_status_t attn_decode_f16_combine(uint16_t *out, const uint32_t *current_pos
  *                   Only entries for positions <= current_pos are read;
  *                   several sequences may share a page.  An entry >=
  *                   num_blocks is read as num_blocks - 1 (in bounds, output
- *                   meaningless).
+ *                   meaningless); attn_paged_table_check finds such entries.
  *   current_pos     DEVICE [batch] uint32; capacity = max_blocks * page_size
  *   page_size       a power of two, 1..65536
  *   q, out          [batch, n_heads, head_dim] fp16; scores_dump NULL or
@@ -262,6 +262,27 @@ attn_status_t attn_decode_f16_paged_split(const uint16_t *q, const uint16_t *k_p
                                           uint32_t max_blocks, uint32_t num_blocks,
                                           float *scores_dump, void *workspace,
                                           size_t workspace_bytes, void *stream);
+
+/*
+ * A check of a paged cache's block table, for callers that want to know
+ * whether a paged call read a table entry that names no page of the pool
+ * (such an entry is read as the last page: in bounds, output meaningless).
+ * It enqueues two small launches on `stream` and writes, in device memory:
+ *   result[0]  the number of entries a paged decode or decode step with these
+ *              block_table and current_pos reads (block j of sequence b when
+ *              j * page_size <= min(current_pos[b], capacity - 1)) that are
+ *              >= num_blocks;
+ *   result[1]  the lowest sequence index holding such an entry, or
+ *              0xFFFFFFFF when there is none.
+ * result: DEVICE uint32[2], written (no initialisation needed).  Other
+ * arguments as attn_decode_f16_paged.  The check reads the table once; it is
+ * not part of a decode call.
+ * Errors: ATTN_ERR_NULL, ATTN_ERR_ALIGN (4-byte pointers), ATTN_ERR_DIM (as
+ * the paged calls), ATTN_ERR_HIP.
+ */
+attn_status_t attn_paged_table_check(const uint32_t *block_table, const uint32_t *current_pos,
+                                     uint32_t batch, uint32_t page_size, uint32_t max_blocks,
+                                     uint32_t num_blocks, uint32_t *result, void *stream);
 
 /*
  * The page's own two-dispatch form (section "The MSL, briefly": kernels

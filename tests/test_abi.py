@@ -39,7 +39,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -173,6 +173,21 @@ def test_noalloc_rejects_bad_arguments(lib):
     for (B, H, D, S) in [(64, 32, 128, 8192), (1, 32, 128, 32768), (1, 64, 64, 131072),
                          (1024, 32, 128, 8192)]:
         assert 0 < ad.workspace_bytes(B, H, D, S) <= ad.NOALLOC_SCRATCH_BYTES
+
+
+@host_only
+def test_table_check_rejects_bad_arguments(lib):
+    f = lib.attn_paged_table_check
+    assert f(None, FAKE, 2, 16, 8, 16, FAKE, None) == NULL
+    assert f(FAKE, None, 2, 16, 8, 16, FAKE, None) == NULL
+    assert f(FAKE, FAKE, 2, 16, 8, 16, None, None) == NULL
+    assert f(FAKE + 2, FAKE, 2, 16, 8, 16, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, 2, 16, 8, 16, FAKE + 2, None) == ALIGN
+    assert f(FAKE, FAKE, 0, 16, 8, 16, FAKE, None) == DIM
+    assert f(FAKE, FAKE, 2, 12, 8, 16, FAKE, None) == DIM
+    assert f(FAKE, FAKE, 2, 16, 0, 16, FAKE, None) == DIM
+    assert f(FAKE, FAKE, 2, 16, 8, 0, FAKE, None) == DIM
+    assert f(FAKE, FAKE, 2, 65536, 1 << 16, 16, FAKE, None) == DIM
 
 
 def test_paged_generator_gathers_the_pool():

@@ -204,6 +204,33 @@ def test_head_counts_off_a_power_of_two(H, D, S, cp):
     assert_dump_close(dump, ref_s, qh.numpy(), kh.numpy(), cp, "H=%d D=%d" % (H, D))
 
 
+def test_paged_table_check_counts_entries_past_the_pool():
+    """attn_paged_table_check counts the entries a paged call reads (blocks
+    up to each sequence's current_pos, clamped to the capacity) that name
+    no page of the pool, and names the first sequence holding one; entries
+    past current_pos do not count.  Expected values from the table itself."""
+    B, P, MB, NB = 5, 16, 8, 40
+    rng = np.random.default_rng(31)
+    table = rng.integers(0, NB, (B, MB)).astype(np.int64)
+    cp = np.array([0, 16, 127, 130, 50])     # blocks read: 1, 2, 8, 8 (clamped), 4
+    n_read = np.minimum(cp, P * MB - 1) // P + 1
+    res = ad.paged_table_check(to_dev(table.astype(np.int32)), to_dev(cp.astype(np.int32)), P, NB)
+    torch.cuda.synchronize()
+    assert res.cpu().tolist() == [0, -1]
+    bad = table.copy()
+    bad[1, 1] = NB              # read (block 1 <= 16 // 16)
+    bad[1, 2] = NB + 7          # not read
+    bad[3, 7] = 2 ** 31 - 1     # read: position 130 clamps to 127
+    bad[4, 3] = NB              # read
+    bad[4, 4] = NB              # not read
+    bad[0, 1] = NB              # not read (sequence 0 reads block 0 only)
+    expect = sum(int(bad[b, j] >= NB) for b in range(B) for j in range(n_read[b]))
+    res = ad.paged_table_check(to_dev(bad.astype(np.int32)), to_dev(cp.astype(np.int32)), P, NB)
+    torch.cuda.synchronize()
+    assert expect == 3
+    assert res.cpu().tolist() == [3, 1]
+
+
 def test_long_context_values_near_one_relative():
     """The 131072-position shape with V ~ N(1, 1), so outputs are mostly of
     size 1 and the bar 1e-3 |ref| + 1e-4 (tighter than the 2e-3 floor of the

@@ -121,9 +121,9 @@ def _sanitized_library():
     """The library with host-side sanitizers, built once per source state
     into _build/sanitized (git-ignored); the device code is built as usual,
     so the library loads exactly like the product one."""
-    sources = [os.path.join(CSRC, f) for f in ("attn_decode.hip", "attn_softmax.hip",
-                                               "attn_status.cpp", "attn_internal.h")]
-    sources.append(os.path.join(ROOT, "include", "attn_decode.h"))
+    from decode_attention_kv_seq_amd import _build as lib_build
+    units = list(lib_build.SOURCES)
+    sources = units + [os.path.join(CSRC, "attn_internal.h"), os.path.join(ROOT, "include", "attn_decode.h")]
     h = hashlib.sha256()
     for p in sources:
         h.update(open(p, "rb").read())
@@ -136,7 +136,7 @@ def _sanitized_library():
     for f in SAN_FLAGS:
         host_san += ["-Xarch_host", f]
     objs, procs = [], []
-    for src in sources[:3]:
+    for src in units:
         obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
         cmd = ([hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + host_san +
