@@ -225,7 +225,7 @@ attn_status_t attn_decode_f16_combine(uint16_t *out, const uint32_t *current_pos
 
 /*
  * A batch whose K/V caches live in a paged pool.  The page "Tutorial 16:
- * Writing Custom Metal Kernels" (section "Performance Impact") names paged
+ * Writing Custom Metal Kernels" (section "7. Performance Impact") names paged
  * attention that reads pages directly instead of gathering them first; the
  * page "Developing Apple Metal Kernels in Rust - A Deep Dive Through
  * Attention" (section "setBuffer_offset_atIndex and unified memory") keeps
