@@ -610,6 +610,9 @@ def main():
         "path": args.path,
         "inputs": "torch.randn (normal)" if not w.paged else
                   "counter-based generator (Irwin-Hall(4), +-3.46 sigma)",
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "hbm_bytes": props.total_memory,
+                   "arch": getattr(props, "gcnArchName", "")},
     }
     if gates is not None:
         config["gates"] = gates

@@ -315,6 +315,30 @@ def pin_linear_in_values(orc):
     assert np.allclose(o12, o1 + o2, rtol=0, atol=1e-13)
 
 
+def pin_output_within_value_range(orc):
+    """The output is a convex combination of the unmasked V rows (weights >= 0
+    summing to 1), so min_p V[p,h,d] <= out[h,d] <= max_p V[p,h,d] over the
+    positions p <= current_pos, up to rounding of the weighted sum; with V of
+    one sign and masked rows far outside that range, the bound also shows
+    that no masked row and no negative weight enters."""
+    rng = _rng(25)
+    S, H, D, cp = 40, 3, 12, 26
+    q = _randn_f16(rng, (H, D)) * np.float16(3)
+    k = _randn_f16(rng, (S, H, D))
+    v = _randn_f16(rng, (S, H, D))
+    v[cp + 1:] = np.float16(1000)               # masked rows far above any valid value
+    out, _, w = orc.decode(q, k, v, cp, want_weights=True)
+    assert np.all(w[:, :cp + 1] >= 0.0) and np.all(w[:, cp + 1:] == 0.0)
+    vv = v[:cp + 1].astype(np.float64)
+    lo, hi = vv.min(axis=0), vv.max(axis=0)
+    slack = 1e-12 * np.maximum(np.abs(lo), np.abs(hi))
+    assert np.all(out >= lo - slack) and np.all(out <= hi + slack)
+    vp = np.abs(v[:cp + 1]).astype(np.float16) + np.float16(1)    # all valid values in [1, ...)
+    vp = np.concatenate([vp, np.full((S - cp - 1, H, D), -1000, np.float16)])
+    out_p, _, _ = orc.decode(q, k, vp, cp)
+    assert np.all(out_p >= 1.0 - 1e-12)
+
+
 def pin_heads_are_independent(orc):
     """Changing the cache of one head leaves every other head's output alone."""
     rng = _rng(13)
@@ -838,6 +862,7 @@ ALL_PINS = [
     pin_torch_sdpa_float64,
     pin_position_permutation_invariance,
     pin_linear_in_values,
+    pin_output_within_value_range,
     pin_heads_are_independent,
     pin_pv_equals_decode_on_representable_scores,
     pin_pv_two_positions_closed_form,

@@ -137,6 +137,24 @@ def test_workload_full_parity_normal(name, source):
     assert_dump_close(dump, ref_s, qh.numpy(), kh.numpy(), w.cur_pos, name)
 
 
+def test_workload_peaked_query_full():
+    """The seq-32768 cache with q of sigma 4 instead of 2 (the more peaked
+    reading of its query distribution): scores of sigma about 4, so a few
+    positions carry most of each head's weight; every output element and
+    every dumped score against the oracle, normal inputs."""
+    w = wl.WORKLOADS["h32_d128_s32768_cp20000_garbage"]
+    q, k, v = wl.make_normal(w, DEV)
+    q = (q.float() * 2.0).half()
+    out = ad.decode(q[0], k[0], v[0], w.cur_pos)
+    out_d, dump = ad.decode(q[0], k[0], v[0], w.cur_pos, dump=True)
+    torch.cuda.synchronize()
+    qh, kh, vh = q[0].cpu(), k[0].cpu(), v[0].cpu()
+    ref, ref_s, _ = oracle.decode(qh, kh, vh, w.cur_pos, want_scores=True, threads=16)
+    assert_close(out, ref, "q sigma 4")
+    assert torch.equal(out, out_d), "dump variant differs from the timed kernel"
+    assert_dump_close(dump, ref_s, qh.numpy(), kh.numpy(), w.cur_pos, "q sigma 4")
+
+
 @pytest.mark.parametrize("source", ["generator", "normal"])
 def test_workload_ragged_batch_full(source):
     """64 sequences x 32 heads, capacity 8192 (the full-size launch the bench
