@@ -312,14 +312,16 @@ struct PieceDst {
 
 // What a split launch computes: the one-pass decode; softmax.V from stored
 // fp16 scores (the page's second dispatch); the decode step (q rotated, the
-// new token's slot left to the combine); or only the scores, written as fp16
-// (the page's first dispatch).
+// new token's slot left to the combine, or merged and appended here when one
+// chunk covers each head block); or only the scores, written as fp16 (the
+// page's first dispatch).
 enum : int { kModeDecode = 0, kModePv = 1, kModeStep = 2, kModeQk = 3 };
 
 // Stream positions [c0, c_end) of head block hb of sequence b through the
 // online softmax and leave one merged state per head at `dst` (kModeQk: write
 // the scores of those positions instead).  The caller
-// guarantees c0 < c_end.  LDS is free again when this returns.
+// guarantees c0 < c_end, except for a one-launch decode step at position 0
+// (c0 == c_end: nothing is streamed, and the new token alone is merged).  LDS is free again when this returns.
 template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
 __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint32_t hb,
                                             uint32_t c0, uint32_t c_end, const PieceDst &dst,
@@ -352,6 +354,9 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         eok[j] = FULL || eoff[j] < (int)a.D;
     }
 
+    // one-launch decode step: the new token's score per head, and v_new
+    __shared__ float sm_tnew[ROPE ? NG : 1];
+    __shared__ uint16_t sm_vnew[ROPE ? NG * DPAD : 1];
     Pack<VEC> qp[NV];
     if constexpr (ROPE) {
         // Decode step: the head block's query rows, rotated at the new
@@ -361,12 +366,40 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         // loop registers, which is worse.
         uint16_t *sq = reinterpret_cast<uint16_t *>(sm_o);
         const uint32_t pos = valid_len(a.cp_dev ? a.cp_dev[b] : a.cp_host, a.S) - 1u;
-        const uint16_t *qblk = a.q + ((size_t)b * a.H + (size_t)hb * a.hpb) * D;
+        const size_t bh0 = (size_t)b * a.H + (size_t)hb * a.hpb;
+        const uint16_t *qblk = a.q + bh0 * D;
         const uint32_t n_q = a.hpb * a.D;
+        // One chunk per head block (dst.out: the step is one launch): the new
+        // token too, which the merge launch takes otherwise.  Its key rows are
+        // rotated alongside q (their loads share q's round trip), both rows
+        // are appended at slot pos (no streamed position reads that slot),
+        // and v_new waits in LDS for the final merge.
+        uint16_t *sk = sq + n_q;
+        size_t slot = (size_t)b * a.S + pos;
+        bool keep = true;
+        if constexpr (PAGED) {
+            if (dst.out) {
+                const uint32_t page = a.block_table[(size_t)b * a.max_blocks + (pos >> a.page_shift)];
+                keep = page < a.num_blocks;   // an entry past the pool: nothing is written
+                slot = (size_t)page << a.page_shift | (pos & ((1u << a.page_shift) - 1u));
+            }
+        }
 #pragma unroll 1
         for (uint32_t idx = tid; idx < n_q; idx += kThreads) {
             const uint32_t ho = idx / a.D;
-            sq[idx] = f2h_rne(rope_elem(qblk + (size_t)ho * D, idx - ho * a.D, a.rope, pos));
+            const uint32_t d = idx - ho * a.D;
+            sq[idx] = f2h_rne(rope_elem(qblk + (size_t)ho * D, d, a.rope, pos));
+            if (dst.out) {
+                const uint16_t k16 = f2h_rne(rope_elem(a.rope.k_new + (bh0 + ho) * D, d, a.rope, pos));
+                const uint16_t v16 = a.rope.v_new[(bh0 + ho) * D + d];
+                sk[idx] = k16;
+                sm_vnew[idx] = v16;
+                if (keep) {
+                    const size_t crow = (slot * a.H + (size_t)hb * a.hpb + ho) * D + d;
+                    a.rope.k_cache[crow] = k16;
+                    a.rope.v_cache[crow] = v16;
+                }
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -375,6 +408,16 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 #pragma unroll
             for (int e = 0; e < VEC; ++e) hv[e] = eok[j] ? sq[hg * a.D + eoff[j] + e] : 0;
             qp[j] = make_pack<VEC>(hv);
+        }
+        if (dst.out) {   // the new token's base-2 score: wave w takes heads w, w + 4, ...
+            for (uint32_t ho = (uint32_t)tid >> 6; ho < a.hpb; ho += kWaves) {
+                float prod = 0.f;
+                for (uint32_t d = lane; d < a.D; d += 64)   // exact products of fp16 values
+                    prod += h2f(sq[ho * a.D + d]) * h2f(sk[ho * a.D + d]);
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) prod += __shfl_xor(prod, off, 64);
+                if (lane == 0) sm_tnew[ho] = prod * a.scale_log2;
+            }
         }
         __syncthreads();   // LDS is written again by the merge below
     } else if constexpr (!SC) {
@@ -541,6 +584,9 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
     };
 
     const uint32_t step = pps * U;
+    // An empty piece (a one-launch decode step at position 0) streams nothing;
+    // other modes never get one, and their code keeps no test for it.
+    if (!ROPE || c0 < c_end) {
     if constexpr (PF) {
         // Two register blocks: the next block's loads are in flight while the
         // current one is reduced.  The steady-state loop issues its loads
@@ -581,6 +627,7 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
             P0 = P1;
         }
     }
+    }
 
     if constexpr (QK) return;   // no softmax state to merge
 
@@ -601,6 +648,13 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
         const uint32_t d = idx % a.D;
         float M = -INFINITY;
         for (uint32_t r = 0; r < pps; ++r) M = fmaxf(M, sm_m[r * a.hpb + ho]);
+        float t_new = -INFINITY;   // the new token's score (one-launch decode step)
+        if constexpr (ROPE) {
+            if (dst.out) {
+                t_new = sm_tnew[ho];
+                M = fmaxf(M, t_new);
+            }
+        }
         // Position lane 0 always saw position c0, so M is finite unless every
         // score here is a stored -inf (softmax.V from a masked stretch of the
         // row); such a head merges to (-inf, 0, 0), which the combine weighs
@@ -614,6 +668,11 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
             lsum = fmaf(sm_l[gg], w, lsum);
         }
         if (dst.out) {
+            if constexpr (ROPE) {   // the new token joins with l term 1
+                const float w = __builtin_amdgcn_exp2f(t_new - Mu);
+                o = fmaf(h2f(sm_vnew[ho * a.D + d]), w, o);
+                lsum = fmaf(1.f, w, lsum);
+            }
             dst.out[ho * a.D + d] = f2h_rne(o / lsum);
         } else {
             dst.po[ho * dst.po_hs + d] = o;
@@ -668,7 +727,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
     // a decode step streams the positions before the new token's slot
     const uint32_t L = valid_len(cp, a.S) - (ROPE ? 1u : 0u);
     const uint32_t c0 = chunk * a.chunk;
-    if (c0 >= L) return;                     // whole workgroup: nothing to read
+    // whole workgroup: nothing to read (a one-launch decode step at position
+    // 0 still merges the new token)
+    if (c0 >= L && !(ROPE && a.direct)) return;
     const uint32_t c_end = min(c0 + a.chunk, L);
     const size_t bh0 = (size_t)b * a.H + (size_t)hb * a.hpb;
     PieceDst dst;
@@ -1622,7 +1683,7 @@ attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t 
     a.header = static_cast<uint32_t *>(ws);
     a.part_o = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.o_off);
     a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.ml_off);
-    a.direct = (!bal && !rope && out && plan.n_chunks == 1) ? 1 : 0;
+    a.direct = (!bal && out && plan.n_chunks == 1) ? 1 : 0;
     a.out = out;
     a.dump = dump;
     a.batch = batch;
@@ -1698,7 +1759,9 @@ void fill_rope(RopeArgs *r, uint32_t dims, double base, int traditional) {
 
 // One decode step: rotate q and k_new at pos = min(current_pos, S - 1),
 // stream positions 0..pos-1 (split launch), then merge them with the new
-// token and append its k and v rows at slot pos (combine launch).
+// token and append its k and v rows at slot pos (combine launch).  When the
+// plan gives each head block one chunk, the split launch does the merge and
+// the append itself, and the step is one launch.
 attn_status_t decode_step(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
                           uint16_t *k_cache, uint16_t *v_cache, uint16_t *out,
                           const uint32_t *cp_dev, uint32_t cp_host, uint32_t batch, uint32_t H,
@@ -1725,9 +1788,9 @@ attn_status_t decode_step(const uint16_t *q, const uint16_t *k_new, const uint16
     r.v_cache = v_cache;
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool wrote = false;
-    s = launch_split(q, k_cache, v_cache, cp_dev, cp_host, batch, H, D, S, nullptr, ws, nullptr,
+    s = launch_split(q, k_cache, v_cache, cp_dev, cp_host, batch, H, D, S, nullptr, ws, out,
                      pg, st, &wrote, nullptr, &r);
-    if (s != ATTN_OK) return s;
+    if (s != ATTN_OK || wrote) return s;   // one chunk per head block: the split launch did it all
     return launch_combine(out, cp_dev, cp_host, batch, H, D, S, ws, st, &r, q, pg);
 }
 
@@ -1847,7 +1910,7 @@ attn_status_t attn_decode_plan(uint32_t batch, uint32_t n_heads, uint32_t head_d
                     (unsigned long long)grid_x, (unsigned long long)(kMaxGridItems / kThreads));
     // one launch: a one-call entry point (a batch with one host current_pos
     // exists only as the split / combine pair) whose plan has one chunk
-    const bool direct = !sp.bal && !step && sp.plan.n_chunks == 1 && (dev_pos || batch == 1);
+    const bool direct = !sp.bal && sp.plan.n_chunks == 1 && (dev_pos || batch == 1);
     info->balanced = sp.bal ? 1u : 0u;
     info->heads_per_workgroup = sp.hpb;
     info->workgroups = sp.bal ? (uint64_t)sp.kn.wgs : grid_x * batch;

@@ -316,7 +316,9 @@ attn_status_t attn_pv_f16(const uint16_t *scores, const uint16_t *v_cache, uint1
 /*
  * One decode step: rotary embedding of the new token's query and key, the
  * append of its key and value rows to the caches, and attention over the
- * cache including the new row, in two launches.  The rotation is the one the
+ * cache including the new row: one launch when the plan gives each head
+ * block of a sequence one chunk (short caches; attn_decode_plan reports it),
+ * else two.  The rotation is the one the
  * page "Tutorial 16: Writing Custom Metal Kernels" describes (section "5.
  * Example: Fused RoPE Kernel": FastRoPE(dims, base, traditional) applied at
  * a per-sequence offset); the cache layout, current_pos and the attention
