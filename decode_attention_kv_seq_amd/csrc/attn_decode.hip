@@ -1850,14 +1850,24 @@ constexpr int kMaxScratchDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxScratchDevices];   // device address of `scratch`, per device
 
-// The current device's `scratch`, looked up on its first use there.
-attn_status_t scratch_of_current_device(void **ptr) {
+// The current device's `scratch`, looked up on its first use there.  A
+// stream of another device is refused: its kernels would be handed this
+// device's address.
+attn_status_t scratch_of_current_device(void **ptr, hipStream_t stream) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     if (dev < 0 || dev >= kMaxScratchDevices)
         return fail(ATTN_ERR_HIP, "device %d is past the %d the library keeps scratch for", dev,
                     kMaxScratchDevices);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(ATTN_ERR_DIM, "the stream belongs to device %d, the current device is %d", sdev,
+                        dev);
+    }
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
         void *p = nullptr;
@@ -1964,7 +1974,7 @@ attn_status_t attn_decode_f16_batched_noalloc(const uint16_t *q, const uint16_t 
                     "these sizes need %zu bytes of workspace; the allocation-free call holds %zu",
                     need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
     void *ws = nullptr;
-    s = scratch_of_current_device(&ws);
+    s = scratch_of_current_device(&ws, static_cast<hipStream_t>(stream));
     if (s != ATTN_OK) return s;
     return decode_full(q, k_cache, v_cache, out, current_pos, 0, batch, n_heads, head_dim,
                        capacity, scores_dump, ws, ATTN_NOALLOC_SCRATCH_BYTES, nullptr, stream);

@@ -181,7 +181,9 @@ attn_status_t attn_decode_f16_batched(const uint16_t *q, const uint16_t *k_cache
  *   Errors: as attn_decode_f16_batched; ATTN_ERR_WORKSPACE when
  *   attn_decode_workspace_bytes(batch, n_heads, head_dim, capacity) exceeds
  *   ATTN_NOALLOC_SCRATCH_BYTES (checked on the host, nothing enqueued);
- *   ATTN_ERR_HIP when the array cannot be located on the current device.
+ *   ATTN_ERR_HIP when the array cannot be located on the current device;
+ *   ATTN_ERR_DIM when `stream` belongs to another device than the current
+ *   one (both checked before anything is enqueued).
  *   Nothing in the array needs to start at zero.
  * The array is per GPU and shared by every call on that GPU: calls that can
  * run at the same time on one GPU (enqueued on different streams, or graphs
