@@ -44,3 +44,61 @@ def test_noalloc_matches_batched_call_twice():
             got = out[b].float().cpu().numpy()
             assert np.all(np.abs(got - o) <= 2e-3 + 4e-3 * np.abs(o)), (B, b)
 
+
+
+FIRST_CALL_CAPTURED = """
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import decode_attention_kv_seq_amd as ad
+dev = torch.device("cuda:0")
+g = torch.Generator(device=dev)
+g.manual_seed(3)
+B, S, H, D = 4, 500, 8, 64
+q = torch.randn((B, H, D), generator=g, device=dev).half()
+k = torch.randn((B, S, H, D), generator=g, device=dev).half()
+v = torch.randn((B, S, H, D), generator=g, device=dev).half()
+cp = torch.tensor([499, 0, 250, 700], dtype=torch.int32, device=dev)
+out = torch.empty_like(q)
+torch.cuda.synchronize()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):          # the process's first allocation-free call
+    ad.decode_batched_noalloc(q, k, v, cp, out=out)
+graph.replay()
+torch.cuda.synchronize()
+ref = ad.decode_batched(q, k, v, cp)
+torch.cuda.synchronize()
+assert torch.equal(out, ref)
+print("first call under capture: ok", flush=True)
+"""
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point is for capture it in a graph: a captured
+    call, replayed four times with eager calls of other sizes on the same
+    array in between, gives the batched call's output bitwise each time;
+    and the process's very first call (which looks up the array's address)
+    may itself be made under capture (child process)."""
+    import os
+    import subprocess
+    import sys
+    q, k, v, cp = _inputs(6, 1200, 8, 128, 11)
+    ref = ad.decode_batched(q, k, v, cp)
+    out = torch.full_like(ref, float("nan"))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ad.decode_batched_noalloc(q, k, v, cp, out=out)
+    q2, k2, v2, cp2 = _inputs(3, 400, 4, 64, 12)
+    ref2 = ad.decode_batched(q2, k2, v2, cp2)
+    for i in range(4):
+        out.fill_(float("nan"))
+        out2 = torch.empty_like(ref2)
+        ad.decode_batched_noalloc(q2, k2, v2, cp2, out=out2)   # eager, same array
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out2, ref2), i
+        assert torch.equal(out, ref), "replay %d differs from the batched call" % i
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", FIRST_CALL_CAPTURED, root], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
