@@ -27,7 +27,8 @@
 // row), a paged cache read through a block table, and the decode step of the
 // page "Tutorial 16: Writing Custom Metal Kernels" (q rotated at the new
 // token's position; the combine folds in the new token and appends its K/V
-// rows).  File layout: device helpers (packs, lane-group sums, rotation),
+// rows, or the split kernel itself when one chunk covers each head block).
+// File layout: device helpers (packs, lane-group sums, rotation),
 // split kernels, combine kernel, dump fill, standalone rotation; then the
 // host planner, kernel selection, launchers and the C ABI.
 
