@@ -612,7 +612,8 @@ def main():
                   "counter-based generator (Irwin-Hall(4), +-3.46 sigma)",
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "hbm_bytes": props.total_memory,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""),
+                   "hip_runtime": getattr(torch.version, "hip", None)},
     }
     if gates is not None:
         config["gates"] = gates
