@@ -243,6 +243,34 @@ def test_step_agrees_with_rope_then_decode():
     assert d <= 2e-3, d
 
 
+def _offset_view(x_host, off):
+    """A contiguous GPU copy of x_host that starts `off` fp16 elements into
+    its own buffer (so not 16-byte aligned for odd `off`)."""
+    flat = torch.from_numpy(np.ascontiguousarray(x_host)).reshape(-1)
+    base = torch.zeros(flat.numel() + off, dtype=torch.float16, device=DEV)
+    base[off:] = flat.to(DEV)
+    return base[off:].view(x_host.shape)
+
+
+@pytest.mark.parametrize("off", [1, 3])
+@pytest.mark.parametrize("S,H,D,cp", [(120, 4, 64, 100), (5000, 8, 128, 4000), (300, 6, 48, 299)],
+                         ids=["one_launch_d64", "two_launches_d128", "one_launch_d48"])
+def test_step_unaligned_tensors(S, H, D, cp, off):
+    """q, k_new, v_new and both caches offset by `off` elements (narrower
+    loads): the step, in one launch or two, against the oracle, with the
+    appended rows and every other row checked."""
+    print("step unaligned", S, H, D, cp, off, flush=True)
+    rng = np.random.default_rng(S + off)
+    q, kn, vn = randn16(rng, (H, D)), randn16(rng, (H, D)), randn16(rng, (H, D))
+    kc, vc = randn16(rng, (S, H, D)), randn16(rng, (S, H, D))
+    kc_d, vc_d = _offset_view(kc, off), _offset_view(vc, off)
+    out = ad.decode_step(_offset_view(q, off), _offset_view(kn, off), _offset_view(vn, off), kc_d, vc_d,
+                         cp, rope_dims=D, traditional=bool(off & 2))
+    torch.cuda.synchronize()
+    check_step(out, kc_d.cpu().numpy(), vc_d.cpu().numpy(), kc, vc, q, kn, vn, cp, D, bool(off & 2),
+               what="offset %d" % off)
+
+
 def test_consecutive_steps_grow_the_cache():
     """Five steps in a row at positions 40..44 (the decode loop), each
     checked against the oracle run on its own copy of the cache."""
