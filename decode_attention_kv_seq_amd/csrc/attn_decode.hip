@@ -1290,6 +1290,7 @@ constexpr uint32_t kShortSpan = 8192;
 constexpr uint64_t kOneChunkBytes = 256u << 10;
 constexpr uint64_t kShortGroups = 8192;
 constexpr uint64_t kShortMinGroups = 256;   // the CU count
+constexpr uint64_t kShortU8MinGroups = 128;  // from here to the CU count, one-chunk batches take U = 8
 constexpr uint64_t kMidBatchBytes = 128ull << 20;
 // A dispatch holds its grid size in work-items, 32 bits per dimension.
 constexpr uint64_t kMaxGridItems = 0xFFFFFFFFull;
@@ -1503,6 +1504,7 @@ SplitFn kernel_for(bool bal) {
 template <int V, int G, int N, bool F, bool DUMP, bool PAGED, int MODE>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
     if constexpr (PAGED) {
+        if (t.unroll == 8) return kernel_for<V, G, N, F, 8, true, DUMP, PAGED, MODE>(bal);
         return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal)
                              : kernel_for<V, G, N, F, 2, true, DUMP, PAGED, MODE>(bal);
     } else {
@@ -1622,12 +1624,21 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     }
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
-    if (kind == Kind::batched_short)
+    if (kind == Kind::batched_short) {
         for (uint32_t w = hpb * 2; (uint64_t)batch * (H / hpb) > kShortGroups && w <= H; w *= 2) {
             const uint32_t h = heads_per_wg(H, ly, w);
             if (h == hpb) break;
             hpb = h;
         }
+        // At most one workgroup per CU, each streaming its whole span: U = 8
+        // keeps four times the bytes in flight (4 x 32 heads x 512 positions:
+        // 11.2 -> 9.7 us; 128 x 2 x 512: 13.5 -> 11.4; 8 x 32 x 1024: 21.8 ->
+        // 19.3).  With fewer workgroups the longer blocks cost latency (1 x
+        // 32 x 256: 3.8 -> 4.4), with more they are not needed.
+        const uint64_t groups = (uint64_t)batch * (H / hpb);
+        if (groups >= kShortU8MinGroups && groups <= kShortMinGroups && env_knobs().unroll == 0)
+            kn.unroll = 8;
+    }
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);

@@ -778,6 +778,35 @@ def test_paged_equals_dense_batched(page_size):
         assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "page %d b=%d" % (page_size, b))
 
 
+@pytest.mark.parametrize("B,S,H,D", [(64, 256, 4, 128), (16, 256, 16, 64), (8, 1024, 32, 128)],
+                         ids=["b64_h4_d128", "b16_h16_d64", "b8_h32_d128_paged_two_launches"])
+def test_one_chunk_batches_with_long_blocks(B, S, H, D):
+    """One-chunk batches of 128-256 workgroups take 8 positions per block:
+    dense and paged (shuffled 16-position pages) give the same bits where
+    they take the same plan, the dump variant gives the timed kernel's bits,
+    and every output matches the oracle."""
+    print("case", B, S, H, D, flush=True)
+    dense_plan = ad.plan(B, H, D, S, flags=ad.PLAN_DEVICE_POS)
+    paged_plan = ad.plan(B, H, D, S, flags=ad.PLAN_PAGED)
+    assert dense_plan["launches"] == 1 and 128 <= dense_plan["workgroups"] <= 256, dense_plan
+    rng = np.random.default_rng(B * 100 + H)
+    q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
+    pos = rng.integers(0, S + 2, B)
+    pos[0] = S - 1
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    dense = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
+    dense_d, _ = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp, dump=True)
+    kp, vp, bt = page_dense_cache(k, v, 16, rng)
+    paged = ad.decode_paged(to_dev(q), to_dev(kp), to_dev(vp), to_dev(bt), cp)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_batched(q, k, v, pos, threads=8)
+    assert_close(dense, ref, "dense")
+    assert_close(paged, ref, "paged")
+    assert torch.equal(dense, dense_d), "dump variant differs from the timed kernel"
+    if paged_plan["launches"] == dense_plan["launches"] and paged_plan["workgroups"] == dense_plan["workgroups"]:
+        assert torch.equal(paged, dense)
+
+
 @pytest.mark.parametrize("B,S,H,D", [(64, 2048, 4, 100), (24, 4096, 4, 250)], ids=["d100", "d250"])
 def test_paged_balanced_grid_with_narrow_loads(B, S, H, D):
     """A paged pool (16-position pages, shuffled) on the balanced grid with
