@@ -1302,7 +1302,10 @@ Knobs knobs(uint32_t D, Kind kind) {
     // workgroup per sequence and head block; smaller head blocks balance
     // ragged lengths better (2048 x 512 positions: +10% ragged, +4% full)
     else if (kind == Kind::batched_chunked) k = Knobs{256, 8192, 4, 2, 1, 0};
-    else if (kind == Kind::batched_mid) k = Knobs{512, 8192, 4, 2, 1, 0};
+    // mid-size batches: two 256-byte heads per workgroup (16 x 8 heads x
+    // 1024 positions: 14.2 -> 13.7 us; 2 x 32 x 4096: 21.0 -> 20.6), four
+    // 128-byte ones (with two, 16 x 16 x 2048: 21.1 -> 21.4)
+    else if (kind == Kind::batched_mid) k = D <= 64 ? Knobs{512, 8192, 4, 2, 1, 0} : Knobs{512, 8192, 2, 2, 1, 0};
     else if (kind == Kind::stream) k = D <= 64 ? Knobs{1024, 8192, 8, 2, 1, 0} : Knobs{1024, 8192, 2, 2, 1, 0};
     else if (kind == Kind::scores) k = D <= 64 ? Knobs{1024, 8192, 4, 2, 1, 0} : Knobs{1024, 8192, 4, 8, 1, 0};
     else if (kind == Kind::single_short && D > 64) k = Knobs{512, 8192, 1, 2, 0, 0};
