@@ -346,13 +346,13 @@ def test_step_batched_every_sequence_at_position_zero():
     assert np.array_equal(kg[:, 0].view(np.uint16), kn.view(np.uint16))
 
 
-@pytest.mark.parametrize("S", [24, 600, 1100])
-def test_step_batched_more_sequences_than_balanced_grid_handles(S):
+@pytest.mark.parametrize("S,D", [(24, 64), (600, 64), (1100, 64), (1100, 128)])
+def test_step_batched_more_sequences_than_balanced_grid_handles(S, D):
     """1030 sequences take the chunked grid with per-sequence lengths, some 0
     (capacities of 24 and 600: the short-capacity plan; 1100: the plain
-    chunked one)."""
+    chunked one, eight positions per block)."""
     rng = np.random.default_rng(10)
-    B, H, D = 1030, 2, 64
+    B, H = 1030, 2
     cps = rng.integers(0, S, B)
     cps[::7] = 0
     q, kn, vn, kc, vc, cps = batched_inputs(rng, B, S, H, D, cps)

@@ -914,6 +914,33 @@ def test_paged_split_then_combine_and_many_sequences(S):
     assert_close(one, ref, "1030 paged sequences")
 
 
+@pytest.mark.parametrize("H,D", [(2, 128), (4, 64)], ids=["d128_two_heads", "d64_four_heads"])
+def test_chunked_grid_long_ragged_sequences(H, D):
+    """1030 sequences with a 1104-position capacity and ragged lengths up to
+    the capacity: the chunked grid, one workgroup per sequence and head block
+    (two heads of 128, four of 64) streaming eight positions per block, so
+    most sequences end in a partial block.  Dense and paged caches (pages of
+    16) give the same bits, the score dump matches the oracle's scores, the
+    outputs the oracle."""
+    rng = np.random.default_rng(47 + D)
+    B, S, P = 1030, 1104, 16
+    q = randn16(rng, (B, H, D))
+    k, v = (rng.standard_normal((B, S, H, D), dtype=np.float32).astype(np.float16) for _ in range(2))
+    pos = rng.integers(0, S, B)
+    pos[:6] = [0, 1, 7, 8, S - 2, S - 1]
+    cp = torch.from_numpy(pos.astype(np.int32)).to(DEV)
+    assert ad.plan(B, H, D, S, flags=ad.PLAN_DEVICE_POS)["workgroups"] == B
+    out, dump = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp, dump=True)
+    kp, vp, bt = page_dense_cache(k, v, P, rng)
+    paged = ad.decode_paged(to_dev(q), to_dev(kp), to_dev(vp), to_dev(bt), cp)
+    torch.cuda.synchronize()
+    assert torch.equal(out, paged), "paged differs from dense"
+    ref, ref_s = oracle.decode_batched(q, k, v, pos, want_scores=True)
+    assert_close(out, ref, "1030 long ragged sequences")
+    for b in (0, 3, 4, 5, 500, B - 1):
+        assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "b=%d" % b)
+
+
 # ------------------------------------------------------------ two dispatches
 
 
