@@ -1299,12 +1299,13 @@ Knobs knobs(uint32_t D, Kind kind) {
     Knobs k;
     if (kind == Kind::batched || kind == Kind::paged) k = Knobs{256, 8192, 8, 4, 1, 1};
     // batches the balanced grid does not take (more than its sequences): one
-    // workgroup per sequence and head block.  Eight positions per block keep
-    // more bytes in flight per workgroup (ragged 1200 x 4 x 128 x 8192: 1951
-    // -> 1597 us; 1030 x 8 x 64 x 4096: 786 -> 726); two 256-byte heads per
-    // workgroup balance ragged lengths better than four (1100 x 8 x 128 x
-    // 4096: 1471 -> 1386), four 128-byte ones stream faster than two (1025 x
-    // 32 x 64 x 2048: 1214 with four, 1300 with two)
+    // workgroup per sequence, head block and chunk of at most 8192 positions
+    // (one chunk, and one launch, up to that capacity).  Eight positions per
+    // block keep more bytes in flight per workgroup (ragged 1200 x 4 x 128 x
+    // 8192: 1951 -> 1597 us; 1030 x 8 x 64 x 4096: 786 -> 726); two 256-byte
+    // heads per workgroup balance ragged lengths better than four (1100 x 8 x
+    // 128 x 4096: 1471 -> 1386), four 128-byte ones stream faster than two
+    // (1025 x 32 x 64 x 2048: 1214 with four, 1300 with two)
     else if (kind == Kind::batched_chunked) k = D <= 64 ? Knobs{256, 8192, 4, 8, 1, 0} : Knobs{256, 8192, 2, 8, 1, 0};
     // mid-size batches: two 256-byte heads per workgroup (16 x 8 heads x
     // 1024 positions: 14.2 -> 13.7 us; 2 x 32 x 4096: 21.0 -> 20.6), four
