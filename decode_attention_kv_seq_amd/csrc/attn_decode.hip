@@ -792,8 +792,23 @@ __device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t
 // `grid` equal ranges, one per workgroup.  A workgroup writes one partial per
 // segment piece it covers, at slot w + s; o [slots, hpb, D], (m, l)
 // [slots, hpb, 2] with slots = grid + batch*n_hb.
+//
+// The grid holds one workgroup per CU, so one wave per SIMD.  Told that it
+// runs at most two waves per SIMD, the compiler stops shortening register
+// lifetimes for occupancy it cannot have: with two positions per block it
+// then issues each block's loads a block ahead, where otherwise it moved the
+// V loads down to their use and every iteration waited for all loads in
+// flight.  Only the dense decode at U = 2 takes the bound: the other
+// instantiations measured no faster with it (at U = 4 slower).
+template <int U, bool PAGED, int MODE>
+constexpr int balanced_max_waves() {
+    return U == 2 && !PAGED && MODE == kModeDecode ? 2 : 8;
+}
+
 template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
-__global__ __launch_bounds__(kThreads) void attn_split_balanced_kernel(SplitArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(1, balanced_max_waves<U, PAGED, MODE>())))
+void attn_split_balanced_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     constexpr bool ROPE = MODE == kModeStep;
     write_header(a, 1);
@@ -1650,6 +1665,17 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
+    // Dense decodes on the balanced grid, at least 16 sequences of at least
+    // four head blocks: two positions per block, in the instantiation bounded
+    // to two waves per SIMD (64 x 32 heads x 8192 positions, ragged: 636 ->
+    // 625 us; 48 x 32 x 8192: 477 -> 465; 32 x 32 x 16384 at head_dim 64:
+    // 345 -> 339).  With one or two head blocks (8 or 16 heads) it lost up
+    // to 4% (32 x 16 x 16384: 356 -> 369), with 4-8 sequences it gained
+    // nothing or lost (8 x 64 x 32768: 789 -> 801).  Paged caches and decode
+    // steps keep four (at two: paged 2-3% slower, the paged step 9.5%).
+    if (bal && kind == Kind::batched && !rope && batch >= 16 && H / hpb >= 4 &&
+        env_knobs().unroll == 0)
+        kn.unroll = 2;
     if (!bal && (kind == Kind::batched || kind == Kind::paged)) {   // a batch on the chunked grid
         kind = Kind::batched_chunked;
         kn = knobs(D, kind);
