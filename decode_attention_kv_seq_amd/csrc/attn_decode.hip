@@ -698,8 +698,9 @@ __device__ __forceinline__ void split_piece(const SplitArgs &a, uint32_t b, uint
 // Chunked grid: workgroup (hb + n_hb*chunk, b) takes positions
 // [chunk*C, (chunk+1)*C) of head block hb.  Partials: o [B, H, nc_stride, D],
 // (m, l) [B, H, nc_stride, 2].
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitArgs a) {
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE, int WAVES>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WAVES)))
+void attn_split_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     constexpr bool ROPE = MODE == kModeStep;
     if constexpr (MODE == kModeQk) {
@@ -792,22 +793,8 @@ __device__ __forceinline__ uint32_t find_sequence(const uint64_t *pref, uint32_t
 // `grid` equal ranges, one per workgroup.  A workgroup writes one partial per
 // segment piece it covers, at slot w + s; o [slots, hpb, D], (m, l)
 // [slots, hpb, 2] with slots = grid + batch*n_hb.
-//
-// The grid holds one workgroup per CU, so one wave per SIMD.  Told that it
-// runs at most two waves per SIMD, the compiler stops shortening register
-// lifetimes for occupancy it cannot have: with two positions per block it
-// then issues each block's loads a block ahead, where otherwise it moved the
-// V loads down to their use and every iteration waited for all loads in
-// flight.  Only the dense decode at U = 2 takes the bound: the other
-// instantiations measured no faster with it (at U = 4 slower).
-template <int U, bool PAGED, int MODE>
-constexpr int balanced_max_waves() {
-    return U == 2 && !PAGED && MODE == kModeDecode ? 2 : 8;
-}
-
-template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, balanced_max_waves<U, PAGED, MODE>())))
+template <int VEC, int GL, int NV, bool FULL, int U, bool PF, bool DUMP, bool PAGED, int MODE, int WAVES>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, WAVES)))
 void attn_split_balanced_kernel(SplitArgs a) {
     ATTN_SPLIT_LDS
     constexpr bool ROPE = MODE == kModeStep;
@@ -1217,8 +1204,8 @@ __global__ __launch_bounds__(256) void attn_rope_kernel(const uint16_t *x, uint1
 // best head blocking makes each position's read 512 contiguous bytes or
 // more, and about 1024 workgroups (4 per CU) keep enough loads in flight.
 // The ATTN_DECODE_TUNE environment variable
-// ("wgs=N,cmax=N,hpb=N,unroll=N,pf=N,bal=N") overrides them for tuning sweeps; it
-// is read once per process.
+// ("wgs=N,cmax=N,hpb=N,unroll=N,pf=N,bal=N,wfloor=N,waves=N") overrides them for
+// tuning sweeps; it is read once per process.
 struct Knobs {
     uint32_t wgs;      // target workgroups per call
     uint32_t cmax;     // largest chunk, positions
@@ -1228,6 +1215,8 @@ struct Knobs {
     uint32_t bal;      // per-sequence lengths: balanced grid (equal work per workgroup)
     uint32_t wfloor = 2;   // chunks per head block from wgs / head blocks: 0 rounded up,
                            // 1 rounded down, 2 down for targets of <= 512 workgroups
+    uint32_t waves = 0;    // 2: the instantiation compiled for at most two waves per
+                           // SIMD (dense decodes, U = 2 or 8, double-buffered); 0: none
 };
 constexpr uint32_t kChunkGranule = 16;
 constexpr uint32_t kMaxHeadsPerWG = kWaves * 64 / 8;   // row groups at 8 lanes per row
@@ -1250,6 +1239,7 @@ const Knobs &env_knobs() {
                 else if (sscanf(tok, "pf=%u", &v) == 1) r.pf = v ? 1 : 0;
                 else if (sscanf(tok, "bal=%u", &v) == 1) r.bal = v ? 1 : 0;
                 else if (sscanf(tok, "wfloor=%u", &v) == 1 && v <= 2) r.wfloor = v;
+                else if (sscanf(tok, "waves=%u", &v) == 1 && (v == 2 || v == 8)) r.waves = v;
             }
         }
         return r;
@@ -1353,6 +1343,7 @@ Knobs knobs(uint32_t D, Kind kind) {
     if (e.pf != 2) k.pf = e.pf;
     if (e.bal != 2) k.bal = e.bal;
     if (e.wfloor != 3) k.wfloor = e.wfloor;
+    if (e.waves) k.waves = e.waves == 2 ? 2 : 0;
     return k;
 }
 
@@ -1513,17 +1504,31 @@ attn_status_t check_sizes(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
 
 using SplitFn = void (*)(SplitArgs);
 
-template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED, int MODE>
+template <int V, int G, int N, bool F, int U, bool PF, bool DUMP, bool PAGED, int MODE, int WAVES = 8>
 SplitFn kernel_for(bool bal) {
     if constexpr (MODE == kModeQk || MODE == kModePv)   // single sequence: chunked grid
-        return attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>;
+        return attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE, WAVES>;
     else
-        return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>
-                   : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE>;
+        return bal ? attn_split_balanced_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE, WAVES>
+                   : attn_split_kernel<V, G, N, F, U, PF, DUMP, PAGED, MODE, WAVES>;
+}
+
+// Double-buffered blocks.  A grid of at most one workgroup per CU runs one
+// wave per SIMD, but the compiler schedules for the occupancy the registers
+// would allow: at U = 2 and U = 8 it moved V loads down to their use, so
+// that iterations waited for all loads in flight.  Compiled for at most two
+// waves per SIMD (amdgpu_waves_per_eu), it issues each block's loads a block
+// ahead.  The plan asks for that instantiation (knob waves = 2) where it
+// measured faster; only dense decodes have it.
+template <int V, int G, int N, bool F, int U, bool DUMP, bool PAGED, int MODE>
+SplitFn kernel_pf(const Knobs &t, bool bal) {
+    if constexpr (MODE == kModeDecode && !PAGED && (U == 2 || U == 8))
+        if (t.waves == 2) return kernel_for<V, G, N, F, U, true, DUMP, PAGED, MODE, 2>(bal);
+    return kernel_for<V, G, N, F, U, true, DUMP, PAGED, MODE>(bal);
 }
 
 // Dense caches honour the unroll/prefetch knobs on the fast layouts; paged
-// caches are double-buffered with U=2 or U=4.
+// caches are double-buffered with U=2, U=4 or U=8.
 template <int V, int G, int N, bool F, bool DUMP, bool PAGED, int MODE>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
     if constexpr (PAGED) {
@@ -1531,9 +1536,9 @@ SplitFn pick_unroll(const Knobs &t, bool bal) {
         return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal)
                              : kernel_for<V, G, N, F, 2, true, DUMP, PAGED, MODE>(bal);
     } else {
-        if (t.unroll == 2) return t.pf ? kernel_for<V, G, N, F, 2, true, DUMP, PAGED, MODE>(bal)
+        if (t.unroll == 2) return t.pf ? kernel_pf<V, G, N, F, 2, DUMP, PAGED, MODE>(t, bal)
                                        : kernel_for<V, G, N, F, 2, false, DUMP, PAGED, MODE>(bal);
-        if (t.unroll == 8) return t.pf ? kernel_for<V, G, N, F, 8, true, DUMP, PAGED, MODE>(bal)
+        if (t.unroll == 8) return t.pf ? kernel_pf<V, G, N, F, 8, DUMP, PAGED, MODE>(t, bal)
                                        : kernel_for<V, G, N, F, 8, false, DUMP, PAGED, MODE>(bal);
         return t.pf ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal)
                     : kernel_for<V, G, N, F, 4, false, DUMP, PAGED, MODE>(bal);
@@ -1615,6 +1620,12 @@ struct SplitPlan {
     Plan plan;
 };
 
+// Positions one block of a workgroup covers: its row groups per head block
+// (64 / gl per wave) times U.
+uint32_t block_positions(const Layout &ly, uint32_t hpb, uint32_t U) {
+    return (uint32_t)(kWaves * 64 / ly.gl) / hpb * U;
+}
+
 // dev_pos: per-sequence current_pos on the device (batched or paged);
 // paged: a paged cache; rope: a decode step; scores: softmax.V from stored
 // scores (the second dispatch).
@@ -1659,8 +1670,15 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
         // 19.3).  With fewer workgroups the longer blocks cost latency (1 x
         // 32 x 256: 3.8 -> 4.4), with more they are not needed.
         const uint64_t groups = (uint64_t)batch * (H / hpb);
-        if (groups >= kShortU8MinGroups && groups <= kShortMinGroups && env_knobs().unroll == 0)
+        if (groups >= kShortU8MinGroups && groups <= kShortMinGroups && env_knobs().unroll == 0) {
             kn.unroll = 8;
+            // and, for dense decodes whose spans hold four blocks or more,
+            // the instantiation bounded to two waves per SIMD (8 x 32 heads
+            // x 1024 positions: 19.7 -> 18.5 us; 4 x 32 x 512: 9.70 ->
+            // 9.33).  At two blocks it lost (64 x 4 x 256: 7.04 -> 7.36).
+            if (!rope && !paged && S >= 4 * block_positions(ly, hpb, 8) && env_knobs().waves == 0)
+                kn.waves = 2;
+        }
     }
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores && kn.bal && batch <= kBalancedMaxBatch &&
@@ -1674,12 +1692,20 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     // nothing or lost (8 x 64 x 32768: 789 -> 801).  Paged caches and decode
     // steps keep four (at two: paged 2-3% slower, the paged step 9.5%).
     if (bal && kind == Kind::batched && !rope && batch >= 16 && H / hpb >= 4 &&
-        env_knobs().unroll == 0)
+        env_knobs().unroll == 0) {
         kn.unroll = 2;
+        if (env_knobs().waves == 0) kn.waves = 2;
+    }
     if (!bal && (kind == Kind::batched || kind == Kind::paged)) {   // a batch on the chunked grid
         kind = Kind::batched_chunked;
         kn = knobs(D, kind);
         hpb = heads_per_wg(H, ly, kn.hpb);
+        // dense decodes: the instantiation bounded to two waves per SIMD
+        // where a chunk holds four blocks or more (1030 x 8 x 64 x 4096:
+        // 718 -> 703 us; 1200 x 4 x 128 x 8192: 1616 -> 1581)
+        if (!rope && !paged && (S < kn.cmax ? S : kn.cmax) >= 4 * block_positions(ly, hpb, kn.unroll) &&
+            env_knobs().waves == 0)
+            kn.waves = 2;
     }
     return SplitPlan{kind, kn, hpb, bal, make_plan(batch, H, D, S, span, kind)};
 }
