@@ -1519,10 +1519,10 @@ SplitFn kernel_for(bool bal) {
 // that iterations waited for all loads in flight.  Compiled for at most two
 // waves per SIMD (amdgpu_waves_per_eu), it issues each block's loads a block
 // ahead.  The plan asks for that instantiation (knob waves = 2) where it
-// measured faster; only dense decodes have it.
+// measured faster; decodes and decode steps have it.
 template <int V, int G, int N, bool F, int U, bool DUMP, bool PAGED, int MODE>
 SplitFn kernel_pf(const Knobs &t, bool bal) {
-    if constexpr (MODE == kModeDecode && !PAGED && (U == 2 || U == 8))
+    if constexpr ((MODE == kModeDecode || MODE == kModeStep) && (U == 2 || U == 8))
         if (t.waves == 2) return kernel_for<V, G, N, F, U, true, DUMP, PAGED, MODE, 2>(bal);
     return kernel_for<V, G, N, F, U, true, DUMP, PAGED, MODE>(bal);
 }
@@ -1532,9 +1532,9 @@ SplitFn kernel_pf(const Knobs &t, bool bal) {
 template <int V, int G, int N, bool F, bool DUMP, bool PAGED, int MODE>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
     if constexpr (PAGED) {
-        if (t.unroll == 8) return kernel_for<V, G, N, F, 8, true, DUMP, PAGED, MODE>(bal);
+        if (t.unroll == 8) return kernel_pf<V, G, N, F, 8, DUMP, PAGED, MODE>(t, bal);
         return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal)
-                             : kernel_for<V, G, N, F, 2, true, DUMP, PAGED, MODE>(bal);
+                             : kernel_pf<V, G, N, F, 2, DUMP, PAGED, MODE>(t, bal);
     } else {
         if (t.unroll == 2) return t.pf ? kernel_pf<V, G, N, F, 2, DUMP, PAGED, MODE>(t, bal)
                                        : kernel_for<V, G, N, F, 2, false, DUMP, PAGED, MODE>(bal);
@@ -1658,10 +1658,11 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     }
     Knobs kn = knobs(D, kind);
     uint32_t hpb = heads_per_wg(H, ly, kn.hpb);
-    // mid-size dense batches (about 512 workgroups, two per CU): the decode
-    // in the instantiation bounded to two waves per SIMD (ragged 1 x 32 x
-    // 8192: 16.4 -> 14.8 us; 8 x 8 x 4096: 21.1 -> 19.6; full lengths level)
-    if (kind == Kind::batched_mid && !rope && !paged && env_knobs().waves == 0) kn.waves = 2;
+    // mid-size batches (about 512 workgroups, two per CU): decodes in the
+    // instantiation bounded to two waves per SIMD (ragged 1 x 32 x 8192:
+    // 16.4 -> 14.8 us, paged 18.4 -> 16.4; 8 x 8 x 4096: 21.1 -> 19.6; full
+    // lengths level).  Dense steps measured mixed (-0.4% to +3.7%).
+    if (kind == Kind::batched_mid && !rope && env_knobs().waves == 0) kn.waves = 2;
     if (kind == Kind::batched_short) {
         for (uint32_t w = hpb * 2; (uint64_t)batch * (H / hpb) > kShortGroups && w <= H; w *= 2) {
             const uint32_t h = heads_per_wg(H, ly, w);
@@ -1704,10 +1705,11 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
         kind = Kind::batched_chunked;
         kn = knobs(D, kind);
         hpb = heads_per_wg(H, ly, kn.hpb);
-        // dense decodes: the instantiation bounded to two waves per SIMD
-        // where a chunk holds four blocks or more (1030 x 8 x 64 x 4096:
-        // 718 -> 703 us; 1200 x 4 x 128 x 8192: 1616 -> 1581)
-        if (!rope && !paged && (S < kn.cmax ? S : kn.cmax) >= 4 * block_positions(ly, hpb, kn.unroll) &&
+        // the instantiation bounded to two waves per SIMD where a chunk holds
+        // four blocks or more (1030 x 8 x 64 x 4096: 718 -> 703 us, paged
+        // 728 -> 713, decode step 698 -> 684; 1200 x 4 x 128 x 8192: 1616
+        // -> 1581)
+        if ((S < kn.cmax ? S : kn.cmax) >= 4 * block_positions(ly, hpb, kn.unroll) &&
             env_knobs().waves == 0)
             kn.waves = 2;
     }
