@@ -1688,16 +1688,16 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
-    // Dense decodes on the balanced grid, at least 16 sequences of at least
-    // four head blocks: two positions per block, in the instantiation bounded
-    // to two waves per SIMD (64 x 32 heads x 8192 positions, ragged: 636 ->
-    // 625 us; 48 x 32 x 8192: 477 -> 465; 32 x 32 x 16384 at head_dim 64:
-    // 345 -> 339).  With one or two head blocks (8 or 16 heads) it lost up
-    // to 4% (32 x 16 x 16384: 356 -> 369), with 4-8 sequences it gained
-    // nothing or lost (8 x 64 x 32768: 789 -> 801).  Paged caches and decode
-    // steps keep four (at two: paged 2-3% slower, the paged step 9.5%).
-    if (bal && kind == Kind::batched && !rope && batch >= 16 && H / hpb >= 4 &&
-        env_knobs().unroll == 0) {
+    // Dense decodes and steps on the balanced grid, at least 16 sequences of
+    // at least four head blocks: two positions per block, in the
+    // instantiation bounded to two waves per SIMD (64 x 32 heads x 8192
+    // positions, ragged: 636 -> 625 us, step 646 -> 638; 48 x 32 x 8192: 477
+    // -> 465; 32 x 32 x 16384 at head_dim 64: 345 -> 339).  With one or two
+    // head blocks (8 or 16 heads) it lost up to 4% (32 x 16 x 16384: 356 ->
+    // 369), with 4-8 sequences it gained nothing or lost (8 x 64 x 32768: 789
+    // -> 801).  Paged caches keep four (at two: paged 2-3% slower, the paged
+    // step 4-10%).
+    if (bal && kind == Kind::batched && batch >= 16 && H / hpb >= 4 && env_knobs().unroll == 0) {
         kn.unroll = 2;
         if (env_knobs().waves == 0) kn.waves = 2;
     }
