@@ -46,7 +46,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("balanced", ctypes.c_uint32), ("heads_per_workgroup", ctypes.c_uint32),
                 ("workgroups", ctypes.c_uint64), ("chunk", ctypes.c_uint32),
                 ("chunks", ctypes.c_uint32), ("launches", ctypes.c_uint32),
-                ("partial_slots", ctypes.c_uint64), ("workspace_slots", ctypes.c_uint64)]
+                ("partial_slots", ctypes.c_uint64), ("workspace_slots", ctypes.c_uint64),
+                ("unroll", ctypes.c_uint32), ("max_waves", ctypes.c_uint32)]
 
 
 PLAN_DEVICE_POS, PLAN_PAGED, PLAN_STEP, PLAN_FROM_SCORES = 1, 2, 4, 8

@@ -1577,6 +1577,24 @@ SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
     return nullptr;
 }
 
+// The unroll and wave bound of the split kernel pick_split runs for these
+// knobs (reported by attn_decode_plan): the two 16-byte layouts honour the
+// unroll knob (paged caches: 2, 4 or 8; dense: 2, 4 or 8, else 4), every
+// other layout runs U = 4; the two-wave instantiation exists for decodes
+// and steps, double-buffered, at U = 2 and U = 8.
+struct KernelShape {
+    uint32_t unroll, waves;
+};
+KernelShape kernel_shape(const Layout &ly, const Knobs &k, bool paged, int mode) {
+    const bool fast = ly.vec == 8 && ly.nv == 1 && ly.full && (ly.gl == 8 || ly.gl == 16);
+    if (!fast) return {4, 8};
+    const uint32_t u = paged ? (k.unroll == 8 ? 8u : k.unroll == 4 ? 4u : 2u)
+                             : (k.unroll == 2 || k.unroll == 8 ? k.unroll : 4u);
+    const bool bounded = (paged || k.pf) && (u == 2 || u == 8) && k.waves == 2 &&
+                         (mode == kModeDecode || mode == kModeStep);
+    return {u, bounded ? 2u : 8u};
+}
+
 // Shared argument checks of the split phase.
 attn_status_t check_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           const uint32_t *cp_dev, uint32_t batch, uint32_t H, uint32_t D,
@@ -2011,6 +2029,9 @@ attn_status_t attn_decode_plan(uint32_t batch, uint32_t n_heads, uint32_t head_d
                         : sp.bal ? ((uint64_t)sp.kn.wgs + (uint64_t)batch * n_hb - 1) * sp.hpb
                                  : ((uint64_t)batch * n_heads - 1) * sp.plan.nc_stride + sp.plan.n_chunks;
     info->workspace_slots = workspace_layout(batch, n_heads, head_dim, seq_len).slots;
+    const KernelShape ks = kernel_shape(ly, sp.kn, paged, scores ? kModePv : step ? kModeStep : kModeDecode);
+    info->unroll = ks.unroll;
+    info->max_waves = ks.waves;
     return ok();
 }
 

@@ -126,6 +126,13 @@ typedef struct attn_plan_info {
                                       split launch may write (0 with one
                                       launch)                                  */
     uint64_t workspace_slots;      /* partial states the workspace holds      */
+    uint32_t unroll;               /* positions each row group of a split
+                                      workgroup streams per block (2, 4, 8);
+                                      calls that differ in it round their
+                                      softmax differently                      */
+    uint32_t max_waves;            /* waves per SIMD the split kernel was
+                                      compiled for: 2 (its loads issued a
+                                      block ahead), or 8 (no bound)            */
 } attn_plan_info;
 
 attn_status_t attn_decode_plan(uint32_t batch, uint32_t n_heads, uint32_t head_dim,

@@ -803,7 +803,7 @@ def test_one_chunk_batches_with_long_blocks(B, S, H, D):
     assert_close(dense, ref, "dense")
     assert_close(paged, ref, "paged")
     assert torch.equal(dense, dense_d), "dump variant differs from the timed kernel"
-    if paged_plan["launches"] == dense_plan["launches"] and paged_plan["workgroups"] == dense_plan["workgroups"]:
+    if all(paged_plan[f] == dense_plan[f] for f in ("launches", "workgroups", "unroll")):
         assert torch.equal(paged, dense)
 
 
@@ -830,12 +830,14 @@ def test_paged_balanced_grid_with_narrow_loads(B, S, H, D):
 def test_paged_balanced_grid_page_sizes(page_size):
     """Page sizes from one position to 2048 on the balanced grid (24
     sequences x 4 heads x 8192 positions, 403 MB of K+V): bitwise equal to
-    the same caches cut into 16-position pages, and with the dense call
-    (which streams two positions per block where paged caches stream four,
-    so its rounding differs) against the oracle on every sequence."""
+    the same caches cut into 16-position pages and, since both stream the
+    same block length here, to the dense call; both against the oracle on
+    every sequence."""
     B, S, H, D = 24, 8192, 4, 128
-    assert ad.plan(B, H, D, S, 0, ad.PLAN_PAGED)["balanced"] == 1
-    assert ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS)["balanced"] == 1
+    paged_plan = ad.plan(B, H, D, S, 0, ad.PLAN_PAGED)
+    dense_plan = ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS)
+    assert paged_plan["balanced"] == 1 and dense_plan["balanced"] == 1
+    assert paged_plan["unroll"] == dense_plan["unroll"]
     rng = np.random.default_rng(60 + page_size)
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
     pos = rng.integers(0, S + 2, B)
@@ -848,6 +850,7 @@ def test_paged_balanced_grid_page_sizes(page_size):
     dense = ad.decode_batched(to_dev(q), to_dev(k), to_dev(v), cp)
     torch.cuda.synchronize()
     assert torch.equal(paged, paged16)
+    assert torch.equal(paged, dense)
     ref, _ = oracle.decode_batched(q, k, v, pos, threads=8)
     assert_close(paged, ref, "page %d" % page_size)
     assert_close(dense, ref, "dense")

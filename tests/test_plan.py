@@ -109,6 +109,54 @@ def test_many_head_blocks_are_widened():
     assert (p["heads_per_workgroup"], p["workgroups"], p["launches"]) == (4, 8192, 1)
 
 
+DP, PG, ST = PLAN_DEVICE_POS, PLAN_PAGED, PLAN_STEP
+
+
+@pytest.mark.parametrize("args,unroll,waves", [
+    # single sequences: the knobs' unroll, never bounded
+    ((1, 64, 64, 131072, 131071, 0), 8, 8),
+    ((1, 32, 128, 32768, 20000, 0), 2, 8),
+    ((1, 32, 128, 32768, 20000, ST), 2, 8),
+    ((1, 4, 64, 128, 100, 0), 8, 8),
+    ((1, 32, 128, 32768, 20000, PLAN_FROM_SCORES), 2, 8),
+    # layouts other than the 16-byte ones for head_dim 64 / 128 run U = 4
+    ((1, 40, 100, 32768, 32767, 0), 4, 8),
+    ((64, 32, 100, 8192, 0, DP), 4, 8),
+    # balanced grid, dense, >= 16 sequences of >= 4 head blocks: U = 2 bounded,
+    # decodes and steps; paged keeps U = 4 unbounded
+    ((64, 32, 128, 8192, 0, DP), 2, 2),
+    ((64, 32, 128, 8192, 0, DP | ST), 2, 2),
+    ((64, 32, 128, 8192, 0, PG), 4, 8),
+    ((64, 32, 128, 8192, 0, PG | ST), 4, 8),
+    ((32, 32, 64, 16384, 0, DP), 2, 2),
+    ((8, 32, 128, 32768, 0, DP), 4, 8),      # fewer than 16 sequences
+    ((32, 16, 128, 16384, 0, DP), 4, 8),     # two head blocks
+    # one chunk per (sequence, head block), 128-256 workgroups: U = 8, bounded
+    # for dense decodes whose capacity holds four blocks (128 positions each)
+    ((8, 32, 128, 1024, 0, DP), 8, 2),
+    ((4, 32, 128, 512, 0, DP), 8, 2),
+    ((64, 4, 128, 256, 0, DP), 8, 8),        # two blocks
+    ((4, 32, 128, 512, 0, PG), 8, 8),
+    ((4, 32, 128, 512, 0, DP | ST), 8, 8),
+    ((8, 32, 128, 1024, 0, PG), 2, 2),       # paged: the 512 KiB band needs > 256 workgroups
+    # mid-size batches: U = 2, bounded for dense and paged decodes, not steps
+    ((8, 8, 128, 4096, 0, DP), 2, 2),
+    ((8, 8, 128, 4096, 0, PG), 2, 2),
+    ((8, 8, 128, 4096, 0, DP | ST), 2, 8),
+    # past 1024 sequences: U = 8, bounded for every call whose chunk holds four blocks
+    ((1100, 8, 128, 4096, 0, DP), 8, 2),
+    ((1100, 8, 128, 4096, 0, PG), 8, 2),
+    ((1100, 8, 128, 2048, 0, DP | ST), 8, 2),
+    ((1100, 8, 128, 2048, 0, PG | ST), 8, 2),
+])
+def test_unroll_and_wave_bound(args, unroll, waves):
+    """Which split kernel each measured rule selects: positions per row group
+    and block, and whether it is the instantiation compiled for at most two
+    waves per SIMD."""
+    p = plan(*args)
+    assert (p["unroll"], p["max_waves"]) == (unroll, waves), p
+
+
 def test_batches_past_the_balanced_limit_take_the_chunked_grid():
     for S in (24, 4200, 100000):
         p = plan(1100, 2, 16, S, flags=PLAN_DEVICE_POS)
