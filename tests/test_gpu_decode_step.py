@@ -463,6 +463,46 @@ def test_paged_step_equals_dense_step(page_size):
                    int(cps[b]), D, True, what="paged sequence %d" % b)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_paged_step_past_the_balanced_grid(D):
+    """1030 sequences with a 1104-position capacity: the paged step takes the
+    chunked grid like the dense step (eight positions per block, in the
+    instantiation compiled for two waves per SIMD), gives the dense step's
+    output bits, writes the new rows into the right pages and nothing else,
+    and matches the oracle's step on sampled sequences."""
+    rng = np.random.default_rng(310 + D)
+    B, S, H, P = 1030, 1104, 2, 16
+    cps = rng.integers(0, S, B)
+    cps[:4] = [0, 1, S - 1, S + 5]
+    dense_plan = ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS | ad.PLAN_STEP)
+    paged_plan = ad.plan(B, H, D, S, 0, ad.PLAN_PAGED | ad.PLAN_STEP)
+    assert dense_plan == paged_plan, (dense_plan, paged_plan)
+    assert (dense_plan["unroll"], dense_plan["max_waves"]) == (8, 2), dense_plan
+    q, kn, vn, kc, vc, cps = batched_inputs(rng, B, S, H, D, cps)
+    print("paged step, 1030 sequences, D %d" % D, flush=True)
+    dense_out, dense_k, dense_v = run_step_batched(q, kn, vn, kc, vc, cps, D, True)
+    kp, vp, bt = scatter_pages(kc, vc, P, rng)
+    kp_d, vp_d = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    cp = torch.from_numpy(cps.astype(np.int32)).to(DEV)
+    out = ad.decode_step_paged(torch.from_numpy(q).to(DEV), torch.from_numpy(kn).to(DEV),
+                               torch.from_numpy(vn).to(DEV), kp_d, vp_d,
+                               torch.from_numpy(bt).to(DEV), cp, traditional=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), dense_out)
+    kp_g, vp_g = kp_d.cpu().numpy(), vp_d.cpu().numpy()
+    want_k, want_v = kp.copy(), vp.copy()
+    for b in range(B):
+        pos = min(int(cps[b]), S - 1)
+        page, r = bt[b, pos // P], pos % P
+        want_k[page, r] = dense_k[b, pos]
+        want_v[page, r] = dense_v[b, pos]
+    assert np.array_equal(kp_g.view(np.uint16), want_k.view(np.uint16))
+    assert np.array_equal(vp_g.view(np.uint16), want_v.view(np.uint16))
+    for b in (0, 1, 2, 3, 700):
+        check_step(out[b], dense_k[b], dense_v[b], kc[b], vc[b], q[b], kn[b], vn[b],
+                   int(cps[b]), D, True, threads=1, what="paged sequence %d" % b)
+
+
 def test_paged_step_out_of_range_entry_writes_nothing():
     """A block-table entry past the pool for the new slot: no row is written
     (the output is unspecified but the call stays in bounds)."""
