@@ -12,6 +12,8 @@ inputs come from the same generator on the device (bit-identical, checked
 in test_device_generator_matches_host).  The full-size cases also run on
 normal draws made on the GPU (torch.randn), the oracle taking host copies.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -947,6 +949,32 @@ def test_chunked_grid_long_ragged_sequences(H, D):
     assert_close(out, ref, "1030 long ragged sequences")
     for b in (0, 3, 4, 5, 500, B - 1):
         assert_dump_close(dump[b], ref_s[b], q[b], k[b], int(pos[b]), "b=%d" % b)
+
+
+def test_wave_bound_changes_no_bits(tmp_path):
+    """The split kernel compiled for at most two waves per SIMD gives the
+    unbounded kernel's bits: every kind of plan that takes the bound (the
+    balanced grid, one-chunk batches at U = 8, mid-size and chunked batches,
+    dense, paged and steps) run here, and again in one child process with
+    the bound switched off through the tuning variable."""
+    import subprocess
+    import sys
+    import wave_cases as wc
+    plans = wc.plans()
+    assert all(p["max_waves"] == 2 for p in plans.values()), plans
+    ref = wc.run_all(DEV)
+    path = tmp_path / "unbounded.pt"
+    env = dict(os.environ, ATTN_DECODE_TUNE="waves=8")
+    print("child process with the bound off", flush=True)
+    r = subprocess.run([sys.executable, wc.__file__, str(path)], env=env, capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0, r.stdout + r.stderr
+    seen = {ln.split()[0]: ln.split()[1:] for ln in r.stdout.splitlines() if ln.split()[0] in plans}
+    for name, p in plans.items():
+        assert seen[name] == [str(p["unroll"]), "8"], (name, seen[name])
+    got = torch.load(path, weights_only=True)
+    for name in ref:
+        assert torch.equal(ref[name], got[name]), name
 
 
 # ------------------------------------------------------------ two dispatches
