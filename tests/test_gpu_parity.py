@@ -839,7 +839,7 @@ def test_paged_balanced_grid_page_sizes(page_size):
     paged_plan = ad.plan(B, H, D, S, 0, ad.PLAN_PAGED)
     dense_plan = ad.plan(B, H, D, S, 0, ad.PLAN_DEVICE_POS)
     assert paged_plan["balanced"] == 1 and dense_plan["balanced"] == 1
-    assert paged_plan["unroll"] == dense_plan["unroll"]
+    assert all(paged_plan[f] == dense_plan[f] for f in ("unroll", "heads_per_workgroup", "workgroups"))
     rng = np.random.default_rng(60 + page_size)
     q, k, v = randn16(rng, (B, H, D)), randn16(rng, (B, S, H, D)), randn16(rng, (B, S, H, D))
     pos = rng.integers(0, S + 2, B)

@@ -58,9 +58,23 @@ def test_four_per_cu_plans_round_up(H, D, S, expect):
 
 
 def test_ragged_batch_workload_takes_the_balanced_grid():
-    p = plan(64, 32, 128, 8192, flags=PLAN_DEVICE_POS)
-    assert (p["balanced"], p["workgroups"], p["heads_per_workgroup"], p["launches"]) == (1, 256, 8, 2)
-    assert plan(64, 32, 128, 8192, flags=PLAN_PAGED)["balanced"] == 1
+    # 256 workgroups of eight heads
+    for flags in (PLAN_DEVICE_POS, PLAN_PAGED):
+        p = plan(64, 32, 128, 8192, flags=flags)
+        assert (p["balanced"], p["workgroups"], p["heads_per_workgroup"], p["launches"]) == (1, 256, 8, 2)
+
+
+@pytest.mark.parametrize("H,D,flags,hpb", [
+    (16, 128, PLAN_DEVICE_POS, 4),   # four head blocks of four heads
+    (16, 128, PLAN_PAGED, 8),
+    (16, 64, PLAN_DEVICE_POS, 8),
+    (8, 128, PLAN_DEVICE_POS, 8),    # four per workgroup would still give two blocks
+    (32, 128, PLAN_DEVICE_POS, 8),
+    (64, 128, PLAN_DEVICE_POS, 8),
+])
+def test_balanced_head_blocks(H, D, flags, hpb):
+    p = plan(32, H, D, 16384, flags=flags)
+    assert (p["balanced"], p["heads_per_workgroup"]) == (1, hpb), p
 
 
 def kind_of(p):
@@ -130,7 +144,9 @@ DP, PG, ST = PLAN_DEVICE_POS, PLAN_PAGED, PLAN_STEP
     ((64, 32, 128, 8192, 0, PG | ST), 4, 8),
     ((32, 32, 64, 16384, 0, DP), 2, 2),
     ((8, 32, 128, 32768, 0, DP), 4, 8),      # fewer than 16 sequences
-    ((32, 16, 128, 16384, 0, DP), 4, 8),     # two head blocks
+    ((32, 16, 64, 16384, 0, DP), 4, 8),      # two head blocks (eight heads of 64)
+    ((32, 16, 128, 16384, 0, DP), 2, 2),     # four head blocks (four heads of 128)
+    ((32, 8, 128, 16384, 0, DP), 4, 8),      # two head blocks
     # one chunk per (sequence, head block), 128-256 workgroups: U = 8, bounded
     # for dense decodes whose capacity holds four blocks (128 positions each)
     ((8, 32, 128, 1024, 0, DP), 8, 2),
