@@ -1420,8 +1420,8 @@ uint32_t chunk_bound(uint32_t batch, uint32_t H, uint32_t D, uint32_t S) {
 // Chunk size for `span` positions.  The head blocking assumed here is the
 // one of the widest-load layout for this head_dim, so the plan depends on
 // sizes only (the combine launch recomputes it without the cache pointers).
-Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span, Kind kind) {
-    const Knobs k = knobs(D, kind);
+Plan make_plan(uint32_t batch, uint32_t H, uint32_t D, uint32_t S, uint32_t span, Kind kind,
+               const Knobs &k) {
     const Layout best = choose_layout(D, nullptr, nullptr, nullptr);
     const uint64_t n_hb = H / heads_per_wg(H, best, k.hpb);
     // Chunks per (sequence, head block): about wgs workgroups in all.  With
@@ -1681,6 +1681,17 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     // 16.4 -> 14.8 us, paged 18.4 -> 16.4; 8 x 8 x 4096: 21.1 -> 19.6; full
     // lengths level).  Dense steps measured mixed (-0.4% to +3.7%).
     if (kind == Kind::batched_mid && !rope && env_knobs().waves == 0) kn.waves = 2;
+    // Single sequences of head_dim 128 (the 16-byte layout) whose head blocks
+    // are a power of two: one workgroup per CU in the bounded instantiation
+    // rather than two in the unbounded one (32 heads x 20001 of 32768
+    // positions: 53.6 -> 52.6 us; 8 x 131072: 83.6 -> 82.0; 16 x 16384: 28.2
+    // -> 26.7).  Unbounded, 256 workgroups lost 8-17%; with six head blocks
+    // (12 heads) the bounded grid lost 3-8%.
+    if (kind == Kind::single && !rope && ly.vec == 8 && ly.gl == 16 && ly.full && ly.nv == 1 &&
+        ((H / hpb) & (H / hpb - 1)) == 0 && env_knobs().wgs == 0 && env_knobs().waves == 0) {
+        kn.wgs = 256;
+        kn.waves = 2;
+    }
     if (kind == Kind::batched_short) {
         for (uint32_t w = hpb * 2; (uint64_t)batch * (H / hpb) > kShortGroups && w <= H; w *= 2) {
             const uint32_t h = heads_per_wg(H, ly, w);
@@ -1742,7 +1753,7 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
             env_knobs().waves == 0)
             kn.waves = 2;
     }
-    return SplitPlan{kind, kn, hpb, bal, make_plan(batch, H, D, S, span, kind)};
+    return SplitPlan{kind, kn, hpb, bal, make_plan(batch, H, D, S, span, kind, kn)};
 }
 
 attn_status_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -2179,7 +2190,7 @@ attn_status_t attn_qk_f16(const uint16_t *q, const uint16_t *k_cache, uint16_t *
     // the reading grid covers positions 0..current_pos; a few more
     // workgroups write -inf over the rest
     const uint32_t L = (current_pos < seq_len - 1 ? current_pos : seq_len - 1) + 1;
-    const Plan plan = make_plan(1, n_heads, head_dim, seq_len, L, Kind::scores);
+    const Plan plan = make_plan(1, n_heads, head_dim, seq_len, L, Kind::scores, kn);
     SplitArgs a = {};
     a.q = q;
     a.k = k_cache;

@@ -25,8 +25,8 @@ def plan(B, H, D, S, cp=0, flags=0):
     ((1, 4, 64, 128, 100), dict(balanced=0, workgroups=1, chunks=1, launches=1)),
     # 4096 positions, head_dim 128: one head per workgroup, 512 workgroups
     ((1, 32, 128, 4096, 4095), dict(balanced=0, heads_per_workgroup=1, workgroups=512, launches=2)),
-    # 20001 of 32768 positions: 512 workgroups of two heads
-    ((1, 32, 128, 32768, 20000), dict(balanced=0, heads_per_workgroup=2, workgroups=512, launches=2)),
+    # 20001 of 32768 positions: 256 workgroups of two heads (16 head blocks)
+    ((1, 32, 128, 32768, 20000), dict(balanced=0, heads_per_workgroup=2, workgroups=256, launches=2)),
     # 131072 positions, head_dim 64: 1024 workgroups of four heads (512-byte rows)
     ((1, 64, 64, 131072, 131071), dict(balanced=0, heads_per_workgroup=4, workgroups=1024, launches=2)),
 ])
@@ -129,7 +129,8 @@ DP, PG, ST = PLAN_DEVICE_POS, PLAN_PAGED, PLAN_STEP
 @pytest.mark.parametrize("args,unroll,waves", [
     # single sequences: the knobs' unroll, never bounded
     ((1, 64, 64, 131072, 131071, 0), 8, 8),
-    ((1, 32, 128, 32768, 20000, 0), 2, 8),
+    ((1, 32, 128, 32768, 20000, 0), 2, 2),   # head_dim 128, 16 head blocks: bounded
+    ((1, 12, 128, 32768, 32767, 0), 2, 8),   # six head blocks: unbounded
     ((1, 32, 128, 32768, 20000, ST), 2, 8),
     ((1, 4, 64, 128, 100, 0), 8, 8),
     ((1, 32, 128, 32768, 20000, PLAN_FROM_SCORES), 2, 8),
