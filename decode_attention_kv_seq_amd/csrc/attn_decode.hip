@@ -1259,10 +1259,11 @@ const Knobs &env_knobs() {
 // the narrower head block wins (4096 positions: 16.5 against 18.6 us; 8192:
 // 27.2 against 27.9; from 16384 on it loses).
 // A decode step over more positions than that, with 256-byte rows (head_dim
-// 128), wants fewer workgroups than the plain decode, one per CU (32 heads x
-// 32768 positions: 83.4 against 87.5 us; 64 x 16384: 88.9 against 94.9); at
-// head_dim 192 it loses (82.4 against 73.2 us), and head_dim 256 does as
-// well on its own row.
+// 128), wants one workgroup per CU (32 heads x 32768 positions: 83.4
+// against 87.5 us with two; 64 x 16384: 88.9 against 94.9); at head_dim 192
+// it loses (82.4 against 73.2 us), and head_dim 256 does as well on its own
+// row.  The plain decode takes one per CU only in the instantiation bounded
+// to two waves per SIMD, which plan_split picks for it at head_dim 128.
 // A single sequence short enough that one workgroup per head block streams
 // its whole span in about the time a combine launch costs (<= 256 KiB of K+V
 // per workgroup) takes one chunk per head block, double-buffered so that its
