@@ -1714,6 +1714,14 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
             if (!rope && !paged && S >= 4 * block_positions(ly, hpb, 8) && env_knobs().waves == 0)
                 kn.waves = 2;
         }
+        // Dense decode steps whose spans hold at most four blocks of U = 2:
+        // one block at a time (the rotation prologue and two register blocks
+        // cost occupancy that many small workgroups need: 256 x 32 heads x
+        // 64 positions 43.6 -> 37.3 us, 1024 x 32 x 32 77.9 -> 66.7, 64 x 32
+        // x 128 21.1 -> 18.7); at eight blocks double buffering wins (16 x 32
+        // x 256: 12.0 against 12.8).
+        if (rope && !paged && kn.unroll == 2 && S <= 4 * block_positions(ly, hpb, 2) && env_knobs().pf == 2)
+            kn.pf = 0;
     }
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores && kn.bal && batch <= kBalancedMaxBatch &&
