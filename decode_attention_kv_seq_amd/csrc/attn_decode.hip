@@ -1529,13 +1529,15 @@ SplitFn kernel_pf(const Knobs &t, bool bal) {
 }
 
 // Dense caches honour the unroll/prefetch knobs on the fast layouts; paged
-// caches are double-buffered with U=2, U=4 or U=8.
+// caches are double-buffered at U=4 and U=8, and honour the prefetch knob at
+// U=2.
 template <int V, int G, int N, bool F, bool DUMP, bool PAGED, int MODE>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
     if constexpr (PAGED) {
         if (t.unroll == 8) return kernel_pf<V, G, N, F, 8, DUMP, PAGED, MODE>(t, bal);
-        return t.unroll == 4 ? kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal)
-                             : kernel_pf<V, G, N, F, 2, DUMP, PAGED, MODE>(t, bal);
+        if (t.unroll == 4) return kernel_for<V, G, N, F, 4, true, DUMP, PAGED, MODE>(bal);
+        return t.pf ? kernel_pf<V, G, N, F, 2, DUMP, PAGED, MODE>(t, bal)
+                    : kernel_for<V, G, N, F, 2, false, DUMP, PAGED, MODE>(bal);
     } else {
         if (t.unroll == 2) return t.pf ? kernel_pf<V, G, N, F, 2, DUMP, PAGED, MODE>(t, bal)
                                        : kernel_for<V, G, N, F, 2, false, DUMP, PAGED, MODE>(bal);
@@ -1591,7 +1593,8 @@ KernelShape kernel_shape(const Layout &ly, const Knobs &k, bool paged, int mode)
     if (!fast) return {4, 8};
     const uint32_t u = paged ? (k.unroll == 8 ? 8u : k.unroll == 4 ? 4u : 2u)
                              : (k.unroll == 2 || k.unroll == 8 ? k.unroll : 4u);
-    const bool bounded = (paged || k.pf) && (u == 2 || u == 8) && k.waves == 2 &&
+    const bool pf = paged ? (u != 2 || k.pf) : k.pf != 0;
+    const bool bounded = pf && (u == 2 || u == 8) && k.waves == 2 &&
                          (mode == kModeDecode || mode == kModeStep);
     return {u, bounded ? 2u : 8u};
 }
@@ -1714,13 +1717,14 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
             if (!rope && !paged && S >= 4 * block_positions(ly, hpb, 8) && env_knobs().waves == 0)
                 kn.waves = 2;
         }
-        // Dense decode steps whose spans hold at most four blocks of U = 2:
-        // one block at a time (the rotation prologue and two register blocks
+        // Decode steps whose spans hold at most four blocks of U = 2: one
+        // block at a time (the rotation prologue and two register blocks
         // cost occupancy that many small workgroups need: 256 x 32 heads x
-        // 64 positions 43.6 -> 37.3 us, 1024 x 32 x 32 77.9 -> 66.7, 64 x 32
-        // x 128 21.1 -> 18.7); at eight blocks double buffering wins (16 x 32
-        // x 256: 12.0 against 12.8).
-        if (rope && !paged && kn.unroll == 2 && S <= 4 * block_positions(ly, hpb, 2) && env_knobs().pf == 2)
+        // 64 positions 43.6 -> 37.3 us, paged 47.8 -> 41.8; 1024 x 32 x 32
+        // 77.9 -> 66.7; 64 x 32 x 128 21.1 -> 18.7); at eight blocks double
+        // buffering wins (16 x 32 x 256: 12.0 against 12.8, paged 13.9
+        // against 17.3).  Decodes keep it (paged ones lost 3-12% without).
+        if (rope && kn.unroll == 2 && S <= 4 * block_positions(ly, hpb, 2) && env_knobs().pf == 2)
             kn.pf = 0;
     }
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
