@@ -87,7 +87,8 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t n_heads, uint32_t he
  * partial states fit the workspace attn_decode_workspace_bytes sizes.
  * Host only: no HIP call is made and no device is needed.  The plan assumes
  * tensors aligned for 16-byte loads (as a caching allocator returns them);
- * with less aligned tensors a call may put fewer heads in a workgroup.
+ * with less aligned tensors a call may put fewer heads in a workgroup and
+ * runs U = 4 without the wave bound.
  *   flags        which call is meant, ATTN_PLAN_* bits (0: attn_decode_f16,
  *                or attn_decode_f16_split with one host current_pos for the
  *                whole batch):
