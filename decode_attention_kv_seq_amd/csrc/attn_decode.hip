@@ -1216,7 +1216,7 @@ struct Knobs {
     uint32_t wfloor = 2;   // chunks per head block from wgs / head blocks: 0 rounded up,
                            // 1 rounded down, 2 down for targets of <= 512 workgroups
     uint32_t waves = 0;    // 2: the instantiation compiled for at most two waves per
-                           // SIMD (dense decodes, U = 2 or 8, double-buffered); 0: none
+                           // SIMD (decodes and steps, U = 2 or 8, double-buffered); 0: none
 };
 constexpr uint32_t kChunkGranule = 16;
 constexpr uint32_t kMaxHeadsPerWG = kWaves * 64 / 8;   // row groups at 8 lanes per row
@@ -1730,6 +1730,18 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     // balanced grid: its 64-bit range arithmetic needs n_hb*batch*S*grid < 2^63
     const bool bal = !scores && kn.bal && batch <= kBalancedMaxBatch &&
                      (unsigned __int128)(H / hpb) * batch * S * kn.wgs < ((unsigned __int128)1 << 63);
+    // Dense head_dim 65-128 on the balanced grid with fewer than four head
+    // blocks: four heads per workgroup where that makes four blocks (16
+    // heads), so that the next rule applies (32 x 16 heads x 16384
+    // positions: 351 -> 346 us, full 642 -> 621; steps 356 -> 351).  At 32
+    // heads four per workgroup lost (the 64 x 32 x 8192 ragged batch: 607 ->
+    // 615 us).
+    if (bal && kind == Kind::batched && D > 64 && D <= 128 && H / hpb < 4 && env_knobs().hpb == 0) {
+        const uint32_t h4 = heads_per_wg(H, ly, hpb / 2);
+        if (h4 >= 4 && H / h4 >= 4 &&
+            (unsigned __int128)(H / h4) * batch * S * kn.wgs < ((unsigned __int128)1 << 63))
+            hpb = h4;
+    }
     // Dense decodes and steps on the balanced grid, at least 16 sequences of
     // at least four head blocks: two positions per block, in the
     // instantiation bounded to two waves per SIMD (64 x 32 heads x 8192
@@ -1739,17 +1751,6 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     // 369), with 4-8 sequences it gained nothing or lost (8 x 64 x 32768: 789
     // -> 801).  Paged caches keep four (at two: paged 2-3% slower, the paged
     // step 4-10%).
-    // Dense head_dim 65-128 with fewer than four head blocks: four heads per
-    // workgroup where that makes four blocks (16 heads), so that the rule
-    // below applies (32 x 16 heads x 16384 positions: 351 -> 346 us, full
-    // 642 -> 621; steps 356 -> 351).  At 32 heads four per workgroup lost
-    // (the 64 x 32 x 8192 ragged batch: 607 -> 615 us).
-    if (bal && kind == Kind::batched && D > 64 && D <= 128 && H / hpb < 4 && env_knobs().hpb == 0) {
-        const uint32_t h4 = heads_per_wg(H, ly, hpb / 2);
-        if (h4 >= 4 && H / h4 >= 4 &&
-            (unsigned __int128)(H / h4) * batch * S * kn.wgs < ((unsigned __int128)1 << 63))
-            hpb = h4;
-    }
     if (bal && kind == Kind::batched && batch >= 16 && H / hpb >= 4 && env_knobs().unroll == 0) {
         kn.unroll = 2;
         if (env_knobs().waves == 0) kn.waves = 2;
