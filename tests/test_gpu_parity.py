@@ -420,6 +420,30 @@ def test_masked_garbage_leaves_output_bitwise_unchanged(fill):
     assert bool(torch.all(dump[:, cp + 1:] == -torch.inf))
 
 
+@pytest.mark.parametrize("H", [1, 2, 4, 8, 16, 32, 64, 12])
+def test_single_sequences_head_dim_128_head_counts(H):
+    """Single sequences of head_dim 128 past the short-span plan: with a
+    power-of-two number of head blocks, 256 workgroups in the instantiation
+    compiled for two waves per SIMD; 12 heads (six blocks) keep the
+    unbounded grid of two workgroups per CU.  Every output against the
+    oracle, the dump against its scores, the dump variant's output bitwise
+    equal to the timed kernel's."""
+    S, D = 20000, 128
+    cp = S - 1 - 7 * H
+    p = ad.plan(1, H, D, S, cp, 0)
+    bounded = H != 12
+    assert p["max_waves"] == (2 if bounded else 8), p
+    assert p["workgroups"] <= (256 if bounded else 512), p
+    rng = np.random.default_rng(900 + H)
+    q, k, v = randn16(rng, (H, D)), randn16(rng, (S, H, D)), randn16(rng, (S, H, D))
+    out = run_single(q, k, v, cp)
+    out_d, dump = run_single(q, k, v, cp, dump=True)
+    assert torch.equal(out, out_d), "dump variant differs from the timed kernel"
+    ref, ref_s, _ = oracle.decode(q, k, v, cp, want_scores=True, threads=8)
+    assert_close(out, ref, "%d heads" % H)
+    assert_dump_close(dump, ref_s, q, k, cp, "%d heads" % H)
+
+
 def test_current_pos_beyond_cache_masks_nothing():
     rng = np.random.default_rng(9)
     S, H, D = 1500, 4, 128
