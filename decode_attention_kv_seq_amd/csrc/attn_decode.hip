@@ -1691,6 +1691,11 @@ SplitPlan plan_split(const Layout &ly, bool dev_pos, uint32_t cp_host, bool page
     // positions: 53.6 -> 52.6 us; 8 x 131072: 83.6 -> 82.0; 16 x 16384: 28.2
     // -> 26.7).  Unbounded, 256 workgroups lost 8-17%; with six head blocks
     // (12 heads) the bounded grid lost 3-8%.
+    // Single sequences of one chunk per head block at head_dim 128 (U = 2,
+    // one workgroup per head): the bounded instantiation (16 heads x 512
+    // positions: 11.95 -> 10.34 us; 64 x 256: 7.6 -> 7.4; 4 x 512: 11.6 ->
+    // 9.8).  The step measured 2% slower with it.
+    if (kind == Kind::single_tiny && !rope && D > 64 && env_knobs().waves == 0) kn.waves = 2;
     if (kind == Kind::single && !rope && ly.vec == 8 && ly.gl == 16 && ly.full && ly.nv == 1 &&
         ((H / hpb) & (H / hpb - 1)) == 0 && env_knobs().wgs == 0 && env_knobs().waves == 0) {
         kn.wgs = 256;

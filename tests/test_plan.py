@@ -133,6 +133,8 @@ DP, PG, ST = PLAN_DEVICE_POS, PLAN_PAGED, PLAN_STEP
     ((1, 12, 128, 32768, 32767, 0), 2, 8),   # six head blocks: unbounded
     ((1, 32, 128, 32768, 20000, ST), 2, 8),
     ((1, 4, 64, 128, 100, 0), 8, 8),
+    ((1, 16, 128, 512, 511, 0), 2, 2),       # one chunk per head, head_dim 128: bounded
+    ((1, 16, 128, 512, 511, ST), 2, 8),
     ((1, 32, 128, 32768, 20000, PLAN_FROM_SCORES), 2, 8),
     # layouts other than the 16-byte ones for head_dim 64 / 128 run U = 4
     ((1, 40, 100, 32768, 32767, 0), 4, 8),
