@@ -516,6 +516,23 @@ def measure_decode(w, args, dev, lib, path="fused", steps=None, warmup=None):
     }
 
 
+def plan_summary(w, path="fused"):
+    """The split plan the library takes for this workload (attn_decode_plan):
+    grid, heads per workgroup, chunks, launches, unroll and wave bound."""
+    import decode_attention_kv_seq_amd as ad
+    flags = 0
+    if w.batched:
+        flags |= ad.PLAN_PAGED if w.paged else ad.PLAN_DEVICE_POS
+    if path == "step":
+        flags |= ad.PLAN_STEP
+    if path == "two_dispatch":
+        flags |= ad.PLAN_FROM_SCORES
+    cp = 0 if w.batched else min(w.cur_pos, w.seq_len - 1)
+    p = ad.plan(w.batch, w.n_heads, w.head_dim, w.seq_len, cp, flags)
+    keep = ("balanced", "workgroups", "heads_per_workgroup", "chunks", "launches", "unroll", "max_waves")
+    return {k: p[k] for k in keep}
+
+
 def gate_entry(w, r):
     """One gated workload's figures for config.gates."""
     target_us = r["nbytes"] / (GATE_FRAC * HBM_PEAK_GBS * 1e9) * 1e6
@@ -529,6 +546,7 @@ def gate_entry(w, r):
         "us_at_80pct": round(target_us, 2),
         "meets_80pct": bool(r["ms"] * 1e3 <= target_us),
         "inputs": r["source"],
+        "plan": plan_summary(w),
     }
 
 
@@ -608,6 +626,7 @@ def main():
         "split_kernel_us": round(split_avg * 1e3, 3),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "path": args.path,
+        "plan": plan_summary(w, args.path),
         "inputs": "torch.randn (normal)" if not w.paged else
                   "counter-based generator (Irwin-Hall(4), +-3.46 sigma)",
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
