@@ -258,6 +258,17 @@ def test_partial_states_fit_the_workspace():
             assert not p["balanced"] and p["chunks"] == 1 and p["partial_slots"] == 0, what
         elif not p["balanced"] and p["chunks"] == 1 and (B == 1 or not single):
             assert False, ("one chunk per head block in two launches", what)
+        # the kernel: U in {2, 4, 8}, U = 4 off the 16-byte layouts of head_dim
+        # 64 and 128; the two-wave instantiation only at U = 2 or 8, never for
+        # softmax.V from stored scores, and on the balanced grid only for dense
+        # calls at U = 2
+        assert p["unroll"] in (2, 4, 8) and p["max_waves"] in (2, 8), what
+        if D not in (64, 128):
+            assert (p["unroll"], p["max_waves"]) == (4, 8), what
+        if p["max_waves"] == 2:
+            assert p["unroll"] in (2, 8) and not flags & PLAN_FROM_SCORES, what
+            if p["balanced"]:
+                assert p["unroll"] == 2 and not flags & PLAN_PAGED, what
         n += 1
     assert n == 4000
 
