@@ -1530,7 +1530,8 @@ SplitFn kernel_pf(const Knobs &t, bool bal) {
 
 // Dense caches honour the unroll/prefetch knobs on the fast layouts; paged
 // caches are double-buffered at U=4 and U=8, and honour the prefetch knob at
-// U=2.
+// U=2.  kernel_shape (below) restates these choices for attn_decode_plan:
+// a change here changes it too.
 template <int V, int G, int N, bool F, bool DUMP, bool PAGED, int MODE>
 SplitFn pick_unroll(const Knobs &t, bool bal) {
     if constexpr (PAGED) {
@@ -1581,7 +1582,8 @@ SplitFn pick_split(const Layout &ly, const Knobs &k, bool bal) {
 }
 
 // The unroll and wave bound of the split kernel pick_split runs for these
-// knobs (reported by attn_decode_plan): the two 16-byte layouts honour the
+// knobs (reported by attn_decode_plan; it follows pick_unroll, kernel_pf and
+// pick_split, and changes with them): the two 16-byte layouts honour the
 // unroll knob (paged caches: 2, 4 or 8; dense: 2, 4 or 8, else 4), every
 // other layout runs U = 4; the two-wave instantiation exists for decodes
 // and steps, double-buffered, at U = 2 and U = 8.
